@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Paged decode benchmark on one MI355X.
+
+Workload: the Llama-3-70B-shaped decode batch over all 80 layers -- 20
+sequences of 8,000 tokens, 64 query / 8 KV heads of 128, bf16 KV cache in
+blocks of 16 tokens with shuffled block tables (10,000 blocks and 655 MB of
+K+V per layer, 52.4 GB in HBM).  One step is the whole decode path of one
+token per sequence: the slot of each newest token, then for each of the 80
+layers the write of the new token's K/V into its slot and the paged
+attention over all 8,000 tokens.
+
+Prints one JSON line.  ``value`` is KV GB/s over the whole step (K and V
+bytes of all 8,000 tokens x 80 layers, counted once, / step time), with
+tokens/s beside it; ``roofline`` prices the decode launch against the
+8 TB/s HBM peak; ``cpu_baseline`` times the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published figure
+
+
+# --------------------------------------------------------------------------
+# byte accounting (host arithmetic)
+# --------------------------------------------------------------------------
+
+def kv_bytes(context_lens, num_kv_heads: int, head_dim: int, elem_bytes: int, layers: int = 1) -> int:
+    """2 (K and V) x layers x kv heads x head_dim x tokens x bytes: the
+    KV-size formula of the ia-vox article ("Pourquoi le KV cache domine"),
+    summed over the batch's real context lengths."""
+    return 2 * layers * num_kv_heads * head_dim * int(sum(int(n) for n in context_lens)) * elem_bytes
+
+
+def decode_algorithmic_bytes(context_lens, num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                             kv_elem: int, q_elem: int, int8_scales: bool = False) -> int:
+    """Bytes one decode call must move at least: K and V of every token
+    (not padded to the block), the per-(block, head) scales of int8 caches,
+    the table entries in use, the context lengths, q and the fp32 output."""
+    S = len(context_lens)
+    blocks = sum(-(-int(n) // block_size) for n in context_lens)
+    b = kv_bytes(context_lens, num_kv_heads, head_dim, kv_elem)
+    if int8_scales:
+        b += blocks * num_kv_heads * 2 * 4
+    b += blocks * 4 + S * 4 + S * num_q_heads * head_dim * (q_elem + 4)
+    return b
+
+
+def waste_report(context_lens, block_size: int, reserved: int):
+    """Reserved-but-empty KV slots: one contiguous region of `reserved`
+    tokens per request versus pages of `block_size` (forum thread, ia-vox and
+    deeplearn.tn articles; glossary figure)."""
+    used = sum(int(n) for n in context_lens)
+    paged = sum(-(-int(n) // block_size) * block_size for n in context_lens)
+    contig = reserved * len(context_lens)
+    return {"contiguous_waste": 1.0 - used / contig if contig else 0.0,
+            "paged_waste": 1.0 - used / paged if paged else 0.0}
+
+
+# --------------------------------------------------------------------------
+# benchmark
+# --------------------------------------------------------------------------
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def run(args) -> dict:
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_192_amd as pa
+    import synth
+
+    pa.library()  # fail loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    c = synth.CFG3
+    L = args.layers
+    st = synth.config3_structure()
+    S, Hq, Hkv, D, BS, ctx = c["num_seqs"], c["num_q_heads"], c["num_kv_heads"], c["head_dim"], c["block_size"], \
+        c["context_len"]
+    scale = float(st["scale"])
+    print("bench: generating %d layers of %d x %d tokens on the device" % (L, S, ctx), file=sys.stderr, flush=True)
+    K, V, Q, KN, VN = [], [], [], [], []
+    for layer in range(L):
+        q, k, v, kn, vn = synth.config3_layer_values(layer, dev)
+        K.append(k)
+        V.append(v)
+        Q.append(q)
+        KN.append(kn)
+        VN.append(vn)
+    bt = torch.from_numpy(st["block_tables"]).to(dev)
+    cl = torch.from_numpy(st["context_lens"]).to(dev)
+    outs = [torch.empty(S, Hq, D, dtype=torch.float32, device=dev) for _ in range(L)]
+    slots = torch.empty(S, dtype=torch.int64, device=dev)
+    probe = pa.make_decode_args(Q[0], K[0], V[0], bt, cl, scale, ctx, out=outs[0])
+    ws_bytes = pa.decode_workspace_size(probe)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def prepare(stream):
+        """One step's calls with arguments packed once, on `stream`."""
+        calls = [pa.prepare_slot_mapping(bt, BS, slots, context_lens=cl, stream=stream)]
+        dec = []
+        for layer in range(L):
+            calls.append(pa.prepare_reshape_and_cache(KN[layer], VN[layer], K[layer], V[layer], slots,
+                                                      stream=stream))
+            d = pa.PreparedDecode(Q[layer], K[layer], V[layer], bt, cl, scale, ctx, outs[layer], workspace=ws,
+                                  stream=stream)
+            calls.append(d)
+            dec.append(d)
+        return calls, dec
+
+    main_stream = torch.cuda.current_stream()
+    eager_calls, eager_dec = prepare(main_stream)
+
+    def eager_step():
+        for f in eager_calls:
+            f()
+
+    # the same step captured once as a HIP graph (no memsets in it: every
+    # node is one of the library's kernels)
+    graph = None
+    if args.graph:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(main_stream)
+        graph_calls, _ = prepare(cap)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            for f in graph_calls:
+                f()
+        torch.cuda.synchronize()
+
+    def step():
+        if graph is not None:
+            graph.replay()
+        else:
+            eager_step()
+
+    # replays must reproduce the eager result bit for bit
+    eager_step()
+    torch.cuda.synchronize()
+    ref = torch.stack(outs).clone()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if not torch.equal(torch.stack(outs), ref):
+        raise RuntimeError("graph replay differs from the eager step")
+
+    # timed region: exactly `steps` steps between two synchronisations
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # per-launch duration of the decode call: events around each eager call
+    launch_ms = []
+    for _ in range(max(1, min(args.steps, 5))):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+        eager_calls[0]()
+        for layer in range(L):
+            eager_calls[1 + 2 * layer]()
+            evs[layer][0].record()
+            eager_dec[layer]()
+            evs[layer][1].record()
+        torch.cuda.synchronize()
+        launch_ms += [a.elapsed_time(b) for a, b in evs]
+    launch_ms = sorted(launch_ms)
+    launch_avg = sum(launch_ms) / len(launch_ms)
+    if not torch.equal(torch.stack(outs), ref):
+        raise RuntimeError("timed steps changed the result")
+
+    cls = st["context_lens"]
+    kv_step = kv_bytes(cls, Hkv, D, 2, layers=L)
+    alg_launch = decode_algorithmic_bytes(cls, Hq, Hkv, D, BS, 2, 2)
+    gbs = kv_step / (ms_per_step * 1e-3) / 1e9
+    achieved = alg_launch / (launch_avg * 1e-3) / 1e9
+    res = {
+        "metric": "paged decode KV GB/s",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3-70b-shaped gqa decode, 80 layers", "layers": L, "num_seqs": S,
+                   "context_len": ctx, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D, "block_size": BS,
+                   "kv_dtype": "bf16", "global_batch": S, "seq_len": ctx},
+        "tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "kv_bytes_per_step": kv_step,
+        "wall_s_timed_region": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pa_decode (partition + merge)", "launch_ms_avg": round(launch_avg, 5),
+                     "launch_ms_p10": round(launch_ms[len(launch_ms) // 10], 5),
+                     "launch_ms_p90": round(launch_ms[(9 * len(launch_ms)) // 10], 5),
+                     "algorithmic_bytes_per_launch": alg_launch, "workspace_bytes": ws_bytes},
+        "waste": waste_report(cls, BS, 8192),
+        "step_mode": "hip graph replay" if graph is not None else "eager prepared calls",
+    }
+    if args.cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args, K, V, Q, st, L)
+    return res
+
+
+def cpu_baseline(args, K, V, Q, st, L) -> dict:
+    """The CPU oracle (fp64, OpenMP over (sequence, head) rows) on a bounded
+    sample of the same workload: whole layers, all 20 sequences, copied back
+    from the device; layers are added until about `cpu_seconds` of wall time
+    have been spent in the oracle.  Reported in the metric's unit."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+
+    c = synth.CFG3
+
+    def host(t):
+        return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+    done, spent = 0, 0.0
+    for layer in range(L):
+        k, v, q = host(K[layer]), host(V[layer]), host(Q[layer])
+        t0 = time.perf_counter()
+        oracle.paged_decode(q, k, v, st["block_tables"], st["context_lens"], float(st["scale"]))
+        spent += time.perf_counter() - t0
+        done += 1
+        del k, v
+        if spent >= args.cpu_seconds:
+            break
+    kvb = kv_bytes(st["context_lens"], c["num_kv_heads"], c["head_dim"], 2, layers=done)
+    return {"value": round(kvb / spent / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%d of %d layers, all %d sequences x %d tokens, fp64 oracle, %.1f s (device-to-host copies "
+                      "excluded); tokens/s over 80 layers = %.4f" % (done, L, c["num_seqs"], c["context_len"],
+                                                                    spent, c["num_seqs"] / (spent / done * 80)),
+            "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=80, help="layers of the 70B-shaped model (80 is the workload)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--eager", dest="graph", action="store_false",
+                    help="launch each call from Python instead of replaying the captured step")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path (asked for --gpus %d)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if args.layers != 80:
+        print("note: --layers %d is not the 80-layer workload; the result is for tuning only" % args.layers,
+              file=sys.stderr)
+    res = run(args)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

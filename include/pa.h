@@ -1,0 +1,256 @@
+/*
+ * pa.h -- C ABI of libpa: paged-KV-cache decode attention for AMD MI355X
+ * (gfx950), its companion cache writes and the block pool.
+ *
+ * The method (from French web pages on the KV cache and PagedAttention):
+ *  - The KV cache keeps the key and value vectors of every processed token;
+ *    they never change once written, and each decode step adds one token
+ *    per request ("Cache KV en production", opening section and section
+ *    "Un cache par requête, une mémoire commune").
+ *  - The cache is cut into fixed-size physical blocks of 16 or 32 tokens; a
+ *    per-sequence block table maps logical block i to a physical block
+ *    anywhere in device memory (ia-vox KV-cache article, section
+ *    "PagedAttention : la révolution de l'allocation mémoire"; glossary
+ *    "PagedAttention & Gestion du KV-Cache", section 2 figure).
+ *  - Decode attends with the newest token's query only (deeplearn.tn
+ *    article, section "La taille réelle du cache KV").
+ *  - Blocks are taken from a shared pool as a request grows and returned
+ *    when it ends or is cancelled; shared prefixes point at the same
+ *    blocks and are copied on write (glossary sections 3 and 4;
+ *    "Cache KV en production", sections on paging and prefix caching).
+ *
+ * Conventions for every call:
+ *  - Device pointers are HIP device memory owned by the caller; the
+ *    library never allocates or frees device memory.  Host pointers are
+ *    marked "host".
+ *  - Device calls are asynchronous on `stream` (a hipStream_t; NULL is the
+ *    null stream).  No call synchronises the host.  Faults inside a kernel
+ *    surface at the caller's next synchronisation.
+ *  - Argument errors visible on the host return PA_ERR_INVALID before any
+ *    launch; unsupported combinations return PA_ERR_UNSUPPORTED; a failed
+ *    launch returns PA_ERR_HIP.  pa_last_error() then holds a message for
+ *    the calling thread.  Nothing is thrown across the ABI.
+ *  - Contents of device arrays (table entries, slot ids, pair ids) are the
+ *    caller's responsibility; the kernels skip or clamp nothing beyond what
+ *    each call documents.
+ *  - Kernels are stateless and re-entrant; a pa_pool is not thread-safe.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = 1,     /* bad argument, detected on the host */
+  PA_ERR_UNSUPPORTED = 2, /* valid but not implemented (dtype or shape) */
+  PA_ERR_OOM = 3,         /* pool has fewer free blocks than asked */
+  PA_ERR_STATE = 4,       /* pool: free or share of a block not held */
+  PA_ERR_HIP = 5          /* a HIP runtime call failed */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2 } pa_dtype;
+
+/* Static string naming a status code. */
+const char* pa_status_string(pa_status s);
+/* Message of the last failure on the calling thread ("" if none). */
+const char* pa_last_error(void);
+/* ABI version of this header (incremented on any incompatible change). */
+#define PA_ABI_VERSION 1
+int32_t pa_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Decode attention
+ * ------------------------------------------------------------------------
+ * For every sequence s and query head h, with G = num_q_heads /
+ * num_kv_heads, kv head g = h / G and n = context_lens[s]:
+ *
+ *   K_s[t] = k_cache[block_tables[s][t / BS]][g][t % BS][:]   (same for V)
+ *   x_t    = scale * <q[s][h][:], K_s[t]>                      t = 0 .. n-1
+ *   out[s][h][:] = sum_t softmax(x)_t * V_s[t]
+ *
+ * The query of the newest token attends over all n tokens of its
+ * sequence, the newest included (write it first with
+ * pa_reshape_and_cache).  n = 0 gives a row of zeros.  For int8 caches the
+ * stored code is multiplied by the fp32 scale of its (block, kv head):
+ * K = k_scales[b][g] * code, V = v_scales[b][g] * code (the per-block form
+ * between the per-layer and per-token scales of the ia-vox article,
+ * section "Quantization du KV cache").
+ *
+ * Layouts (row-major, densely packed):
+ *   q             [num_seqs][num_q_heads][head_dim]          q_dtype
+ *   k/v_cache     [num_blocks][num_kv_heads][block_size][head_dim]  kv_dtype
+ *   k/v_scales    [num_blocks][num_kv_heads] fp32 (int8 caches only)
+ *   block_tables  [num_seqs][max_blocks_per_seq] int32; entries past
+ *                 ceil(n / BS) are never read
+ *   context_lens  [num_seqs] int32, 0 <= n <= max_blocks_per_seq * BS and
+ *                 n <= max_context_len
+ *   out           [num_seqs][num_q_heads][head_dim] fp32
+ * Slots at or beyond n inside a sequence's last block, and blocks no table
+ * names, are never read: they may hold anything, NaN included.
+ *
+ * Supported: head_dim in {64, 128}; block_size in {16, 32};
+ * q_dtype in {PA_F32, PA_BF16}; kv_dtype in {PA_F32, PA_BF16, PA_I8};
+ * out_dtype PA_F32; num_q_heads a multiple of num_kv_heads, at most 16
+ * query heads per kv head.  All of q, caches and out 16-byte aligned.
+ *
+ * Long contexts are split into partitions of `partition_tokens` tokens
+ * (0 = chosen by the library), each computed separately and merged by a
+ * second kernel; the merge needs `workspace` of at least the size
+ * pa_decode_workspace_size reports for the same arguments (it may be NULL
+ * when that size is 0).  The workspace is scratch of the call: its
+ * contents are not needed before or after it.  Two calls that run
+ * concurrently need separate workspaces.
+ *
+ * `kernel` selects the implementation: 0 = automatic, 1 = vector-ALU
+ * kernel (any supported case), 2 = matrix-core kernel (bf16 or int8
+ * caches with bf16 queries, head_dim 128, 2..16 query heads per kv head;
+ * else PA_ERR_UNSUPPORTED).  Both compute the definition above; they
+ * differ in rounding only.
+ */
+typedef struct {
+  size_t struct_size;            /* = sizeof(pa_decode_args) */
+  void* out;
+  pa_dtype out_dtype;
+  const void* q;
+  pa_dtype q_dtype;
+  const void* k_cache;
+  const void* v_cache;
+  pa_dtype kv_dtype;
+  const float* k_scales;         /* non-NULL iff kv_dtype == PA_I8 */
+  const float* v_scales;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t max_context_len;       /* host-side bound on context_lens; sizes the grid */
+  float scale;                   /* finite; usually 1/sqrt(head_dim) */
+  int32_t partition_tokens;      /* 0 = automatic; else a positive multiple of 16 */
+  int32_t kernel;                /* 0 automatic, 1 vector ALU, 2 matrix cores */
+  void* workspace;
+  size_t workspace_bytes;
+  void* stream;                  /* hipStream_t */
+} pa_decode_args;
+
+/* Host only: bytes of workspace pa_decode needs for these arguments
+ * (device pointers are not read and may be NULL).  PA_ERR_INVALID /
+ * PA_ERR_UNSUPPORTED as pa_decode would return. */
+pa_status pa_decode_workspace_size(const pa_decode_args* a, size_t* bytes);
+
+/* Launch decode attention as defined above. */
+pa_status pa_decode(const pa_decode_args* a);
+
+/* ------------------------------------------------------------------------
+ * Slot mapping: where each new token goes
+ * ------------------------------------------------------------------------
+ * slot_mapping[t] = block_tables[seq][pos / BS] * BS + pos % BS  (int64),
+ * the flat slot of logical position pos of sequence seq (glossary figure,
+ * section 2: token 40 of the table [7, 2, 11] lands in block 11, slot 8).
+ *   seq = seq_idx[t], or t when seq_idx is NULL (then num_tokens must not
+ *         exceed num_seqs);
+ *   pos = positions[t], or context_lens[seq] - 1 (the newest token of a
+ *         decode step) when positions is NULL.  Exactly one of positions
+ *         and context_lens is non-NULL.
+ * A negative position, a position past the table row, or a negative table
+ * entry gives slot -1, which pa_reshape_and_cache skips.  Device arrays:
+ * block_tables [num_seqs][max_blocks_per_seq], seq_idx / positions
+ * [num_tokens] int32, context_lens [num_seqs] int32, slot_mapping
+ * [num_tokens] int64 (written).
+ */
+pa_status pa_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          int32_t num_seqs, const int32_t* seq_idx, const int32_t* positions,
+                          const int32_t* context_lens, int32_t num_tokens, int32_t block_size,
+                          int64_t* slot_mapping, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Cache write: scatter the new tokens' keys and values into their slots
+ * ------------------------------------------------------------------------
+ * For t < num_tokens with slot = slot_mapping[t] >= 0, for every kv head h:
+ *   k_cache[slot / BS][h][slot % BS][:] = key[t][h][:]   (and value -> v_cache)
+ * Bytes are copied unchanged; nothing else in the caches is written
+ * ("Cache KV en production", section "Un cache par requête": the cache
+ * grows by one token per decode step; K and V are never rewritten).
+ * key, value [num_tokens][num_kv_heads][head_dim] of kv_dtype, caches as in
+ * pa_decode, slot_mapping [num_tokens] int64.  Slots must be distinct and
+ * below num_blocks * block_size (caller's responsibility).
+ * kv_dtype PA_I8 is PA_ERR_UNSUPPORTED (quantising writes are not built).
+ */
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                               pa_dtype kv_dtype, const int64_t* slot_mapping, int32_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Block copy for copy-on-write
+ * ------------------------------------------------------------------------
+ * For each pair p: (src, dst) = (block_pairs[2p], block_pairs[2p+1]), copy
+ * the whole physical block -- all kv heads, all block_size slots -- of
+ * k_cache and of v_cache from src to dst, and k_scales[src][:] /
+ * v_scales[src][:] likewise when given (glossary, section 3, scenario 01:
+ * shared pages are copied only when a sequence starts writing its own
+ * tokens into them).  block_pairs is device int64 [num_pairs][2].  All ids
+ * must lie in [0, num_blocks); destinations must be distinct and disjoint
+ * from the sources (caller's responsibility), so the order of the pairs
+ * does not matter.  Scales: non-NULL iff kv_dtype == PA_I8.
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, pa_dtype kv_dtype, float* k_scales,
+                         float* v_scales, const int64_t* block_pairs, int32_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t num_blocks, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Block pool (host only)
+ * ------------------------------------------------------------------------
+ * A stack of free physical block ids with a reference count per block.
+ * Blocks are taken page by page as sequences grow and go back to the
+ * common pool as soon as no sequence holds them ("Cache KV en production",
+ * section "PagedAttention : la pagination appliquée au cache KV"); a
+ * cancelled request must return its blocks or they leak (glossary,
+ * section 4); a shared prefix is held by several sequences at once
+ * (glossary, section 3, scenario 01).
+ *
+ *  pa_pool_create: ids 0..num_blocks-1, all free; initial_order (host,
+ *    NULL = 0, 1, 2, ...) is a permutation giving the order in which a
+ *    fresh pool hands them out.  *out receives a pool the caller destroys.
+ *  pa_block_alloc: all or nothing: PA_ERR_OOM (nothing changes) if fewer
+ *    than n blocks are free; else pops n ids into out_ids (host, n
+ *    entries), each with refcount 1.
+ *  pa_block_share: refcount + 1 per entry of ids (host, n entries): one
+ *    more sequence points at the block.
+ *  pa_block_free: refcount - 1 per entry, in order; a block whose count
+ *    reaches 0 is pushed back on the free stack at once (last freed is
+ *    the next handed out).
+ *  Share and free validate the whole call first: an id outside
+ *  [0, num_blocks) is PA_ERR_INVALID (reported before any other error);
+ *  sharing a free block, or freeing a block more times than it is held,
+ *  is PA_ERR_STATE; nothing changes on error.  n = 0 is a no-op; n < 0 is
+ *  PA_ERR_INVALID.
+ */
+typedef struct pa_pool pa_pool;
+
+pa_status pa_pool_create(int32_t num_blocks, const int32_t* initial_order, pa_pool** out);
+void pa_pool_destroy(pa_pool* p);
+pa_status pa_block_alloc(pa_pool* p, int32_t n, int32_t* out_ids);
+pa_status pa_block_share(pa_pool* p, int32_t n, const int32_t* ids);
+pa_status pa_block_free(pa_pool* p, int32_t n, const int32_t* ids);
+/* Reference count of block id, or -1 if id is out of range or p is NULL. */
+int32_t pa_block_refcount(const pa_pool* p, int32_t id);
+/* Number of free blocks, or -1 if p is NULL. */
+int32_t pa_pool_num_free(const pa_pool* p);
+int32_t pa_pool_num_blocks(const pa_pool* p);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -74,6 +74,8 @@ def _bind(lib):
     lib.oracle_copy_blocks.restype = i32
     lib.oracle_quantize_int8.argtypes = [P, P, P, P, i32, i32, i32, i32]
     lib.oracle_quantize_int8.restype = None
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
     return lib
 
 
@@ -127,6 +129,11 @@ def as_float64(a: np.ndarray) -> np.ndarray:
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     return a.astype(np.float64)
+
+
+def num_threads() -> int:
+    """Threads the C oracle's decode loop uses (OpenMP maximum)."""
+    return int(_load().oracle_num_threads())
 
 
 # --------------------------------------------------------------------------

@@ -35,6 +35,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define OR_F32 0
 #define OR_BF16 1
@@ -59,6 +62,15 @@ static double elem_as_double(const void* base, int64_t idx, int dtype) {
   }
   /* int8 */
   return (double)((const int8_t*)base)[idx];
+}
+
+/* Threads the decode loop may use (OpenMP's current maximum). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }
 
 int oracle_elem_bytes(int dtype) {

@@ -1,0 +1,399 @@
+"""Python binding of libpa (paged-KV-cache decode for MI355X).
+
+Argument marshalling only: every entry point hands torch tensors' device
+pointers, shapes and the current HIP stream to the C ABI declared in
+``include/pa.h``; all work runs in the library's kernels.  PyTorch supplies
+device memory and streams.  There is no fallback: if ``libpa.so`` is not
+built, importing the binding's functions raises.
+
+Build the library with ``python -m paged_kv_cache_192_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_OOM, PA_ERR_STATE, PA_ERR_HIP = range(6)
+PA_F32, PA_BF16, PA_I8 = 0, 1, 2
+KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
+
+STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_OOM",
+                4: "PA_ERR_STATE", 5: "PA_ERR_HIP"}
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (STATUS_NAMES.get(status, status), message))
+        self.status = status
+        self.message = message
+
+
+class DecodeArgs(ctypes.Structure):
+    """Mirror of ``pa_decode_args`` (field order and types as in pa.h)."""
+
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("out", ctypes.c_void_p),
+        ("out_dtype", ctypes.c_int),
+        ("q", ctypes.c_void_p),
+        ("q_dtype", ctypes.c_int),
+        ("k_cache", ctypes.c_void_p),
+        ("v_cache", ctypes.c_void_p),
+        ("kv_dtype", ctypes.c_int),
+        ("k_scales", ctypes.c_void_p),
+        ("v_scales", ctypes.c_void_p),
+        ("block_tables", ctypes.c_void_p),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("context_lens", ctypes.c_void_p),
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_context_len", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("partition_tokens", ctypes.c_int32),
+        ("kernel", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libpa.so (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libpa.so is not built (%s); run `python -m paged_kv_cache_192_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_last_error.argtypes = []
+    lib.pa_last_error.restype = ctypes.c_char_p
+    lib.pa_abi_version.argtypes = []
+    lib.pa_abi_version.restype = i32
+    lib.pa_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_size_t)]
+    lib.pa_decode_workspace_size.restype = ctypes.c_int
+    lib.pa_decode.argtypes = [ctypes.POINTER(DecodeArgs)]
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_slot_mapping.argtypes = [P, i32, i32, P, P, P, i32, i32, P, P]
+    lib.pa_slot_mapping.restype = ctypes.c_int
+    lib.pa_reshape_and_cache.argtypes = [P, P, P, P, ctypes.c_int, P, i32, i32, i32, i32, i32, P]
+    lib.pa_reshape_and_cache.restype = ctypes.c_int
+    lib.pa_copy_blocks.argtypes = [P, P, ctypes.c_int, P, P, P, i32, i32, i32, i32, i32, P]
+    lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_pool_create.argtypes = [i32, P, ctypes.POINTER(ctypes.c_void_p)]
+    lib.pa_pool_create.restype = ctypes.c_int
+    lib.pa_pool_destroy.argtypes = [P]
+    lib.pa_pool_destroy.restype = None
+    lib.pa_block_alloc.argtypes = [P, i32, P]
+    lib.pa_block_alloc.restype = ctypes.c_int
+    lib.pa_block_share.argtypes = [P, i32, P]
+    lib.pa_block_share.restype = ctypes.c_int
+    lib.pa_block_free.argtypes = [P, i32, P]
+    lib.pa_block_free.restype = ctypes.c_int
+    lib.pa_block_refcount.argtypes = [P, i32]
+    lib.pa_block_refcount.restype = i32
+    lib.pa_pool_num_free.argtypes = [P]
+    lib.pa_pool_num_free.restype = i32
+    lib.pa_pool_num_blocks.argtypes = [P]
+    lib.pa_pool_num_blocks.restype = i32
+    del i64
+    if lib.pa_abi_version() != 1:
+        raise RuntimeError("libpa ABI version %d, binding expects 1" % lib.pa_abi_version())
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != PA_OK:
+        raise PaError(status, library().pa_last_error().decode(errors="replace"))
+
+
+def _torch():
+    import torch  # noqa: PLC0415
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    codes = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8}
+    try:
+        return codes[t.dtype]
+    except KeyError:
+        raise TypeError("unsupported tensor dtype %s (float32, bfloat16 or int8)" % t.dtype)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+# --------------------------------------------------------------------------
+# decode
+# --------------------------------------------------------------------------
+
+def make_decode_args(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int,
+                     out=None, k_scales=None, v_scales=None, workspace=None, partition_tokens: int = 0,
+                     kernel: int = KERNEL_AUTO, stream=None, device_pointers: bool = True) -> DecodeArgs:
+    """Fill a DecodeArgs from tensors.  q ``[S][Hq][D]``; caches
+    ``[NB][Hkv][BS][D]``; block_tables int32 ``[S][max_blocks]``;
+    context_lens int32 ``[S]``; out float32 ``[S][Hq][D]``."""
+    S, Hq, D = q.shape
+    NB, Hkv, BS, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes %s / %s do not match q %s" % (tuple(k_cache.shape), tuple(v_cache.shape),
+                                                                      tuple(q.shape)))
+    a = DecodeArgs()
+    a.struct_size = ctypes.sizeof(DecodeArgs)
+    get = _ptr if device_pointers else (lambda t: None if t is None else t.data_ptr())
+    a.out = get(out)
+    a.out_dtype = PA_F32 if out is None else _dtype_code(out)
+    a.q = get(q)
+    a.q_dtype = _dtype_code(q)
+    a.k_cache = get(k_cache)
+    a.v_cache = get(v_cache)
+    a.kv_dtype = _dtype_code(k_cache)
+    a.k_scales = get(k_scales)
+    a.v_scales = get(v_scales)
+    a.block_tables = get(block_tables)
+    a.max_blocks_per_seq = int(block_tables.shape[1])
+    a.context_lens = get(context_lens)
+    a.num_seqs = S
+    a.num_q_heads = Hq
+    a.num_kv_heads = Hkv
+    a.head_dim = D
+    a.block_size = BS
+    a.num_blocks = NB
+    a.max_context_len = int(max_context_len)
+    a.scale = float(scale)
+    a.partition_tokens = int(partition_tokens)
+    a.kernel = int(kernel)
+    a.workspace = get(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a.stream = _stream(stream) if device_pointers else None
+    return a
+
+
+def decode_workspace_size(args: DecodeArgs) -> int:
+    n = ctypes.c_size_t(0)
+    _check(library().pa_decode_workspace_size(ctypes.byref(args), ctypes.byref(n)))
+    return n.value
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int, out=None,
+           k_scales=None, v_scales=None, workspace=None, partition_tokens: int = 0, kernel: int = KERNEL_AUTO,
+           stream=None):
+    """Paged decode attention (``pa_decode``).  Returns ``out`` (float32
+    ``[S][Hq][D]``), allocated on q's device when not given.  A workspace is
+    allocated when needed and none is passed."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    args = make_decode_args(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, out=out,
+                            k_scales=k_scales, v_scales=v_scales, workspace=workspace,
+                            partition_tokens=partition_tokens, kernel=kernel, stream=stream)
+    need = decode_workspace_size(args)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        args.workspace = workspace.data_ptr()
+        args.workspace_bytes = need
+    _check(library().pa_decode(ctypes.byref(args)))
+    return out
+
+
+# --------------------------------------------------------------------------
+# slot mapping, cache writes, copies
+# --------------------------------------------------------------------------
+
+def slot_mapping(block_tables, block_size: int, positions=None, context_lens=None, seq_idx=None, out=None,
+                 stream=None):
+    """``pa_slot_mapping``: int64 slot of each new token (-1 = none)."""
+    torch = _torch()
+    T = (positions if positions is not None else (seq_idx if seq_idx is not None else context_lens)).shape[0]
+    if out is None:
+        out = torch.empty(T, dtype=torch.int64, device=block_tables.device)
+    _check(library().pa_slot_mapping(_ptr(block_tables), int(block_tables.shape[1]), int(block_tables.shape[0]),
+                                     _ptr(seq_idx), _ptr(positions), _ptr(context_lens), T, int(block_size),
+                                     _ptr(out), _stream(stream)))
+    return out
+
+
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None) -> None:
+    """``pa_reshape_and_cache``: key/value ``[T][Hkv][D]`` into their slots."""
+    NB, Hkv, BS, D = k_cache.shape
+    T = key.shape[0]
+    if tuple(key.shape) != (T, Hkv, D) or tuple(value.shape) != (T, Hkv, D):
+        raise ValueError("key/value must be [T][%d][%d]" % (Hkv, D))
+    if key.dtype != k_cache.dtype or value.dtype != v_cache.dtype:
+        raise TypeError("key/value dtype must match the caches")
+    _check(library().pa_reshape_and_cache(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+                                          _dtype_code(k_cache), _ptr(slot_mapping), T, Hkv, D, BS, NB,
+                                          _stream(stream)))
+
+
+def copy_blocks(k_cache, v_cache, block_pairs, k_scales=None, v_scales=None, stream=None) -> None:
+    """``pa_copy_blocks``: block_pairs int64 ``[P][2]`` of (src, dst)."""
+    NB, Hkv, BS, D = k_cache.shape
+    P = block_pairs.shape[0]
+    _check(library().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), _ptr(k_scales),
+                                    _ptr(v_scales), _ptr(block_pairs), P, Hkv, D, BS, NB, _stream(stream)))
+
+
+# --------------------------------------------------------------------------
+# block pool (host)
+# --------------------------------------------------------------------------
+
+class BlockPool:
+    """Host block pool (``pa_pool``): stack of free ids with refcounts."""
+
+    def __init__(self, num_blocks: int, initial_order: Optional[Sequence[int]] = None):
+        lib = library()
+        h = ctypes.c_void_p()
+        order = None
+        if initial_order is not None:
+            order = (ctypes.c_int32 * num_blocks)(*[int(i) for i in initial_order])
+        _check(lib.pa_pool_create(int(num_blocks), order, ctypes.byref(h)))
+        self._h = h
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            library().pa_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass
+
+    def alloc(self, n: int):
+        ids = (ctypes.c_int32 * max(n, 1))()
+        _check(library().pa_block_alloc(self._h, int(n), ids))
+        return list(ids[:n])
+
+    def _ids(self, ids):
+        arr = (ctypes.c_int32 * max(len(ids), 1))(*[int(i) for i in ids])
+        return len(ids), arr
+
+    def free(self, ids) -> None:
+        n, arr = self._ids(ids)
+        _check(library().pa_block_free(self._h, n, arr))
+
+    def share(self, ids) -> None:
+        n, arr = self._ids(ids)
+        _check(library().pa_block_share(self._h, n, arr))
+
+    def status_of(self, op: str, ids) -> int:
+        """Raw status of alloc/free/share without raising (for tests)."""
+        lib = library()
+        if op == "alloc":
+            out = (ctypes.c_int32 * max(int(ids), 1))()
+            return lib.pa_block_alloc(self._h, int(ids), out)
+        n, arr = self._ids(ids)
+        return (lib.pa_block_free if op == "free" else lib.pa_block_share)(self._h, n, arr)
+
+    def refcount(self, i: int) -> int:
+        return library().pa_block_refcount(self._h, int(i))
+
+    def num_free(self) -> int:
+        return library().pa_pool_num_free(self._h)
+
+    @property
+    def num_blocks(self) -> int:
+        return library().pa_pool_num_blocks(self._h)
+
+
+# --------------------------------------------------------------------------
+# prepared calls: arguments marshalled once, launched many times (decode
+# loops, graph capture).  The stream is fixed when the call is prepared.
+# --------------------------------------------------------------------------
+
+class PreparedDecode:
+    """``pa_decode`` with its arguments packed once.  A workspace is
+    allocated here when the plan needs one and none is given."""
+
+    def __init__(self, q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int, out,
+                 k_scales=None, v_scales=None, workspace=None, partition_tokens: int = 0, kernel: int = KERNEL_AUTO,
+                 stream=None):
+        torch = _torch()
+        self.args = make_decode_args(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                                     out=out, k_scales=k_scales, v_scales=v_scales, workspace=workspace,
+                                     partition_tokens=partition_tokens, kernel=kernel, stream=stream)
+        need = decode_workspace_size(self.args)
+        if need and (workspace is None or self.args.workspace_bytes < need):
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            self.args.workspace = workspace.data_ptr()
+            self.args.workspace_bytes = need
+        self.workspace_bytes = need
+        self._keep = (q, k_cache, v_cache, block_tables, context_lens, out, k_scales, v_scales, workspace)
+        self._fn = library().pa_decode
+        self._ref = ctypes.byref(self.args)
+
+    def __call__(self) -> None:
+        st = self._fn(self._ref)
+        if st != PA_OK:
+            _check(st)
+
+
+class PreparedCall:
+    """Any other entry point with its argument tuple packed once."""
+
+    def __init__(self, name: str, args: tuple, keep: tuple = ()):
+        self._fn = getattr(library(), name)
+        self._args = args
+        self._keep = keep
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != PA_OK:
+            _check(st)
+
+
+def prepare_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None) -> PreparedCall:
+    NB, Hkv, BS, D = k_cache.shape
+    T = key.shape[0]
+    if tuple(key.shape) != (T, Hkv, D) or tuple(value.shape) != (T, Hkv, D):
+        raise ValueError("key/value must be [T][%d][%d]" % (Hkv, D))
+    args = (_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), _ptr(slot_mapping), T, Hkv,
+            D, BS, NB, _stream(stream))
+    return PreparedCall("pa_reshape_and_cache", args, (key, value, k_cache, v_cache, slot_mapping))
+
+
+def prepare_slot_mapping(block_tables, block_size: int, out, positions=None, context_lens=None, seq_idx=None,
+                         stream=None) -> PreparedCall:
+    T = out.shape[0]
+    args = (_ptr(block_tables), int(block_tables.shape[1]), int(block_tables.shape[0]), _ptr(seq_idx),
+            _ptr(positions), _ptr(context_lens), T, int(block_size), _ptr(out), _stream(stream))
+    return PreparedCall("pa_slot_mapping", args, (block_tables, out, positions, context_lens, seq_idx))
+
+
+def prepare_copy_blocks(k_cache, v_cache, block_pairs, k_scales=None, v_scales=None, stream=None) -> PreparedCall:
+    NB, Hkv, BS, D = k_cache.shape
+    args = (_ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), _ptr(k_scales), _ptr(v_scales), _ptr(block_pairs),
+            int(block_pairs.shape[0]), Hkv, D, BS, NB, _stream(stream))
+    return PreparedCall("pa_copy_blocks", args, (k_cache, v_cache, block_pairs, k_scales, v_scales))

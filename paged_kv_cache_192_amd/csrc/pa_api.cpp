@@ -1,0 +1,230 @@
+// Host side of libpa: status strings, per-thread error messages, argument
+// validation and the decode plan (which kernel, how the context is split),
+// then the launches.  No device memory is allocated here.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+static thread_local char g_last_error[512] = "";
+
+pa_status fail(pa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+pa_status hip_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static bool valid_dtype(int t) { return t == PA_F32 || t == PA_BF16 || t == PA_I8; }
+
+// Waves a decode launch should put on the chip: about ten per compute unit
+// of a 256-CU MI355X keeps enough loads in flight to cover HBM latency
+// while every work item still runs in a single round.
+static const int kTargetItems = 2560;
+
+pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
+  if (!a) return fail(PA_ERR_INVALID, "pa_decode: args is NULL");
+  if (a->struct_size != sizeof(pa_decode_args))
+    return fail(PA_ERR_INVALID, "pa_decode: struct_size %zu, expected %zu (ABI mismatch)",
+                a->struct_size, sizeof(pa_decode_args));
+  if (a->num_seqs < 0) return fail(PA_ERR_INVALID, "pa_decode: num_seqs < 0");
+  if (a->num_q_heads <= 0 || a->num_kv_heads <= 0 || a->head_dim <= 0 || a->block_size <= 0 ||
+      a->num_blocks <= 0 || a->max_blocks_per_seq <= 0)
+    return fail(PA_ERR_INVALID, "pa_decode: head counts, head_dim, block_size, num_blocks and "
+                                "max_blocks_per_seq must be positive");
+  if (a->num_q_heads % a->num_kv_heads)
+    return fail(PA_ERR_INVALID, "pa_decode: num_q_heads %d is not a multiple of num_kv_heads %d",
+                a->num_q_heads, a->num_kv_heads);
+  const int G = a->num_q_heads / a->num_kv_heads;
+  if (G > 16) return fail(PA_ERR_UNSUPPORTED, "pa_decode: %d query heads per kv head (max 16)", G);
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(PA_ERR_INVALID, "pa_decode: head_dim %d not in {64, 128}", a->head_dim);
+  if (a->block_size != 16 && a->block_size != 32)
+    return fail(PA_ERR_INVALID, "pa_decode: block_size %d not in {16, 32}", a->block_size);
+  if (!valid_dtype(a->q_dtype) || !valid_dtype(a->kv_dtype) || !valid_dtype(a->out_dtype))
+    return fail(PA_ERR_INVALID, "pa_decode: unknown dtype code");
+  if (a->out_dtype != PA_F32) return fail(PA_ERR_UNSUPPORTED, "pa_decode: out_dtype must be PA_F32");
+  if (a->q_dtype == PA_I8) return fail(PA_ERR_UNSUPPORTED, "pa_decode: int8 queries");
+  const bool i8 = a->kv_dtype == PA_I8;
+  if (i8 != (a->k_scales != nullptr) || i8 != (a->v_scales != nullptr))
+    return fail(PA_ERR_INVALID, "pa_decode: k_scales/v_scales must be given exactly for int8 caches");
+  if (!std::isfinite(a->scale)) return fail(PA_ERR_INVALID, "pa_decode: scale is not finite");
+  if (a->max_context_len < 0 || (int64_t)a->max_context_len > (int64_t)a->max_blocks_per_seq * a->block_size)
+    return fail(PA_ERR_INVALID, "pa_decode: max_context_len %d outside [0, max_blocks_per_seq*block_size]",
+                a->max_context_len);
+  if (a->partition_tokens < 0 || a->partition_tokens % 16 || a->partition_tokens > 64 * a->block_size)
+    return fail(PA_ERR_INVALID, "pa_decode: partition_tokens %d is not a multiple of 16 in [0, 64*block_size]",
+                a->partition_tokens);
+  if (a->kernel < 0 || a->kernel > 2) return fail(PA_ERR_INVALID, "pa_decode: kernel %d not in {0, 1, 2}", a->kernel);
+
+  const bool mfma_ok = a->q_dtype == PA_BF16 && (a->kv_dtype == PA_BF16 || a->kv_dtype == PA_I8) &&
+                       a->head_dim == 128;
+  KernelKind kind;
+  if (a->kernel == KERNEL_MFMA) {
+    if (!mfma_ok)
+      return fail(PA_ERR_UNSUPPORTED, "pa_decode: matrix-core kernel needs bf16 queries, bf16 or int8 "
+                                      "caches and head_dim 128");
+    kind = KERNEL_MFMA;
+  } else if (a->kernel == KERNEL_VALU) {
+    kind = KERNEL_VALU;
+  } else {
+    kind = (mfma_ok && G >= 4) ? KERNEL_MFMA : KERNEL_VALU;
+  }
+
+  p->kind = kind;
+  p->G = G;
+  int hpw = 1;
+  while (hpw < G && hpw < 8) hpw *= 2;
+  p->heads_per_wave = kind == KERNEL_VALU ? hpw : G;
+  p->head_groups = kind == KERNEL_VALU ? (G + hpw - 1) / hpw : 1;
+
+  const int64_t tiles = a->max_context_len > 0 ? (a->max_context_len + 15) / 16 : 1;
+  int P = a->partition_tokens;
+  if (P == 0) {
+    const int64_t waves_per_partition = (int64_t)(a->num_seqs > 0 ? a->num_seqs : 1) *
+                                        a->num_kv_heads * p->head_groups;
+    int64_t per_item = (tiles * waves_per_partition + kTargetItems - 1) / kTargetItems;
+    if (per_item < 4) per_item = 4;
+    if (per_item > tiles) per_item = tiles;
+    // a partition spans at most 64 blocks (one table entry per lane)
+    if (per_item > 4 * a->block_size) per_item = 4 * a->block_size;
+    P = (int)(16 * per_item);
+  }
+  p->partition_tokens = P;
+  p->num_partitions = a->max_context_len > 0 ? (a->max_context_len + P - 1) / P : 1;
+  p->workspace_bytes = 0;
+  if (p->num_partitions > 1) {
+    p->workspace_bytes = ws_ml_bytes(a->num_seqs, a->num_q_heads, p->num_partitions) +
+                         (size_t)a->num_seqs * a->num_q_heads * p->num_partitions * a->head_dim * sizeof(float);
+  }
+  return PA_OK;
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID: return "PA_ERR_INVALID";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_OOM: return "PA_ERR_OOM";
+    case PA_ERR_STATE: return "PA_ERR_STATE";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+  }
+  return "PA_ERR_UNKNOWN";
+}
+
+const char* pa_last_error(void) { return g_last_error; }
+
+int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
+
+pa_status pa_decode_workspace_size(const pa_decode_args* a, size_t* bytes) {
+  DecodePlan p;
+  if (!bytes) return fail(PA_ERR_INVALID, "pa_decode_workspace_size: bytes is NULL");
+  pa_status s = plan_decode(a, &p);
+  if (s != PA_OK) return s;
+  *bytes = p.workspace_bytes;
+  return PA_OK;
+}
+
+pa_status pa_decode(const pa_decode_args* a) {
+  DecodePlan p;
+  pa_status s = plan_decode(a, &p);
+  if (s != PA_OK) return s;
+  if (a->num_seqs == 0) return PA_OK;
+  if (!a->out || !a->q || !a->k_cache || !a->v_cache || !a->block_tables || !a->context_lens)
+    return fail(PA_ERR_INVALID, "pa_decode: a required device pointer is NULL");
+  if (!aligned(a->out, 16) || !aligned(a->q, 16) || !aligned(a->k_cache, 16) || !aligned(a->v_cache, 16))
+    return fail(PA_ERR_INVALID, "pa_decode: out, q and the caches must be 16-byte aligned");
+  if (!aligned(a->block_tables, 4) || !aligned(a->context_lens, 4) ||
+      (a->k_scales && (!aligned(a->k_scales, 4) || !aligned(a->v_scales, 4))))
+    return fail(PA_ERR_INVALID, "pa_decode: tables, lengths and scales must be 4-byte aligned");
+  if (p.workspace_bytes) {
+    if (!a->workspace || a->workspace_bytes < p.workspace_bytes)
+      return fail(PA_ERR_INVALID, "pa_decode: workspace of %zu bytes needed, %zu given", p.workspace_bytes,
+                  a->workspace ? a->workspace_bytes : (size_t)0);
+    if (!aligned(a->workspace, 16)) return fail(PA_ERR_INVALID, "pa_decode: workspace must be 16-byte aligned");
+  }
+  hipStream_t st = (hipStream_t)a->stream;
+  s = p.kind == KERNEL_MFMA ? launch_decode_mfma(a, p, st) : launch_decode_valu(a, p, st);
+  if (s != PA_OK) return s;
+  if (p.num_partitions > 1) s = launch_decode_reduce(a, p, st);
+  return s;
+}
+
+pa_status pa_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
+                          const int32_t* seq_idx, const int32_t* positions, const int32_t* context_lens,
+                          int32_t num_tokens, int32_t block_size, int64_t* slot_mapping, void* stream) {
+  if (num_tokens < 0 || num_seqs < 0) return fail(PA_ERR_INVALID, "pa_slot_mapping: negative count");
+  if (max_blocks_per_seq <= 0 || block_size <= 0)
+    return fail(PA_ERR_INVALID, "pa_slot_mapping: max_blocks_per_seq and block_size must be positive");
+  if ((positions == nullptr) == (context_lens == nullptr))
+    return fail(PA_ERR_INVALID, "pa_slot_mapping: give exactly one of positions and context_lens");
+  if (!seq_idx && num_tokens > num_seqs)
+    return fail(PA_ERR_INVALID, "pa_slot_mapping: without seq_idx, num_tokens (%d) must not exceed num_seqs (%d)",
+                num_tokens, num_seqs);
+  if (num_tokens == 0) return PA_OK;
+  if (!block_tables || !slot_mapping) return fail(PA_ERR_INVALID, "pa_slot_mapping: NULL device pointer");
+  return launch_slot_mapping(block_tables, max_blocks_per_seq, num_seqs, seq_idx, positions, context_lens, num_tokens,
+                             block_size, slot_mapping, (hipStream_t)stream);
+}
+
+static pa_status check_cache_shape(const char* fn, pa_dtype kv, int32_t Hkv, int32_t D, int32_t BS, int32_t NB) {
+  if (!valid_dtype(kv)) return fail(PA_ERR_INVALID, "%s: unknown dtype code", fn);
+  if (Hkv <= 0 || NB <= 0) return fail(PA_ERR_INVALID, "%s: num_kv_heads and num_blocks must be positive", fn);
+  if (D != 64 && D != 128) return fail(PA_ERR_INVALID, "%s: head_dim %d not in {64, 128}", fn, D);
+  if (BS != 16 && BS != 32) return fail(PA_ERR_INVALID, "%s: block_size %d not in {16, 32}", fn, BS);
+  return PA_OK;
+}
+
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache, pa_dtype kv_dtype,
+                               const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t num_blocks, void* stream) {
+  pa_status s = check_cache_shape("pa_reshape_and_cache", kv_dtype, num_kv_heads, head_dim, block_size, num_blocks);
+  if (s != PA_OK) return s;
+  if (num_tokens < 0) return fail(PA_ERR_INVALID, "pa_reshape_and_cache: num_tokens < 0");
+  if (kv_dtype == PA_I8)
+    return fail(PA_ERR_UNSUPPORTED, "pa_reshape_and_cache: int8 caches need a quantising write (not built)");
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+    return fail(PA_ERR_INVALID, "pa_reshape_and_cache: NULL device pointer");
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 8))
+    return fail(PA_ERR_INVALID, "pa_reshape_and_cache: key, value and caches must be 16-byte aligned");
+  return launch_reshape_and_cache(key, value, k_cache, v_cache, dtype_bytes(kv_dtype), slot_mapping, num_tokens,
+                                  num_kv_heads, head_dim, block_size, num_blocks, (hipStream_t)stream);
+}
+
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, pa_dtype kv_dtype, float* k_scales, float* v_scales,
+                         const int64_t* block_pairs, int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, void* stream) {
+  pa_status s = check_cache_shape("pa_copy_blocks", kv_dtype, num_kv_heads, head_dim, block_size, num_blocks);
+  if (s != PA_OK) return s;
+  if (num_pairs < 0) return fail(PA_ERR_INVALID, "pa_copy_blocks: num_pairs < 0");
+  const bool i8 = kv_dtype == PA_I8;
+  if (i8 != (k_scales != nullptr) || i8 != (v_scales != nullptr))
+    return fail(PA_ERR_INVALID, "pa_copy_blocks: k_scales/v_scales must be given exactly for int8 caches");
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_pairs) return fail(PA_ERR_INVALID, "pa_copy_blocks: NULL device pointer");
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_pairs, 8))
+    return fail(PA_ERR_INVALID, "pa_copy_blocks: caches must be 16-byte aligned");
+  return launch_copy_blocks(k_cache, v_cache, dtype_bytes(kv_dtype), k_scales, v_scales, block_pairs, num_pairs,
+                            num_kv_heads, head_dim, block_size, num_blocks, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,721 @@
+// Paged decode attention for gfx950.
+//
+// What is computed (the definition restated in pa.h): for each sequence s
+// and query head h, the newest token's query attends over the n tokens of
+// its sequence, which a block table scatters over fixed-size physical
+// blocks ("Cache KV en production", opening section and section on paging;
+// glossary "PagedAttention & Gestion du KV-Cache", section 2 figure).
+// Decode reads every cached key and value once per step and does little
+// arithmetic per byte, so it is bound by HBM bandwidth (forum thread, post
+// of 17:05; deeplearn.tn article, section "Le compromis fondamental").
+//
+// Work decomposition: one wave per (sequence, kv head, partition of the
+// context); the partition's tokens are processed in tiles of 16.  With
+// more than one partition each wave leaves (m, l, acc) in the workspace and
+// decode_reduce_kernel merges them; with one partition the wave writes the
+// output row directly.
+//
+// Softmax bookkeeping is in log2 units: x = log2(e) * scale * <q, k>, weights
+// exp2(x - m).  m is a per-head reference value, moved only when a score
+// exceeds it by more than kRescaleThreshold (results are exact for any
+// reference; the threshold bounds weights by 2^8 and makes rescaling of
+// the accumulators rare).
+#include "pa_internal.h"
+
+namespace pa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleThreshold = 8.0f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Streaming loads: every cached byte is read once per step, so they bypass
+// reuse in the caches (non-temporal hint).
+__device__ __forceinline__ u32x4_t ld16(const void* p) { return __builtin_nontemporal_load((const u32x4_t*)p); }
+__device__ __forceinline__ u32x2_t ld8(const void* p) { return __builtin_nontemporal_load((const u32x2_t*)p); }
+__device__ __forceinline__ unsigned ld4(const void* p) { return __builtin_nontemporal_load((const unsigned*)p); }
+
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+// signed byte k of w as float
+__device__ __forceinline__ float i8_at(unsigned w, int k) { return (float)(int)(signed char)(w >> (8 * k)); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the total.
+__device__ __forceinline__ float row_sum16(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));  // row_ror:8
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));  // row_ror:4
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false));  // row_ror:2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false));  // row_ror:1
+  return x;
+}
+
+// Reductions across the four 16-lane rows (lanes l, l^16, l^32, l^48) with
+// the gfx950 row-swap instructions: permlane16_swap exchanges odd and even
+// rows, permlane32_swap the two wave halves; combining both returned copies
+// gives every lane the result for its column.
+__device__ __forceinline__ float swap16_max(float x) {
+  const u32x2_t r = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane16_swap(__float_as_uint(x),
+                                                                                  __float_as_uint(x), false, false));
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap32_max(float x) {
+  const u32x2_t r = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                                                  __float_as_uint(x), false, false));
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap16_sum(float x) {
+  const u32x2_t r = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane16_swap(__float_as_uint(x),
+                                                                                  __float_as_uint(x), false, false));
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap32_sum(float x) {
+  const u32x2_t r = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                                                  __float_as_uint(x), false, false));
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor_max_rows(float x) { return swap32_max(swap16_max(x)); }
+__device__ __forceinline__ float xor_sum_rows(float x) { return swap32_sum(swap16_sum(x)); }
+
+// ===========================================================================
+// Matrix-core kernel: bf16 or int8 cache, bf16 queries, head_dim 128,
+// up to 16 query heads per kv head.
+//
+// Per 16-token tile:
+//  * scores S[t][h] = K[t][:] . q[h][:] with four v_mfma_f32_16x16x32_bf16:
+//    A = K tile (row = token, read straight from HBM), B = the group's
+//    queries (column = head; columns >= G hold zeros).  Lane l receives the
+//    scores of head l%16 for tokens 4*(l/16) + r, r = 0..3.
+//  * weights P = exp2(x - m) stay in fp32 and are split into bf16 hi + lo
+//    parts so the P.V product keeps ~16 significant bits of P.
+//  * O^T[d][h] += V^T[d][t] P^T[t][h] with v_mfma_f32_16x16x16bf16_1k: the
+//    B operand is P in exactly the layout the score MFMA produced; the A
+//    operand wants four tokens of one d per lane, which each lane builds
+//    from its four 16-byte V rows with v_perm_b32 (no LDS round trip).
+//    MFMA e (0..7) covers d = 8*c + e for c = 0..15, so lane l ends with
+//    head l%16 and the 32 contiguous d = 32*(l/16) .. +31.
+// ===========================================================================
+
+template <bool I8>
+struct MfmaTile {
+  // K: bf16 -> 4 x 16 B per lane (row l%16, d-chunks kk*4 + l/16);
+  //    int8 -> 2 x 16 B per lane (row l%16, d = 32*(l/16) .. +31).
+  u32x4_t k[I8 ? 2 : 4];
+  // V: rows 4*(l/16) + i, d = 8*(l%16) .. +7: bf16 -> 16 B per row, int8 -> 8 B.
+  u32x4_t v[4];
+};
+
+// base: the tile's first row in the (block, kv head) chunk (wave-uniform);
+// koff / voff: this lane's byte offsets, the same for every tile.
+template <bool I8>
+__device__ __forceinline__ void mfma_load_tile(MfmaTile<I8>& T, const char* kbase, const char* vbase, unsigned koff,
+                                               unsigned voff) {
+  constexpr int ROW = I8 ? 128 : 256;  // bytes per cached token row (head_dim 128)
+  if (I8) {
+    T.k[0] = ld16(kbase + koff);
+    T.k[1] = ld16(kbase + koff + 16);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) T.k[kk] = ld16(kbase + koff + kk * 64);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (I8) {
+      u32x2_t w = ld8(vbase + voff + i * ROW);
+      T.v[i] = u32x4_t{w[0], w[1], 0u, 0u};
+    } else {
+      T.v[i] = ld16(vbase + voff + i * ROW);
+    }
+  }
+}
+
+// int8 -> bf16 for 4 consecutive codes packed in w: exact (|code| <= 127 fits
+// bf16's 8-bit significand), so the float's upper half is the bf16.
+__device__ __forceinline__ u32x2_t i8x4_to_bf16x4(unsigned w) {
+  const unsigned f0 = __float_as_uint(i8_at(w, 0)), f1 = __float_as_uint(i8_at(w, 1));
+  const unsigned f2 = __float_as_uint(i8_at(w, 2)), f3 = __float_as_uint(i8_at(w, 3));
+  return u32x2_t{__builtin_amdgcn_perm(f1, f0, 0x07060302u), __builtin_amdgcn_perm(f3, f2, 0x07060302u)};
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t w) { return __builtin_bit_cast(bf16x8_t, w); }
+__device__ __forceinline__ i16x4_t as_i16x4(unsigned a, unsigned b) {
+  return __builtin_bit_cast(i16x4_t, u32x2_t{a, b});
+}
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  return (unsigned)__builtin_bit_cast(unsigned short, (__bf16)lo) |
+         ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)hi) << 16);
+}
+
+template <bool I8, int BS>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(
+    float* __restrict__ out, float2* __restrict__ ws_ml, float* __restrict__ ws_acc,
+    const unsigned short* __restrict__ q, const char* __restrict__ k_cache, const char* __restrict__ v_cache,
+    const float* __restrict__ k_scales, const float* __restrict__ v_scales, const int32_t* __restrict__ tables,
+    int max_blocks, const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int NB, float qk_log2,
+    int P, int nP) {
+  constexpr int D = 128;
+  constexpr int E = I8 ? 1 : 2;
+  const int lane = threadIdx.x;
+  const int j = lane >> 4;
+  const int c = lane & 15;
+  const int p = blockIdx.x % nP;
+  const int sg = blockIdx.x / nP;
+  const int g = sg % Hkv;
+  const int s = sg / Hkv;
+  // a length past the table row is a caller error; never read beyond the row
+  const int n = min(context_lens[s], max_blocks * BS);
+  const int t_begin = p * P;
+  const int t_end = min(n, t_begin + P);
+  const bool head_ok = c < G;
+  const int h = g * G + c;
+
+  if (t_begin >= t_end) {
+    // Nothing to attend to.  With one partition the output row is zero;
+    // otherwise the merge skips partitions past the context.
+    if (nP == 1 && head_ok) {
+      float4* o = (float4*)(out + ((size_t)s * Hq + h) * D + 32 * j);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = float4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
+
+  // Queries of the group as the B operand: column = head c, the 8 values of
+  // d-chunk (kk*4 + j) [bf16 cache] or (j*4 + kk) [int8 cache].
+  bf16x8_t qf[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int chunk = I8 ? j * 4 + kk : kk * 4 + j;
+    u32x4_t w = {0u, 0u, 0u, 0u};
+    if (head_ok) w = *(const u32x4_t*)(q + ((size_t)s * Hq + h) * D + chunk * 8);
+    qf[kk] = as_bf16x8(w);
+  }
+
+  const int32_t* trow = tables + (size_t)s * max_blocks;
+  const int tile_begin = t_begin >> 4;
+  const int tile_end = (t_end + 15) >> 4;
+  const int seq_blocks = (n + BS - 1) / BS;
+  // The partition's table entries, one per lane (a partition spans at most
+  // 64 blocks, which the host guarantees).
+  const int tbl_base = t_begin / BS;
+  const int tbl = (tbl_base + lane < seq_blocks) ? trow[tbl_base + lane] : -1;
+
+  constexpr int ROW = D * E;                       // bytes per token row
+  const size_t head_stride = (size_t)BS * ROW;     // bytes per (block, kv head)
+  const unsigned koff = c * ROW + (I8 ? j * 32 : j * 16);
+  const unsigned voff = 4 * j * ROW + c * 8 * E;
+  auto tile_ptrs = [&](int ti, const char*& kb, const char*& vb, bool& ok, float& ks, float& vs) {
+    const int lb = (ti * 16) / BS;
+    int b = __builtin_amdgcn_readlane(tbl, lb - tbl_base);
+    ok = b >= 0 && b < NB;
+    if (!ok) b = 0;
+    const size_t off = ((size_t)b * Hkv + g) * head_stride + (size_t)((ti * 16) % BS) * ROW;
+    kb = k_cache + off;
+    vb = v_cache + off;
+    if (I8) {
+      ks = k_scales[(size_t)b * Hkv + g];
+      vs = v_scales[(size_t)b * Hkv + g];
+    }
+  };
+
+  f32x4_t acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf, l_run = 0.f;
+
+  auto compute = [&](MfmaTile<I8>& T, int ti, bool ok, float ks, float vs) {
+    // ---- scores
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8_t a;
+      if (I8) {
+        const unsigned w0 = T.k[kk >> 1][(kk & 1) * 2], w1 = T.k[kk >> 1][(kk & 1) * 2 + 1];
+        const u32x2_t lo = i8x4_to_bf16x4(w0), hi = i8x4_to_bf16x4(w1);
+        a = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+      } else {
+        a = as_bf16x8(T.k[kk]);
+      }
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], sc, 0, 0, 0);
+    }
+    const float xs = I8 ? qk_log2 * ks : qk_log2;
+    const int tok0 = ti * 16 + 4 * j;
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = (ok && tok0 + r < t_end) ? sc[r] * xs : kNegInf;
+    float mloc = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mloc = xor_max_rows(mloc);
+    // ---- lazy rescale of the running reference
+    const bool need = mloc > m_run + kRescaleThreshold;
+    if (__any(need)) {
+      const float m_new = need ? mloc : m_run;
+      const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    float pw[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pw[r] = x[r] == kNegInf ? 0.f : fast_exp2(x[r] - m_run);
+    l_run += (pw[0] + pw[1]) + (pw[2] + pw[3]);
+    if (I8) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pw[r] *= vs;
+    }
+    // ---- P as bf16 hi + lo, B operand of the P.V MFMA
+    float lo[4];
+    unsigned hi01 = pack_bf16x2(pw[0], pw[1]), hi23 = pack_bf16x2(pw[2], pw[3]);
+    lo[0] = pw[0] - bf16_lo(hi01);
+    lo[1] = pw[1] - bf16_hi(hi01);
+    lo[2] = pw[2] - bf16_lo(hi23);
+    lo[3] = pw[3] - bf16_hi(hi23);
+    const i16x4_t Phi = as_i16x4(hi01, hi23);
+    const i16x4_t Plo = as_i16x4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
+    // ---- V^T operands: rows 4j+i of this lane; rows past the context are
+    // zeroed (they may hold NaN and would poison 0 * NaN in the MFMA)
+    const bool partial = !ok || ti * 16 + 15 >= t_end;  // wave-uniform
+    if (partial) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool keep = ok && tok0 + i < t_end;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) T.v[i][w] = keep ? T.v[i][w] : 0u;
+      }
+    }
+    unsigned vw[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (I8) {
+        const u32x2_t a = i8x4_to_bf16x4(T.v[i][0]), b = i8x4_to_bf16x4(T.v[i][1]);
+        vw[i][0] = a[0];
+        vw[i][1] = a[1];
+        vw[i][2] = b[0];
+        vw[i][3] = b[1];
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) vw[i][w] = T.v[i][w];
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      // word w holds d = 8c + 2w (low half) and 8c + 2w + 1 (high half)
+      const i16x4_t a_even = as_i16x4(__builtin_amdgcn_perm(vw[1][w], vw[0][w], 0x05040100u),
+                                      __builtin_amdgcn_perm(vw[3][w], vw[2][w], 0x05040100u));
+      const i16x4_t a_odd = as_i16x4(__builtin_amdgcn_perm(vw[1][w], vw[0][w], 0x07060302u),
+                                     __builtin_amdgcn_perm(vw[3][w], vw[2][w], 0x07060302u));
+      acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_even, Phi, acc[2 * w], 0, 0, 0);
+      acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_even, Plo, acc[2 * w], 0, 0, 0);
+      acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_odd, Phi, acc[2 * w + 1], 0, 0, 0);
+      acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_odd, Plo, acc[2 * w + 1], 0, 0, 0);
+    }
+  };
+
+  // Software pipeline: the next tile's loads are in flight while the
+  // current one is computed.  The last prefetch re-reads the final tile
+  // (always in bounds) so every iteration issues the same loads.
+  MfmaTile<I8> A, B;
+  const char *kA, *vA, *kB, *vB;
+  bool okA, okB;
+  float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
+  int ti = tile_begin;
+  tile_ptrs(ti, kA, vA, okA, ksA, vsA);
+  mfma_load_tile<I8>(A, kA, vA, koff, voff);
+  while (true) {
+    tile_ptrs(min(ti + 1, tile_end - 1), kB, vB, okB, ksB, vsB);
+    mfma_load_tile<I8>(B, kB, vB, koff, voff);
+    compute(A, ti, okA, ksA, vsA);
+    if (++ti >= tile_end) break;
+    tile_ptrs(min(ti + 1, tile_end - 1), kA, vA, okA, ksA, vsA);
+    mfma_load_tile<I8>(A, kA, vA, koff, voff);
+    compute(B, ti, okB, ksB, vsB);
+    if (++ti >= tile_end) break;
+  }
+
+  const float l_tot = xor_sum_rows(l_run);
+  if (!head_ok) return;
+  // lane holds d = 32j + 8r + e in acc[e][r]
+  if (nP == 1) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float* o = out + ((size_t)s * Hq + h) * D + 32 * j;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      *(float4*)(o + 8 * r) = float4{acc[0][r] * inv, acc[1][r] * inv, acc[2][r] * inv, acc[3][r] * inv};
+      *(float4*)(o + 8 * r + 4) = float4{acc[4][r] * inv, acc[5][r] * inv, acc[6][r] * inv, acc[7][r] * inv};
+    }
+  } else {
+    const size_t row_id = ((size_t)s * Hq + h) * nP + p;
+    float* o = ws_acc + row_id * D + 32 * j;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      *(float4*)(o + 8 * r) = float4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+      *(float4*)(o + 8 * r + 4) = float4{acc[4][r], acc[5][r], acc[6][r], acc[7][r]};
+    }
+    if (j == 0) ws_ml[row_id] = float2{m_run, l_tot};
+  }
+}
+
+// ===========================================================================
+// Vector-ALU kernel: any supported dtype, head_dim 64 or 128.
+//
+// Lane l handles token slot tt = l/16 of each group of four tokens and the
+// d-chunk c = l%16 (D/16 consecutive elements).  A score is an in-lane
+// partial dot product summed over the 16 lanes of the DPP row.  Each of
+// the four token slots keeps its own (m, l, acc) per head; the four are
+// merged at the end.
+// ===========================================================================
+
+template <typename KV, int DC>
+struct KvChunk;
+
+template <int DC>
+struct KvChunk<float, DC> {
+  static __device__ __forceinline__ void load(const char* p, float (&v)[DC]) {
+#pragma unroll
+    for (int i = 0; i < DC; i += 4) {
+      u32x4_t w = ld16(p + 4 * i);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[i + k] = __uint_as_float(w[k]);
+    }
+  }
+};
+
+template <int DC>
+struct KvChunk<__bf16, DC> {
+  static __device__ __forceinline__ void load(const char* p, float (&v)[DC]) {
+    if constexpr (DC == 8) {
+      u32x4_t w = ld16(p);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] = bf16_lo(w[k]);
+        v[2 * k + 1] = bf16_hi(w[k]);
+      }
+    } else {
+      u32x2_t w = ld8(p);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        v[2 * k] = bf16_lo(w[k]);
+        v[2 * k + 1] = bf16_hi(w[k]);
+      }
+    }
+  }
+};
+
+template <int DC>
+struct KvChunk<signed char, DC> {
+  static __device__ __forceinline__ void load(const char* p, float (&v)[DC]) {
+    if constexpr (DC == 8) {
+      u32x2_t w = ld8(p);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[k] = i8_at(w[0], k);
+        v[4 + k] = i8_at(w[1], k);
+      }
+    } else {
+      unsigned w = ld4(p);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = i8_at(w, k);
+    }
+  }
+};
+
+template <typename QT, int DC>
+__device__ __forceinline__ void load_q(const QT* p, float (&v)[DC]) {
+  if constexpr (sizeof(QT) == 4) {
+#pragma unroll
+    for (int i = 0; i < DC; ++i) v[i] = ((const float*)p)[i];
+  } else {
+    const unsigned short* u = (const unsigned short*)p;
+#pragma unroll
+    for (int i = 0; i < DC; ++i) v[i] = __uint_as_float((unsigned)u[i] << 16);
+  }
+}
+
+template <typename QT, typename KV, int D, int BS, int GT>
+__global__ __launch_bounds__(64) void decode_valu_kernel(
+    float* __restrict__ out, float2* __restrict__ ws_ml, float* __restrict__ ws_acc, const QT* __restrict__ q,
+    const char* __restrict__ k_cache, const char* __restrict__ v_cache, const float* __restrict__ k_scales,
+    const float* __restrict__ v_scales, const int32_t* __restrict__ tables, int max_blocks,
+    const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int head_groups, int NB, float qk_log2,
+    int P, int nP) {
+  constexpr int DC = D / 16;
+  constexpr bool I8 = sizeof(KV) == 1;
+  constexpr int E = sizeof(KV);
+  const int lane = threadIdx.x;
+  const int tt = lane >> 4;
+  const int c = lane & 15;
+  const int p = blockIdx.x % nP;
+  int rest = blockIdx.x / nP;
+  const int hg = rest % head_groups;
+  rest /= head_groups;
+  const int g = rest % Hkv;
+  const int s = rest / Hkv;
+  const int n = min(context_lens[s], max_blocks * BS);
+  const int t_begin = p * P;
+  const int t_end = min(n, t_begin + P);
+  const int h0 = g * G + hg * GT;
+  const int nh = min(GT, G - hg * GT);
+
+  if (t_begin >= t_end) {
+    if (nP == 1 && tt == 0) {
+      for (int i = 0; i < nh; ++i) {
+        float* o = out + ((size_t)s * Hq + h0 + i) * D + c * DC;
+#pragma unroll
+        for (int k = 0; k < DC; ++k) o[k] = 0.f;
+      }
+    }
+    return;
+  }
+
+  float qv[GT][DC];
+#pragma unroll
+  for (int i = 0; i < GT; ++i) {
+    if (i < nh) {
+      load_q<QT, DC>(q + ((size_t)s * Hq + h0 + i) * D + c * DC, qv[i]);
+#pragma unroll
+      for (int k = 0; k < DC; ++k) qv[i][k] *= qk_log2;
+    } else {
+#pragma unroll
+      for (int k = 0; k < DC; ++k) qv[i][k] = 0.f;
+    }
+  }
+
+  float m[GT], l[GT], acc[GT][DC];
+#pragma unroll
+  for (int i = 0; i < GT; ++i) {
+    m[i] = kNegInf;
+    l[i] = 0.f;
+#pragma unroll
+    for (int k = 0; k < DC; ++k) acc[i][k] = 0.f;
+  }
+
+  const int32_t* trow = tables + (size_t)s * max_blocks;
+  const size_t head_stride = (size_t)BS * D * E;
+  for (int t4 = t_begin; t4 < t_end; t4 += 16) {
+    // one 16-token tile: four passes of four tokens
+    const int lb = t4 / BS;
+    int b = trow[lb];
+    const bool ok = b >= 0 && b < NB;
+    if (!ok) b = 0;
+    const size_t off = ((size_t)b * Hkv + g) * head_stride;
+    const float ks = I8 ? k_scales[(size_t)b * Hkv + g] : 1.f;
+    const float vs = I8 ? v_scales[(size_t)b * Hkv + g] : 1.f;
+    const int row0 = t4 % BS;
+    float kv[4][DC], vv[4][DC];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const size_t roff = off + (size_t)(row0 + 4 * r + tt) * D * E + (size_t)c * DC * E;
+      KvChunk<KV, DC>::load(k_cache + roff, kv[r]);
+      KvChunk<KV, DC>::load(v_cache + roff, vv[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t4 + 4 * r + tt;
+      const bool valid = ok && t < t_end;
+      float x[GT];
+#pragma unroll
+      for (int i = 0; i < GT; ++i) {
+        float d = 0.f;
+#pragma unroll
+        for (int k = 0; k < DC; ++k) d = fmaf(qv[i][k], kv[r][k], d);
+        d = row_sum16(d);
+        x[i] = valid ? d * ks : kNegInf;
+      }
+      bool need = false;
+#pragma unroll
+      for (int i = 0; i < GT; ++i) need |= x[i] > m[i] + kRescaleThreshold;
+      if (__any(need)) {
+#pragma unroll
+        for (int i = 0; i < GT; ++i) {
+          const bool up = x[i] > m[i] + kRescaleThreshold;
+          const float m_new = up ? x[i] : m[i];
+          const float alpha = up ? fast_exp2(m[i] - m_new) : 1.f;
+          l[i] *= alpha;
+#pragma unroll
+          for (int k = 0; k < DC; ++k) acc[i][k] *= alpha;
+          m[i] = m_new;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < GT; ++i) {
+        const float pw = valid ? fast_exp2(x[i] - m[i]) : 0.f;
+        l[i] += pw;
+        const float pv = pw * vs;
+#pragma unroll
+        for (int k = 0; k < DC; ++k) acc[i][k] = fmaf(pv, valid ? vv[r][k] : 0.f, acc[i][k]);
+      }
+    }
+  }
+
+  // merge the four token slots: common reference, then sums across rows
+#pragma unroll
+  for (int i = 0; i < GT; ++i) {
+    const float mt = xor_max_rows(m[i]);
+    const float alpha = m[i] == kNegInf ? 0.f : fast_exp2(m[i] - mt);
+    l[i] = xor_sum_rows(l[i] * alpha);
+#pragma unroll
+    for (int k = 0; k < DC; ++k) acc[i][k] = xor_sum_rows(acc[i][k] * alpha);
+    m[i] = mt;
+  }
+  if (tt != 0) return;
+#pragma unroll
+  for (int i = 0; i < GT; ++i) {
+    if (i >= nh) break;
+    const int h = h0 + i;
+    if (nP == 1) {
+      const float inv = l[i] > 0.f ? 1.f / l[i] : 0.f;
+      float* o = out + ((size_t)s * Hq + h) * D + c * DC;
+#pragma unroll
+      for (int k = 0; k < DC; ++k) o[k] = acc[i][k] * inv;
+    } else {
+      const size_t row_id = ((size_t)s * Hq + h) * nP + p;
+      float* o = ws_acc + row_id * D + c * DC;
+#pragma unroll
+      for (int k = 0; k < DC; ++k) o[k] = acc[i][k];
+      if (c == 0) ws_ml[row_id] = float2{m[i], l[i]};
+    }
+  }
+}
+
+// ===========================================================================
+// Split-K merge: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p over
+// the partitions that hold tokens of the sequence.
+// ===========================================================================
+template <int D>
+__global__ __launch_bounds__(64) void decode_reduce_kernel(float* __restrict__ out, const float2* __restrict__ ws_ml,
+                                                           const float* __restrict__ ws_acc,
+                                                           const int32_t* __restrict__ context_lens, int Hq, int P,
+                                                           int nP) {
+  constexpr int PER = D / 64;
+  const int sh = blockIdx.x;  // s * Hq + h
+  const int s = sh / Hq;
+  const int n = context_lens[s];
+  const int np = min(nP, (n + P - 1) / P);
+  float* o = out + (size_t)sh * D;
+  const float2* ml = ws_ml + (size_t)sh * nP;
+  float M = kNegInf;
+  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[p].x);
+  float L = 0.f, a[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) a[k] = 0.f;
+  if (M != kNegInf) {
+    for (int p = 0; p < np; ++p) {
+      const float2 v = ml[p];
+      if (v.y == 0.f) continue;
+      const float w = fast_exp2(v.x - M);
+      L += w * v.y;
+      const float* src = ws_acc + ((size_t)sh * nP + p) * D;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) a[k] = fmaf(w, src[threadIdx.x + 64 * k], a[k]);
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) o[threadIdx.x + 64 * k] = a[k] * inv;
+}
+
+// ===========================================================================
+// launchers
+// ===========================================================================
+
+static inline float2* ws_ml_ptr(const pa_decode_args* a) { return (float2*)a->workspace; }
+static inline float* ws_acc_ptr(const pa_decode_args* a, const DecodePlan& p) {
+  return (float*)((char*)a->workspace + ws_ml_bytes(a->num_seqs, a->num_q_heads, p.num_partitions));
+}
+
+pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipStream_t st) {
+  const size_t items = (size_t)a->num_seqs * a->num_kv_heads * p.num_partitions;
+  if (items > 0x7fffffffu) return fail(PA_ERR_UNSUPPORTED, "pa_decode: grid too large");
+  const float qk = a->scale * kLog2e;
+  float2* ml = p.num_partitions > 1 ? ws_ml_ptr(a) : nullptr;
+  float* wacc = p.num_partitions > 1 ? ws_acc_ptr(a, p) : nullptr;
+#define PA_MFMA_LAUNCH(I8, BS)                                                                                   \
+  hipLaunchKernelGGL((decode_mfma_kernel<I8, BS>), dim3((unsigned)items), dim3(64), 0, st, (float*)a->out, ml,  \
+                     wacc, (const unsigned short*)a->q, (const char*)a->k_cache, (const char*)a->v_cache,      \
+                     a->k_scales, a->v_scales, a->block_tables, a->max_blocks_per_seq, a->context_lens,        \
+                     a->num_q_heads, a->num_kv_heads, p.G, a->num_blocks, qk, p.partition_tokens,              \
+                     p.num_partitions)
+  const bool i8 = a->kv_dtype == PA_I8;
+  if (i8) {
+    if (a->block_size == 16) PA_MFMA_LAUNCH(true, 16); else PA_MFMA_LAUNCH(true, 32);
+  } else {
+    if (a->block_size == 16) PA_MFMA_LAUNCH(false, 16); else PA_MFMA_LAUNCH(false, 32);
+  }
+#undef PA_MFMA_LAUNCH
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode (matrix-core kernel) launch");
+}
+
+template <typename QT, typename KV, int D, int BS>
+static void valu_dispatch_g(const pa_decode_args* a, const DecodePlan& p, hipStream_t st, unsigned items,
+                            float2* ml, float* wacc, float qk) {
+#define PA_VALU_LAUNCH(GT)                                                                                    \
+  hipLaunchKernelGGL((decode_valu_kernel<QT, KV, D, BS, GT>), dim3(items), dim3(64), 0, st, (float*)a->out,  \
+                     ml, wacc, (const QT*)a->q, (const char*)a->k_cache, (const char*)a->v_cache, a->k_scales, \
+                     a->v_scales, a->block_tables, a->max_blocks_per_seq, a->context_lens, a->num_q_heads,   \
+                     a->num_kv_heads, p.G, p.head_groups, a->num_blocks, qk, p.partition_tokens,             \
+                     p.num_partitions)
+  switch (p.heads_per_wave) {
+    case 1: PA_VALU_LAUNCH(1); break;
+    case 2: PA_VALU_LAUNCH(2); break;
+    case 4: PA_VALU_LAUNCH(4); break;
+    default: PA_VALU_LAUNCH(8); break;
+  }
+#undef PA_VALU_LAUNCH
+}
+
+template <typename QT, typename KV>
+static void valu_dispatch_shape(const pa_decode_args* a, const DecodePlan& p, hipStream_t st, unsigned items,
+                                float2* ml, float* wacc, float qk) {
+  if (a->head_dim == 64) {
+    if (a->block_size == 16) valu_dispatch_g<QT, KV, 64, 16>(a, p, st, items, ml, wacc, qk);
+    else valu_dispatch_g<QT, KV, 64, 32>(a, p, st, items, ml, wacc, qk);
+  } else {
+    if (a->block_size == 16) valu_dispatch_g<QT, KV, 128, 16>(a, p, st, items, ml, wacc, qk);
+    else valu_dispatch_g<QT, KV, 128, 32>(a, p, st, items, ml, wacc, qk);
+  }
+}
+
+template <typename QT>
+static void valu_dispatch_kv(const pa_decode_args* a, const DecodePlan& p, hipStream_t st, unsigned items,
+                             float2* ml, float* wacc, float qk) {
+  switch (a->kv_dtype) {
+    case PA_F32: valu_dispatch_shape<QT, float>(a, p, st, items, ml, wacc, qk); break;
+    case PA_BF16: valu_dispatch_shape<QT, __bf16>(a, p, st, items, ml, wacc, qk); break;
+    default: valu_dispatch_shape<QT, signed char>(a, p, st, items, ml, wacc, qk); break;
+  }
+}
+
+pa_status launch_decode_valu(const pa_decode_args* a, const DecodePlan& p, hipStream_t st) {
+  const size_t items = (size_t)a->num_seqs * a->num_kv_heads * p.head_groups * p.num_partitions;
+  if (items > 0x7fffffffu) return fail(PA_ERR_UNSUPPORTED, "pa_decode: grid too large");
+  const float qk = a->scale * kLog2e;
+  float2* ml = p.num_partitions > 1 ? ws_ml_ptr(a) : nullptr;
+  float* wacc = p.num_partitions > 1 ? ws_acc_ptr(a, p) : nullptr;
+  if (a->q_dtype == PA_F32) valu_dispatch_kv<float>(a, p, st, (unsigned)items, ml, wacc, qk);
+  else valu_dispatch_kv<unsigned short>(a, p, st, (unsigned)items, ml, wacc, qk);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode (vector-ALU kernel) launch");
+}
+
+pa_status launch_decode_reduce(const pa_decode_args* a, const DecodePlan& p, hipStream_t st) {
+  const size_t rows = (size_t)a->num_seqs * a->num_q_heads;
+  if (a->head_dim == 64)
+    hipLaunchKernelGGL(decode_reduce_kernel<64>, dim3((unsigned)rows), dim3(64), 0, st, (float*)a->out,
+                       ws_ml_ptr(a), ws_acc_ptr(a, p), a->context_lens, a->num_q_heads, p.partition_tokens,
+                       p.num_partitions);
+  else
+    hipLaunchKernelGGL(decode_reduce_kernel<128>, dim3((unsigned)rows), dim3(64), 0, st, (float*)a->out,
+                       ws_ml_ptr(a), ws_acc_ptr(a, p), a->context_lens, a->num_q_heads, p.partition_tokens,
+                       p.num_partitions);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode (merge kernel) launch");
+}
+
+}  // namespace pa
