@@ -114,7 +114,7 @@ def run(args) -> dict:
     slots = torch.empty(S, dtype=torch.int64, device=dev)
     probe = pa.make_decode_args(Q[0], K[0], V[0], bt, cl, scale, ctx, out=outs[0])
     ws_bytes = pa.decode_workspace_size(probe)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def prepare(stream):
@@ -222,7 +222,7 @@ def run(args) -> dict:
         "wall_s_timed_region": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "pa_decode (partition + merge)", "launch_ms_avg": round(launch_avg, 5),
+                     "kernel": "decode_mfma_kernel (pa_decode: one launch, merge fused)", "launch_ms_avg": round(launch_avg, 5),
                      "launch_ms_p10": round(launch_ms[len(launch_ms) // 10], 5),
                      "launch_ms_p90": round(launch_ms[(9 * len(launch_ms)) // 10], 5),
                      "algorithmic_bytes_per_launch": alg_launch, "workspace_bytes": ws_bytes},
@@ -269,6 +269,30 @@ def cpu_baseline(args, K, V, Q, st, L) -> dict:
             "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
+def copy_calibration(args) -> dict:
+    """A plain copy of known size through pa_copy_blocks, for scaling HBM
+    byte counters: `pairs` whole blocks of K and of V (8 kv heads x 32 slots
+    x 128 bf16 = 64 KiB each) read once and written once."""
+    import torch
+
+    import paged_kv_cache_192_amd as pa
+
+    pa.library()
+    dev = torch.device("cuda:0")
+    pairs = args.copy_pairs
+    NB = 2 * pairs
+    k = torch.zeros(NB, 8, 32, 128, dtype=torch.bfloat16, device=dev)
+    v = torch.zeros_like(k)
+    pr = torch.stack([torch.arange(pairs), torch.arange(pairs, 2 * pairs)], dim=1).to(torch.int64).to(dev)
+    for _ in range(args.steps):
+        pa.copy_blocks(k, v, pr)
+    torch.cuda.synchronize()
+    per = 2 * pairs * 8 * 32 * 128 * 2
+    return {"mode": "copy-calibration", "kernel": "copy_blocks_kernel", "launches": args.steps,
+            "bytes_read_per_launch": per, "bytes_written_per_launch": per,
+            "kib_read_per_launch": per / 1024, "kib_written_per_launch": per / 1024}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -279,6 +303,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--eager", dest="graph", action="store_false",
                     help="launch each call from Python instead of replaying the captured step")
+    ap.add_argument("--mode", choices=["decode", "copy-calibration"], default="decode",
+                    help="copy-calibration: a known-size block copy for scaling HBM byte counters")
+    ap.add_argument("--copy-pairs", type=int, default=4096)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path (asked for --gpus %d)"
@@ -287,7 +314,7 @@ def main():
     if args.layers != 80:
         print("note: --layers %d is not the 80-layer workload; the result is for tuning only" % args.layers,
               file=sys.stderr)
-    res = run(args)
+    res = copy_calibration(args) if args.mode == "copy-calibration" else run(args)
     print(json.dumps(res), flush=True)
 
 

@@ -100,12 +100,12 @@ int32_t pa_abi_version(void);
  * query heads per kv head.  All of q, caches and out 16-byte aligned.
  *
  * Long contexts are split into partitions of `partition_tokens` tokens
- * (0 = chosen by the library), each computed separately and merged by a
- * second kernel; the merge needs `workspace` of at least the size
- * pa_decode_workspace_size reports for the same arguments (it may be NULL
- * when that size is 0).  The workspace is scratch of the call: its
- * contents are not needed before or after it.  Two calls that run
- * concurrently need separate workspaces.
+ * (0 = chosen by the library), each computed by its own wave and merged by
+ * a second kernel in partition order.  The merge needs `workspace` of at
+ * least the size pa_decode_workspace_size reports for the same arguments
+ * (NULL is fine when that size is 0).  The workspace is scratch of the
+ * call: its contents are not needed before or after it.  Calls that may
+ * run concurrently need separate workspaces.
  *
  * `kernel` selects the implementation: 0 = automatic, 1 = vector-ALU
  * kernel (any supported case), 2 = matrix-core kernel (bf16 or int8
@@ -135,7 +135,7 @@ typedef struct {
   int32_t num_blocks;
   int32_t max_context_len;       /* host-side bound on context_lens; sizes the grid */
   float scale;                   /* finite; usually 1/sqrt(head_dim) */
-  int32_t partition_tokens;      /* 0 = automatic; else a positive multiple of 16 */
+  int32_t partition_tokens;      /* 0 = automatic; else a multiple of 16, at most 128 * block_size */
   int32_t kernel;                /* 0 automatic, 1 vector ALU, 2 matrix cores */
   void* workspace;
   size_t workspace_bytes;

@@ -209,8 +209,10 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_co
            k_scales=None, v_scales=None, workspace=None, partition_tokens: int = 0, kernel: int = KERNEL_AUTO,
            stream=None):
     """Paged decode attention (``pa_decode``).  Returns ``out`` (float32
-    ``[S][Hq][D]``), allocated on q's device when not given.  A workspace is
-    allocated when needed and none is passed."""
+    ``[S][Hq][D]``), allocated on q's device when not given.  A zeroed
+    workspace is allocated when needed and none is passed; a caller-owned
+    workspace must be zero-filled before its first use (calls leave it
+    zeroed)."""
     torch = _torch()
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
@@ -219,7 +221,7 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_co
                             partition_tokens=partition_tokens, kernel=kernel, stream=stream)
     need = decode_workspace_size(args)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
         args.workspace = workspace.data_ptr()
         args.workspace_bytes = need
     _check(library().pa_decode(ctypes.byref(args)))
@@ -346,7 +348,7 @@ class PreparedDecode:
                                      partition_tokens=partition_tokens, kernel=kernel, stream=stream)
         need = decode_workspace_size(self.args)
         if need and (workspace is None or self.args.workspace_bytes < need):
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
             self.args.workspace = workspace.data_ptr()
             self.args.workspace_bytes = need
         self.workspace_bytes = need

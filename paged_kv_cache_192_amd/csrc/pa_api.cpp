@@ -28,10 +28,11 @@ static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 static bool valid_dtype(int t) { return t == PA_F32 || t == PA_BF16 || t == PA_I8; }
 
-// Waves a decode launch should put on the chip: about ten per compute unit
-// of a 256-CU MI355X keeps enough loads in flight to cover HBM latency
-// while every work item still runs in a single round.
-static const int kTargetItems = 2560;
+// Waves a decode launch should put on the chip: about five per compute unit
+// of a 256-CU MI355X.  Measured on the 70B-shaped layer, five waves per CU
+// keep the HBM busy, while more waves per CU only compete for the CU's
+// memory pipeline (and two or three leave it short of loads in flight).
+static const int kTargetWaves = 1280;
 
 pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   if (!a) return fail(PA_ERR_INVALID, "pa_decode: args is NULL");
@@ -63,9 +64,9 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   if (a->max_context_len < 0 || (int64_t)a->max_context_len > (int64_t)a->max_blocks_per_seq * a->block_size)
     return fail(PA_ERR_INVALID, "pa_decode: max_context_len %d outside [0, max_blocks_per_seq*block_size]",
                 a->max_context_len);
-  if (a->partition_tokens < 0 || a->partition_tokens % 16 || a->partition_tokens > 64 * a->block_size)
-    return fail(PA_ERR_INVALID, "pa_decode: partition_tokens %d is not a multiple of 16 in [0, 64*block_size]",
-                a->partition_tokens);
+  if (a->partition_tokens < 0 || a->partition_tokens % 16 || a->partition_tokens > kMaxPartitionBlocks * a->block_size)
+    return fail(PA_ERR_INVALID, "pa_decode: partition_tokens %d is not a multiple of 16 in [0, %d*block_size]",
+                a->partition_tokens, kMaxPartitionBlocks);
   if (a->kernel < 0 || a->kernel > 2) return fail(PA_ERR_INVALID, "pa_decode: kernel %d not in {0, 1, 2}", a->kernel);
 
   const bool mfma_ok = a->q_dtype == PA_BF16 && (a->kv_dtype == PA_BF16 || a->kv_dtype == PA_I8) &&
@@ -90,24 +91,24 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   p->head_groups = kind == KERNEL_VALU ? (G + hpw - 1) / hpw : 1;
 
   const int64_t tiles = a->max_context_len > 0 ? (a->max_context_len + 15) / 16 : 1;
+  const int64_t max_tiles = (int64_t)kMaxPartitionBlocks * a->block_size / 16;
   int P = a->partition_tokens;
   if (P == 0) {
-    const int64_t waves_per_partition = (int64_t)(a->num_seqs > 0 ? a->num_seqs : 1) *
-                                        a->num_kv_heads * p->head_groups;
-    int64_t per_item = (tiles * waves_per_partition + kTargetItems - 1) / kTargetItems;
-    if (per_item < 4) per_item = 4;
-    if (per_item > tiles) per_item = tiles;
-    // a partition spans at most 64 blocks (one table entry per lane)
-    if (per_item > 4 * a->block_size) per_item = 4 * a->block_size;
-    P = (int)(16 * per_item);
+    // Split each sequence into nP equal partitions so the grid holds about
+    // kTargetWaves waves, within [4 tiles, kMaxPartitionBlocks blocks] per
+    // partition and at most kMaxAutoPartitions partitions.
+    const int64_t groups = (int64_t)(a->num_seqs > 0 ? a->num_seqs : 1) * a->num_kv_heads * p->head_groups;
+    int64_t nP = (kTargetWaves + groups / 2) / groups;
+    if (nP < 1) nP = 1;
+    if (nP > kMaxAutoPartitions) nP = kMaxAutoPartitions;
+    if (nP > (tiles + 3) / 4) nP = (tiles + 3) / 4;
+    int64_t per = (tiles + nP - 1) / nP;
+    if (per > max_tiles) per = max_tiles;
+    P = (int)(16 * per);
   }
   p->partition_tokens = P;
   p->num_partitions = a->max_context_len > 0 ? (a->max_context_len + P - 1) / P : 1;
-  p->workspace_bytes = 0;
-  if (p->num_partitions > 1) {
-    p->workspace_bytes = ws_ml_bytes(a->num_seqs, a->num_q_heads, p->num_partitions) +
-                         (size_t)a->num_seqs * a->num_q_heads * p->num_partitions * a->head_dim * sizeof(float);
-  }
+  p->workspace_bytes = workspace_layout(a, *p).bytes;
   return PA_OK;
 }
 
@@ -162,9 +163,8 @@ pa_status pa_decode(const pa_decode_args* a) {
   }
   hipStream_t st = (hipStream_t)a->stream;
   s = p.kind == KERNEL_MFMA ? launch_decode_mfma(a, p, st) : launch_decode_valu(a, p, st);
-  if (s != PA_OK) return s;
-  if (p.num_partitions > 1) s = launch_decode_reduce(a, p, st);
-  return s;
+  if (s != PA_OK || p.num_partitions == 1) return s;
+  return launch_decode_merge(a, p, st);
 }
 
 pa_status pa_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,

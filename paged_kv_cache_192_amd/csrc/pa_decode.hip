@@ -12,7 +12,7 @@
 // Work decomposition: one wave per (sequence, kv head, partition of the
 // context); the partition's tokens are processed in tiles of 16.  With
 // more than one partition each wave leaves (m, l, acc) in the workspace and
-// decode_reduce_kernel merges them; with one partition the wave writes the
+// decode_merge_kernel combines them; with one partition the wave writes the
 // output row directly.
 //
 // Softmax bookkeeping is in log2 units: x = log2(e) * scale * <q, k>, weights
@@ -83,6 +83,81 @@ __device__ __forceinline__ float swap32_sum(float x) {
 __device__ __forceinline__ float xor_max_rows(float x) { return swap32_max(swap16_max(x)); }
 __device__ __forceinline__ float xor_sum_rows(float x) { return swap32_sum(swap16_sum(x)); }
 
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false)));
+  return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false)));
+}
+__device__ __forceinline__ float wave_max(float x) { return xor_max_rows(row_max16(x)); }
+__device__ __forceinline__ float wave_sum(float x) { return xor_sum_rows(row_sum16(x)); }
+
+// ---------------------------------------------------------------------------
+// Split-K partials.  With more than one partition every wave that attended
+// to some tokens stores (m, l, acc) in the workspace; decode_merge_kernel
+// then combines each row's partials in partition order:
+//   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
+// (A merge fused into the last-arriving wave needs an agent-scope release
+// per wave, which on gfx950 writes back the XCD's L2; measured 70 us slower
+// per 70B-shaped layer than this separate launch.)
+// ---------------------------------------------------------------------------
+
+struct SplitK {
+  float2* ml;     // [S][Hq][nP]: reference max (log2 units), sum of weights
+  float* acc;     // [S][Hq][nP][D]: unnormalised weighted sum of values
+};
+
+// Merge the np partials of rows row0 .. row0+nh-1 (row = s*Hq + h) into out.
+template <int D>
+__device__ void merge_partials(float* __restrict__ out, const SplitK& w, size_t row0, int nh, int nP, int np) {
+  constexpr int PER = D / 64;
+  const int lane = threadIdx.x;
+  for (int i = 0; i < nh; ++i) {
+    const size_t r = (row0 + i) * (size_t)nP;
+    float M = kNegInf;
+    for (int p0 = 0; p0 < np; p0 += 64)
+      if (p0 + lane < np) M = fmaxf(M, w.ml[r + p0 + lane].x);
+    M = wave_max(M);
+    float L = 0.f, a[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) a[k] = 0.f;
+    if (M != kNegInf) {
+      for (int p0 = 0; p0 < np; p0 += 64) {
+        const int cnt = min(64, np - p0);
+        float wt = 0.f;
+        if (lane < cnt) {
+          const float2 v = w.ml[r + p0 + lane];
+          wt = v.y > 0.f ? fast_exp2(v.x - M) : 0.f;
+          L = fmaf(wt, v.y, L);
+        }
+        const float* src = w.acc + (r + p0) * D + lane;
+#pragma unroll 4
+        for (int k = 0; k < cnt; ++k) {
+          const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), k));
+#pragma unroll
+          for (int q = 0; q < PER; ++q) a[q] = fmaf(wk, src[(size_t)k * D + 64 * q], a[q]);
+        }
+      }
+    }
+    L = wave_sum(L);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    float* o = out + (row0 + i) * D + lane;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) o[64 * q] = a[q] * inv;
+  }
+}
+
+// One wave per output row (s, h).
+template <int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(float* __restrict__ out, SplitK ws,
+                                                          const int32_t* __restrict__ context_lens, int Hq, int P,
+                                                          int nP, int max_tokens) {
+  const int row = blockIdx.x;
+  const int n = min(context_lens[row / Hq], max_tokens);
+  const int np = n > 0 ? min(nP, (n + P - 1) / P) : 0;
+  merge_partials<D>(out, ws, row, 1, nP, np);
+}
+
 // ===========================================================================
 // Matrix-core kernel: bf16 or int8 cache, bf16 queries, head_dim 128,
 // up to 16 query heads per kv head.
@@ -104,7 +179,9 @@ __device__ __forceinline__ float xor_sum_rows(float x) { return swap32_sum(swap1
 
 template <bool I8>
 struct MfmaTile {
-  // K: bf16 -> 4 x 16 B per lane (row l%16, d-chunks kk*4 + l/16);
+  // K: bf16 -> 4 x 16 B per lane, coalesced: instruction i reads rows
+  //    4i .. 4i+3, lane l the 16 B chunk l%16 of row 4i + l/16 (staged
+  //    through LDS into the MFMA layout);
   //    int8 -> 2 x 16 B per lane (row l%16, d = 32*(l/16) .. +31).
   u32x4_t k[I8 ? 2 : 4];
   // V: rows 4*(l/16) + i, d = 8*(l%16) .. +7: bf16 -> 16 B per row, int8 -> 8 B.
@@ -122,7 +199,7 @@ __device__ __forceinline__ void mfma_load_tile(MfmaTile<I8>& T, const char* kbas
     T.k[1] = ld16(kbase + koff + 16);
   } else {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) T.k[kk] = ld16(kbase + koff + kk * 64);
+    for (int i = 0; i < 4; ++i) T.k[i] = ld16(kbase + koff + i * 1024);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -152,9 +229,36 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
          ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)hi) << 16);
 }
 
+// Work item of a wave: (sequence s, kv head g, partition p).  With the kv
+// head fastest, the waves that start together read neighbouring 4 KB
+// chunks of the same physical blocks (measured ~1 % faster than partition
+// fastest on the 70B-shaped layer).
+constexpr int kItemOrder = 1;     // 0: p fastest; 1: g fastest
+constexpr bool kXcdRemap = false;  // give each XCD a contiguous range of items
+__device__ __forceinline__ void mfma_item(int bid, int nblk, int Hkv, int nP, int& s, int& g, int& p) {
+  int item = bid;
+  if (kXcdRemap) {
+    // workgroups are dispatched round-robin over the 8 XCDs: XCD x runs
+    // bid = x, x+8, ...; map those to one contiguous range of items
+    const int q = nblk / 8, r = nblk % 8, x = bid % 8, l = bid / 8;
+    item = x * q + min(x, r) + l;
+  }
+  if (kItemOrder == 0) {
+    p = item % nP;
+    const int sg = item / nP;
+    g = sg % Hkv;
+    s = sg / Hkv;
+  } else {
+    g = item % Hkv;
+    const int sp = item / Hkv;
+    p = sp % nP;
+    s = sp / nP;
+  }
+}
+
 template <bool I8, int BS>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(
-    float* __restrict__ out, float2* __restrict__ ws_ml, float* __restrict__ ws_acc,
+    float* __restrict__ out, SplitK ws,
     const unsigned short* __restrict__ q, const char* __restrict__ k_cache, const char* __restrict__ v_cache,
     const float* __restrict__ k_scales, const float* __restrict__ v_scales, const int32_t* __restrict__ tables,
     int max_blocks, const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int NB, float qk_log2,
@@ -164,10 +268,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   const int lane = threadIdx.x;
   const int j = lane >> 4;
   const int c = lane & 15;
-  const int p = blockIdx.x % nP;
-  const int sg = blockIdx.x / nP;
-  const int g = sg % Hkv;
-  const int s = sg / Hkv;
+  int s, g, p;
+  mfma_item(blockIdx.x, gridDim.x, Hkv, nP, s, g, p);
   // a length past the table row is a caller error; never read beyond the row
   const int n = min(context_lens[s], max_blocks * BS);
   const int t_begin = p * P;
@@ -201,18 +303,30 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   const int tile_begin = t_begin >> 4;
   const int tile_end = (t_end + 15) >> 4;
   const int seq_blocks = (n + BS - 1) / BS;
-  // The partition's table entries, one per lane (a partition spans at most
-  // 64 blocks, which the host guarantees).
+  // The partition's table entries, two per lane (a partition spans at most
+  // 128 blocks, which the host guarantees): entry i of the partition is
+  // lane i of tbl0 or lane i - 64 of tbl1.
   const int tbl_base = t_begin / BS;
-  const int tbl = (tbl_base + lane < seq_blocks) ? trow[tbl_base + lane] : -1;
+  const int tbl0 = (tbl_base + lane < seq_blocks) ? trow[tbl_base + lane] : -1;
+  const int tbl1 = (tbl_base + 64 + lane < seq_blocks) ? trow[tbl_base + 64 + lane] : -1;
 
   constexpr int ROW = D * E;                       // bytes per token row
   const size_t head_stride = (size_t)BS * ROW;     // bytes per (block, kv head)
-  const unsigned koff = c * ROW + (I8 ? j * 32 : j * 16);
+  // bf16 K goes through a per-wave LDS tile of 16 rows x 16 chunks of 16 B;
+  // chunk ch of row r sits at position ch ^ r, so both the row-wise writes
+  // and the MFMA-layout reads (16 rows, one chunk each) hit distinct banks.
+  __shared__ u32x4_t ktile[I8 ? 1 : 256];
+  const unsigned koff = I8 ? c * ROW + j * 32 : lane * 16;
+  int kw[4], kr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    kw[i] = (4 * i + j) * 16 + (c ^ (4 * i + j));  // write slot of load i
+    kr[i] = c * 16 + ((i * 4 + j) ^ c);            // read slot of d-chunk (i*4 + j), row c
+  }
   const unsigned voff = 4 * j * ROW + c * 8 * E;
   auto tile_ptrs = [&](int ti, const char*& kb, const char*& vb, bool& ok, float& ks, float& vs) {
-    const int lb = (ti * 16) / BS;
-    int b = __builtin_amdgcn_readlane(tbl, lb - tbl_base);
+    const int e = (ti * 16) / BS - tbl_base;
+    int b = e < 64 ? __builtin_amdgcn_readlane(tbl0, e) : __builtin_amdgcn_readlane(tbl1, e - 64);
     ok = b >= 0 && b < NB;
     if (!ok) b = 0;
     const size_t off = ((size_t)b * Hkv + g) * head_stride + (size_t)((ti * 16) % BS) * ROW;
@@ -230,6 +344,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   float m_run = kNegInf, l_run = 0.f;
 
   auto compute = [&](MfmaTile<I8>& T, int ti, bool ok, float ks, float vs) {
+    if (!I8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ktile[kw[i]] = T.k[i];
+    }
     // ---- scores
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -240,7 +358,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
         const u32x2_t lo = i8x4_to_bf16x4(w0), hi = i8x4_to_bf16x4(w1);
         a = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
       } else {
-        a = as_bf16x8(T.k[kk]);
+        a = as_bf16x8(ktile[kr[kk]]);
       }
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], sc, 0, 0, 0);
     }
@@ -339,9 +457,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   }
 
   const float l_tot = xor_sum_rows(l_run);
-  if (!head_ok) return;
   // lane holds d = 32j + 8r + e in acc[e][r]
   if (nP == 1) {
+    if (!head_ok) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     float* o = out + ((size_t)s * Hq + h) * D + 32 * j;
 #pragma unroll
@@ -349,15 +467,17 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       *(float4*)(o + 8 * r) = float4{acc[0][r] * inv, acc[1][r] * inv, acc[2][r] * inv, acc[3][r] * inv};
       *(float4*)(o + 8 * r + 4) = float4{acc[4][r] * inv, acc[5][r] * inv, acc[6][r] * inv, acc[7][r] * inv};
     }
-  } else {
+    return;
+  }
+  if (head_ok) {
     const size_t row_id = ((size_t)s * Hq + h) * nP + p;
-    float* o = ws_acc + row_id * D + 32 * j;
+    float* o = ws.acc + row_id * D + 32 * j;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       *(float4*)(o + 8 * r) = float4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
       *(float4*)(o + 8 * r + 4) = float4{acc[4][r], acc[5][r], acc[6][r], acc[7][r]};
     }
-    if (j == 0) ws_ml[row_id] = float2{m_run, l_tot};
+    if (j == 0) ws.ml[row_id] = float2{m_run, l_tot};
   }
 }
 
@@ -439,7 +559,7 @@ __device__ __forceinline__ void load_q(const QT* p, float (&v)[DC]) {
 
 template <typename QT, typename KV, int D, int BS, int GT>
 __global__ __launch_bounds__(64) void decode_valu_kernel(
-    float* __restrict__ out, float2* __restrict__ ws_ml, float* __restrict__ ws_acc, const QT* __restrict__ q,
+    float* __restrict__ out, SplitK ws, const QT* __restrict__ q,
     const char* __restrict__ k_cache, const char* __restrict__ v_cache, const float* __restrict__ k_scales,
     const float* __restrict__ v_scales, const int32_t* __restrict__ tables, int max_blocks,
     const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int head_groups, int NB, float qk_log2,
@@ -563,81 +683,50 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
     for (int k = 0; k < DC; ++k) acc[i][k] = xor_sum_rows(acc[i][k] * alpha);
     m[i] = mt;
   }
-  if (tt != 0) return;
+  if (tt == 0) {
 #pragma unroll
-  for (int i = 0; i < GT; ++i) {
-    if (i >= nh) break;
-    const int h = h0 + i;
-    if (nP == 1) {
-      const float inv = l[i] > 0.f ? 1.f / l[i] : 0.f;
-      float* o = out + ((size_t)s * Hq + h) * D + c * DC;
+    for (int i = 0; i < GT; ++i) {
+      if (i >= nh) break;
+      const int h = h0 + i;
+      if (nP == 1) {
+        const float inv = l[i] > 0.f ? 1.f / l[i] : 0.f;
+        float* o = out + ((size_t)s * Hq + h) * D + c * DC;
 #pragma unroll
-      for (int k = 0; k < DC; ++k) o[k] = acc[i][k] * inv;
-    } else {
-      const size_t row_id = ((size_t)s * Hq + h) * nP + p;
-      float* o = ws_acc + row_id * D + c * DC;
+        for (int k = 0; k < DC; ++k) o[k] = acc[i][k] * inv;
+      } else {
+        const size_t row_id = ((size_t)s * Hq + h) * nP + p;
+        float* o = ws.acc + row_id * D + c * DC;
 #pragma unroll
-      for (int k = 0; k < DC; ++k) o[k] = acc[i][k];
-      if (c == 0) ws_ml[row_id] = float2{m[i], l[i]};
+        for (int k = 0; k < DC; ++k) o[k] = acc[i][k];
+        if (c == 0) ws.ml[row_id] = float2{m[i], l[i]};
+      }
     }
   }
-}
-
-// ===========================================================================
-// Split-K merge: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p over
-// the partitions that hold tokens of the sequence.
-// ===========================================================================
-template <int D>
-__global__ __launch_bounds__(64) void decode_reduce_kernel(float* __restrict__ out, const float2* __restrict__ ws_ml,
-                                                           const float* __restrict__ ws_acc,
-                                                           const int32_t* __restrict__ context_lens, int Hq, int P,
-                                                           int nP) {
-  constexpr int PER = D / 64;
-  const int sh = blockIdx.x;  // s * Hq + h
-  const int s = sh / Hq;
-  const int n = context_lens[s];
-  const int np = min(nP, (n + P - 1) / P);
-  float* o = out + (size_t)sh * D;
-  const float2* ml = ws_ml + (size_t)sh * nP;
-  float M = kNegInf;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[p].x);
-  float L = 0.f, a[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) a[k] = 0.f;
-  if (M != kNegInf) {
-    for (int p = 0; p < np; ++p) {
-      const float2 v = ml[p];
-      if (v.y == 0.f) continue;
-      const float w = fast_exp2(v.x - M);
-      L += w * v.y;
-      const float* src = ws_acc + ((size_t)sh * nP + p) * D;
-#pragma unroll
-      for (int k = 0; k < PER; ++k) a[k] = fmaf(w, src[threadIdx.x + 64 * k], a[k]);
-    }
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) o[threadIdx.x + 64 * k] = a[k] * inv;
 }
 
 // ===========================================================================
 // launchers
 // ===========================================================================
 
-static inline float2* ws_ml_ptr(const pa_decode_args* a) { return (float2*)a->workspace; }
-static inline float* ws_acc_ptr(const pa_decode_args* a, const DecodePlan& p) {
-  return (float*)((char*)a->workspace + ws_ml_bytes(a->num_seqs, a->num_q_heads, p.num_partitions));
+static inline SplitK split_k(const pa_decode_args* a, const DecodePlan& p) {
+  SplitK w{nullptr, nullptr};
+  if (p.num_partitions > 1) {
+    const WorkspaceLayout L = workspace_layout(a, p);
+    char* base = (char*)a->workspace;
+    w.ml = (float2*)(base + L.ml_offset);
+    w.acc = (float*)(base + L.acc_offset);
+  }
+  return w;
 }
 
 pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipStream_t st) {
   const size_t items = (size_t)a->num_seqs * a->num_kv_heads * p.num_partitions;
   if (items > 0x7fffffffu) return fail(PA_ERR_UNSUPPORTED, "pa_decode: grid too large");
   const float qk = a->scale * kLog2e;
-  float2* ml = p.num_partitions > 1 ? ws_ml_ptr(a) : nullptr;
-  float* wacc = p.num_partitions > 1 ? ws_acc_ptr(a, p) : nullptr;
+  const SplitK ws = split_k(a, p);
 #define PA_MFMA_LAUNCH(I8, BS)                                                                                   \
-  hipLaunchKernelGGL((decode_mfma_kernel<I8, BS>), dim3((unsigned)items), dim3(64), 0, st, (float*)a->out, ml,  \
-                     wacc, (const unsigned short*)a->q, (const char*)a->k_cache, (const char*)a->v_cache,      \
+  hipLaunchKernelGGL((decode_mfma_kernel<I8, BS>), dim3((unsigned)items), dim3(64), 0, st, (float*)a->out, ws,  \
+                     (const unsigned short*)a->q, (const char*)a->k_cache, (const char*)a->v_cache,      \
                      a->k_scales, a->v_scales, a->block_tables, a->max_blocks_per_seq, a->context_lens,        \
                      a->num_q_heads, a->num_kv_heads, p.G, a->num_blocks, qk, p.partition_tokens,              \
                      p.num_partitions)
@@ -654,10 +743,10 @@ pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipSt
 
 template <typename QT, typename KV, int D, int BS>
 static void valu_dispatch_g(const pa_decode_args* a, const DecodePlan& p, hipStream_t st, unsigned items,
-                            float2* ml, float* wacc, float qk) {
+                            const SplitK& ws, float qk) {
 #define PA_VALU_LAUNCH(GT)                                                                                    \
   hipLaunchKernelGGL((decode_valu_kernel<QT, KV, D, BS, GT>), dim3(items), dim3(64), 0, st, (float*)a->out,  \
-                     ml, wacc, (const QT*)a->q, (const char*)a->k_cache, (const char*)a->v_cache, a->k_scales, \
+                     ws, (const QT*)a->q, (const char*)a->k_cache, (const char*)a->v_cache, a->k_scales, \
                      a->v_scales, a->block_tables, a->max_blocks_per_seq, a->context_lens, a->num_q_heads,   \
                      a->num_kv_heads, p.G, p.head_groups, a->num_blocks, qk, p.partition_tokens,             \
                      p.num_partitions)
@@ -672,23 +761,23 @@ static void valu_dispatch_g(const pa_decode_args* a, const DecodePlan& p, hipStr
 
 template <typename QT, typename KV>
 static void valu_dispatch_shape(const pa_decode_args* a, const DecodePlan& p, hipStream_t st, unsigned items,
-                                float2* ml, float* wacc, float qk) {
+                                const SplitK& ws, float qk) {
   if (a->head_dim == 64) {
-    if (a->block_size == 16) valu_dispatch_g<QT, KV, 64, 16>(a, p, st, items, ml, wacc, qk);
-    else valu_dispatch_g<QT, KV, 64, 32>(a, p, st, items, ml, wacc, qk);
+    if (a->block_size == 16) valu_dispatch_g<QT, KV, 64, 16>(a, p, st, items, ws, qk);
+    else valu_dispatch_g<QT, KV, 64, 32>(a, p, st, items, ws, qk);
   } else {
-    if (a->block_size == 16) valu_dispatch_g<QT, KV, 128, 16>(a, p, st, items, ml, wacc, qk);
-    else valu_dispatch_g<QT, KV, 128, 32>(a, p, st, items, ml, wacc, qk);
+    if (a->block_size == 16) valu_dispatch_g<QT, KV, 128, 16>(a, p, st, items, ws, qk);
+    else valu_dispatch_g<QT, KV, 128, 32>(a, p, st, items, ws, qk);
   }
 }
 
 template <typename QT>
 static void valu_dispatch_kv(const pa_decode_args* a, const DecodePlan& p, hipStream_t st, unsigned items,
-                             float2* ml, float* wacc, float qk) {
+                             const SplitK& ws, float qk) {
   switch (a->kv_dtype) {
-    case PA_F32: valu_dispatch_shape<QT, float>(a, p, st, items, ml, wacc, qk); break;
-    case PA_BF16: valu_dispatch_shape<QT, __bf16>(a, p, st, items, ml, wacc, qk); break;
-    default: valu_dispatch_shape<QT, signed char>(a, p, st, items, ml, wacc, qk); break;
+    case PA_F32: valu_dispatch_shape<QT, float>(a, p, st, items, ws, qk); break;
+    case PA_BF16: valu_dispatch_shape<QT, __bf16>(a, p, st, items, ws, qk); break;
+    default: valu_dispatch_shape<QT, signed char>(a, p, st, items, ws, qk); break;
   }
 }
 
@@ -696,24 +785,23 @@ pa_status launch_decode_valu(const pa_decode_args* a, const DecodePlan& p, hipSt
   const size_t items = (size_t)a->num_seqs * a->num_kv_heads * p.head_groups * p.num_partitions;
   if (items > 0x7fffffffu) return fail(PA_ERR_UNSUPPORTED, "pa_decode: grid too large");
   const float qk = a->scale * kLog2e;
-  float2* ml = p.num_partitions > 1 ? ws_ml_ptr(a) : nullptr;
-  float* wacc = p.num_partitions > 1 ? ws_acc_ptr(a, p) : nullptr;
-  if (a->q_dtype == PA_F32) valu_dispatch_kv<float>(a, p, st, (unsigned)items, ml, wacc, qk);
-  else valu_dispatch_kv<unsigned short>(a, p, st, (unsigned)items, ml, wacc, qk);
+  const SplitK ws = split_k(a, p);
+  if (a->q_dtype == PA_F32) valu_dispatch_kv<float>(a, p, st, (unsigned)items, ws, qk);
+  else valu_dispatch_kv<unsigned short>(a, p, st, (unsigned)items, ws, qk);
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode (vector-ALU kernel) launch");
 }
 
-pa_status launch_decode_reduce(const pa_decode_args* a, const DecodePlan& p, hipStream_t st) {
+pa_status launch_decode_merge(const pa_decode_args* a, const DecodePlan& p, hipStream_t st) {
   const size_t rows = (size_t)a->num_seqs * a->num_q_heads;
+  const SplitK ws = split_k(a, p);
+  const int max_tokens = a->max_blocks_per_seq * a->block_size;
   if (a->head_dim == 64)
-    hipLaunchKernelGGL(decode_reduce_kernel<64>, dim3((unsigned)rows), dim3(64), 0, st, (float*)a->out,
-                       ws_ml_ptr(a), ws_acc_ptr(a, p), a->context_lens, a->num_q_heads, p.partition_tokens,
-                       p.num_partitions);
+    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3((unsigned)rows), dim3(64), 0, st, (float*)a->out, ws,
+                       a->context_lens, a->num_q_heads, p.partition_tokens, p.num_partitions, max_tokens);
   else
-    hipLaunchKernelGGL(decode_reduce_kernel<128>, dim3((unsigned)rows), dim3(64), 0, st, (float*)a->out,
-                       ws_ml_ptr(a), ws_acc_ptr(a, p), a->context_lens, a->num_q_heads, p.partition_tokens,
-                       p.num_partitions);
+    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3((unsigned)rows), dim3(64), 0, st, (float*)a->out, ws,
+                       a->context_lens, a->num_q_heads, p.partition_tokens, p.num_partitions, max_tokens);
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode (merge kernel) launch");
 }

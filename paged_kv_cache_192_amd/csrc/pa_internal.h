@@ -28,6 +28,13 @@ inline int dtype_bytes(pa_dtype t) {
 
 enum KernelKind { KERNEL_VALU = 1, KERNEL_MFMA = 2 };
 
+// Longest partition, in blocks: the matrix-core kernel keeps a partition's
+// table entries in two registers of 64 lanes.
+constexpr int kMaxPartitionBlocks = 128;
+// Most partitions the automatic plan splits one sequence into (the last
+// wave of each (sequence, kv head) merges them all).
+constexpr int kMaxAutoPartitions = 32;
+
 // Everything the launchers need, derived on the host from pa_decode_args.
 struct DecodePlan {
   KernelKind kind;
@@ -41,17 +48,30 @@ struct DecodePlan {
 
 pa_status plan_decode(const pa_decode_args* a, DecodePlan* plan);
 
-// Workspace layout for num_partitions > 1:
-//   float2 ml [S][Hq][nP]        (running max in log2 units, sum of weights)
-//   float  acc[S][Hq][nP][D]     (unnormalised weighted sum of values)
-inline size_t ws_ml_bytes(int S, int Hq, int nP) {
-  size_t b = (size_t)S * Hq * nP * 2 * sizeof(float);
-  return (b + 255) & ~(size_t)255;
+// Workspace layout for num_partitions > 1 (offsets 256-byte aligned):
+//   float2 ml [S][Hq][nP]      reference max (log2 units), sum of weights
+//   float  acc[S][Hq][nP][D]   unnormalised weighted sum of values
+// Every entry a merge reads is written by the same call, so the workspace
+// needs no initialisation.
+struct WorkspaceLayout {
+  size_t ml_offset, acc_offset, bytes;
+};
+
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+inline WorkspaceLayout workspace_layout(const pa_decode_args* a, const DecodePlan& p) {
+  WorkspaceLayout L{0, 0, 0};
+  if (p.num_partitions <= 1) return L;
+  const size_t rows = (size_t)a->num_seqs * a->num_q_heads * p.num_partitions;
+  L.ml_offset = 0;
+  L.acc_offset = align256(rows * 2 * sizeof(float));
+  L.bytes = L.acc_offset + align256(rows * a->head_dim * sizeof(float));
+  return L;
 }
 
 pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipStream_t st);
 pa_status launch_decode_valu(const pa_decode_args* a, const DecodePlan& p, hipStream_t st);
-pa_status launch_decode_reduce(const pa_decode_args* a, const DecodePlan& p, hipStream_t st);
+pa_status launch_decode_merge(const pa_decode_args* a, const DecodePlan& p, hipStream_t st);
 
 pa_status launch_slot_mapping(const int32_t* block_tables, int32_t max_blocks, int32_t num_seqs, const int32_t* seq_idx,
                               const int32_t* positions, const int32_t* context_lens, int32_t T,

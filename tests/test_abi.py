@@ -61,11 +61,12 @@ def test_struct_layout_and_workspace_size():
     st, n = _ws(a)
     assert st == pa.PA_OK, pa.library().pa_last_error()
     # 3 seqs x 2 kv heads, 7 tiles: the planner splits the 100 tokens into
-    # partitions of 64 (4 tiles minimum) -> 2 partitions
-    P = 64
-    nP = -(-100 // P)
-    ml = (3 * 8 * nP * 8 + 255) // 256 * 256
-    assert n == ml + 3 * 8 * nP * 128 * 4
+    # partitions of 64 (4 tiles minimum) -> 2 partitions; workspace = the
+    # partial (m, l) rows, then the acc rows, 256-aligned
+    nP = -(-100 // 64)
+    rows = 3 * 8 * nP
+    al = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    assert n == al(rows * 8) + al(rows * 128 * 4)
     # one partition: no workspace
     st, n = _ws(_cpu_args(partition_tokens=128))
     assert st == pa.PA_OK and n == 0
@@ -93,7 +94,7 @@ def test_struct_layout_and_workspace_size():
     ("max_context_len", 161, pa.PA_ERR_INVALID),      # > 10 blocks x 16
     ("max_context_len", -1, pa.PA_ERR_INVALID),
     ("partition_tokens", 24, pa.PA_ERR_INVALID),
-    ("partition_tokens", 2048, pa.PA_ERR_INVALID),    # > 64 blocks
+    ("partition_tokens", 2064, pa.PA_ERR_INVALID),    # > 128 blocks
     ("kernel", 3, pa.PA_ERR_INVALID),
     ("num_seqs", -1, pa.PA_ERR_INVALID),
 ])

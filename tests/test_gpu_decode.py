@@ -271,7 +271,7 @@ def test_explicit_workspace_and_stream():
                                out=torch.empty(2, 32, 128, device="cuda:0"), partition_tokens=256)
     need = pa.decode_workspace_size(args)
     assert need > 0
-    ws = torch.empty(need + 64, dtype=torch.uint8, device="cuda:0")
+    ws = torch.zeros(need + 64, dtype=torch.uint8, device="cuda:0")
     side = torch.cuda.Stream()
     say("explicit workspace, side stream")
     with torch.cuda.stream(side):
@@ -279,3 +279,62 @@ def test_explicit_workspace_and_stream():
                         workspace=ws, partition_tokens=256)
     side.synchronize()
     assert np.array_equal(out.cpu().numpy().astype(np.float64), a)
+
+
+def test_workspace_reused_across_shapes():
+    """One workspace (filled with garbage first) serves calls of different
+    shapes and partition sizes back to back."""
+    big = synth.make_case("ws-big", 46, [5000, 3000, 700], 64, 8, 128, 16)
+    small = synth.make_case("ws-small", 47, [900, 33], 32, 8, 128, 32)
+    db, ds = case_on_device(big), case_on_device(small)
+    ws = torch.full((64 << 20,), 0xA5, dtype=torch.uint8, device="cuda:0")
+    for case, dev, P in ((big, db, 256), (small, ds, 64), (big, db, 0), (small, ds, 0), (big, db, 256)):
+        say("workspace reuse", case.name, P)
+        for kern in _kernels(case):
+            out = pa.decode(dev["q"], dev["k"], dev["v"], dev["bt"], dev["cl"], float(case.scale),
+                            case.max_context_len, workspace=ws, partition_tokens=P, kernel=kern)
+            torch.cuda.synchronize()
+            err = max_err(out.cpu().numpy().astype(np.float64), run_oracle(case))
+            assert err <= TOL_BF16, (case.name, P, kern, err)
+
+
+def test_graph_replay_matches_eager():
+    """A captured step (slot mapping, cache write, decode) replayed several
+    times, with eager work and synchronisations between replays, gives the
+    eager result every time."""
+    case = synth.make_case("graph", 48, [4000, 1234, 64, 8000], 64, 8, 128, 16)
+    dev = case_on_device(case)
+    kn = to_dev(synth.bf16_bits(np.random.default_rng(5).standard_normal((4, 8, 128), dtype=np.float32)))
+    out = torch.zeros(4, 64, 128, device="cuda:0")
+    slots = torch.empty(4, dtype=torch.int64, device="cuda:0")
+    main = torch.cuda.current_stream()
+
+    def calls(stream):
+        return [pa.prepare_slot_mapping(dev["bt"], 16, slots, context_lens=dev["cl"], stream=stream),
+                pa.prepare_reshape_and_cache(kn, kn, dev["k"], dev["v"], slots, stream=stream),
+                pa.PreparedDecode(dev["q"], dev["k"], dev["v"], dev["bt"], dev["cl"], float(case.scale), 8000, out,
+                                  stream=stream)]
+
+    say("graph eager reference")
+    for f in calls(main):
+        f()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(main)
+    gcalls = calls(cap)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        for f in gcalls:
+            f()
+    torch.cuda.synchronize()
+    for i in range(4):
+        say("graph replay", i)
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), i
+        for f in calls(main):  # eager work between replays
+            f()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), i
