@@ -5,9 +5,10 @@ Workload: the Llama-3-70B-shaped decode batch over all 80 layers -- 20
 sequences of 8,000 tokens, 64 query / 8 KV heads of 128, bf16 KV cache in
 blocks of 16 tokens with shuffled block tables (10,000 blocks and 655 MB of
 K+V per layer, 52.4 GB in HBM).  One step is the whole decode path of one
-token per sequence: the slot of each newest token, then for each of the 80
-layers the write of the new token's K/V into its slot and the paged
-attention over all 8,000 tokens.
+token per sequence: for each of the 80 layers, the write of the new token's
+K/V into its slot (found through the block table) and the paged attention
+over all 8,000 tokens -- by default in one fused pa_decode call per layer,
+with --unfused as pa_slot_mapping + pa_reshape_and_cache + pa_decode.
 
 Prints one JSON line.  ``value`` is KV GB/s over the whole step (K and V
 bytes of all 8,000 tokens x 80 layers, counted once, / step time), with
@@ -112,30 +113,40 @@ def run(args) -> dict:
     cl = torch.from_numpy(st["context_lens"]).to(dev)
     outs = [torch.empty(S, Hq, D, dtype=torch.float32, device=dev) for _ in range(L)]
     slots = torch.empty(S, dtype=torch.int64, device=dev)
-    probe = pa.make_decode_args(Q[0], K[0], V[0], bt, cl, scale, ctx, out=outs[0])
+    probe = pa.make_decode_args(Q[0], K[0], V[0], bt, cl, scale, ctx, out=outs[0],
+                                partition_tokens=args.partition_tokens)
     ws_bytes = pa.decode_workspace_size(probe)
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
+    fused = not args.unfused
+
     def prepare(stream):
-        """One step's calls with arguments packed once, on `stream`."""
-        calls = [pa.prepare_slot_mapping(bt, BS, slots, context_lens=cl, stream=stream)]
-        dec = []
+        """One step's calls, arguments packed once, on `stream`: per layer the
+        new token's cache write and the decode (one fused launch by default;
+        with --unfused a slot-mapping launch per step and a cache-write
+        launch per layer before each decode)."""
+        pre = [pa.prepare_slot_mapping(bt, BS, slots, context_lens=cl, stream=stream)] if not fused else []
+        layers = []
         for layer in range(L):
-            calls.append(pa.prepare_reshape_and_cache(KN[layer], VN[layer], K[layer], V[layer], slots,
-                                                      stream=stream))
+            writes = [] if fused else [pa.prepare_reshape_and_cache(KN[layer], VN[layer], K[layer], V[layer], slots,
+                                                                     stream=stream)]
             d = pa.PreparedDecode(Q[layer], K[layer], V[layer], bt, cl, scale, ctx, outs[layer], workspace=ws,
-                                  stream=stream)
-            calls.append(d)
-            dec.append(d)
-        return calls, dec
+                                  stream=stream, new_key=KN[layer] if fused else None,
+                                  new_value=VN[layer] if fused else None, partition_tokens=args.partition_tokens)
+            layers.append((writes, d))
+        return pre, layers
 
     main_stream = torch.cuda.current_stream()
-    eager_calls, eager_dec = prepare(main_stream)
+    eager_pre, eager_layers = prepare(main_stream)
 
     def eager_step():
-        for f in eager_calls:
+        for f in eager_pre:
             f()
+        for writes, d in eager_layers:
+            for f in writes:
+                f()
+            d()
 
     # the same step captured once as a HIP graph (no memsets in it: every
     # node is one of the library's kernels)
@@ -143,11 +154,15 @@ def run(args) -> dict:
     if args.graph:
         cap = torch.cuda.Stream()
         cap.wait_stream(main_stream)
-        graph_calls, _ = prepare(cap)
+        g_pre, g_layers = prepare(cap)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=cap):
-            for f in graph_calls:
+            for f in g_pre:
                 f()
+            for writes, d in g_layers:
+                for f in writes:
+                    f()
+                d()
         torch.cuda.synchronize()
 
     def step():
@@ -182,11 +197,13 @@ def run(args) -> dict:
     launch_ms = []
     for _ in range(max(1, min(args.steps, 5))):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
-        eager_calls[0]()
-        for layer in range(L):
-            eager_calls[1 + 2 * layer]()
+        for f in eager_pre:
+            f()
+        for layer, (writes, d) in enumerate(eager_layers):
+            for f in writes:
+                f()
             evs[layer][0].record()
-            eager_dec[layer]()
+            d()
             evs[layer][1].record()
         torch.cuda.synchronize()
         launch_ms += [a.elapsed_time(b) for a, b in evs]
@@ -222,15 +239,138 @@ def run(args) -> dict:
         "wall_s_timed_region": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_mfma_kernel (pa_decode: one launch, merge fused)", "launch_ms_avg": round(launch_avg, 5),
+                     "kernel": "pa_decode = decode_mfma_kernel + decode_merge_kernel", "launch_ms_avg": round(launch_avg, 5),
                      "launch_ms_p10": round(launch_ms[len(launch_ms) // 10], 5),
                      "launch_ms_p90": round(launch_ms[(9 * len(launch_ms)) // 10], 5),
                      "algorithmic_bytes_per_launch": alg_launch, "workspace_bytes": ws_bytes},
         "waste": waste_report(cls, BS, 8192),
-        "step_mode": "hip graph replay" if graph is not None else "eager prepared calls",
+        "step_mode": ("hip graph replay" if graph is not None else "eager prepared calls") +
+                     (", cache write fused into pa_decode" if fused else ", separate slot-mapping and cache-write launches"),
     }
     if args.cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args, K, V, Q, st, L)
+    return res
+
+
+WORKLOADS = {
+    "llama3-70b": "70B-shaped GQA decode, 80 layers (20 x 8,000 tokens, 64/8 heads, bf16, block 16)",
+    "tiny": "tiny fp32 decode (4 seqs of 17/33/100/200 tokens, 8 heads of 64, block 16)",
+    "llama13b": "13B-shaped MHA decode, one layer (32 seqs, U[200,2048] tokens, 40 heads of 128, bf16)",
+    "prefix": "prefix sharing + copy-on-write, one layer (50 seqs, 2,000 shared + U[50,500], 32/8 heads, block 32)",
+    "int8": "int8 KV decode, one layer (64 seqs, log-normal lengths, 32/8 heads, per-(block, head) scales)",
+}
+
+
+def run_single_layer(args) -> dict:
+    """The four one-layer workloads.  A step is one decode layer per replica:
+    the pool is replicated R times (R such that >= 1 GB is touched between
+    reuses of the same bytes, so MALL/L2 cannot serve it) and each step
+    walks all replicas; per-layer time = step time / R.  The new token's
+    cache write is fused into pa_decode (not for int8: no quantising
+    write); the prefix workload also copies the shared partial block to 50
+    scratch blocks per layer (pa_copy_blocks) before decoding."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_192_amd as pa
+    import synth
+
+    pa.library()
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    w = args.workload
+    case = {"tiny": synth.config1, "llama13b": synth.config2, "prefix": synth.config4,
+            "int8": synth.config5}[w]()
+    if w == "int8":
+        synth.random_int8_cache(case, seed=55)
+
+    def put(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    S, Hq, Hkv, D, BS = case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim, case.block_size
+    e = {"f32": 4, "bf16": 2, "i8": 1}[case.kv_dtype]
+    eq = {"f32": 4, "bf16": 2}[case.q_dtype]
+    layer_bytes = 2 * case.k_cache.nbytes
+    R = max(1, -(-(1 << 30) // layer_bytes)) if w != "tiny" else 1
+    q, bt, cl = put(case.q), put(case.block_tables), put(case.context_lens)
+    k0, v0 = put(case.k_cache), put(case.v_cache)
+    ks = put(case.k_scales) if case.k_scales is not None else None
+    vs = put(case.v_scales) if case.v_scales is not None else None
+    K = [k0] + [k0.clone() for _ in range(R - 1)]
+    V = [v0] + [v0.clone() for _ in range(R - 1)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    tdt = torch.float32 if case.kv_dtype == "f32" else torch.bfloat16
+    newk = torch.randn(S, Hkv, D, generator=gen, device=dev).to(tdt) if w != "int8" else None
+    newv = torch.randn(S, Hkv, D, generator=gen, device=dev).to(tdt) if w != "int8" else None
+    pairs = None
+    if w == "prefix":
+        pr = np.stack([np.full(S, case.extra["partial"]), case.extra["scratch"]], axis=1).astype(np.int64)
+        pairs = put(pr)
+    outs = [torch.empty(S, Hq, D, dtype=torch.float32, device=dev) for _ in range(R)]
+    ws = torch.zeros(1 << 26, dtype=torch.uint8, device=dev)
+    mcl = case.max_context_len
+
+    def prepare(stream):
+        calls = []
+        for r in range(R):
+            if pairs is not None:
+                calls.append(pa.prepare_copy_blocks(K[r], V[r], pairs, stream=stream))
+            calls.append(pa.PreparedDecode(q, K[r], V[r], bt, cl, float(case.scale), mcl, outs[r], k_scales=ks,
+                                           v_scales=vs, workspace=ws, stream=stream, new_key=newk, new_value=newv,
+                                           partition_tokens=args.partition_tokens))
+        return calls
+
+    main = torch.cuda.current_stream()
+    eager = prepare(main)
+    for f in eager:
+        f()
+    torch.cuda.synchronize()
+    ref = torch.stack(outs).clone()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(main)
+    gcalls = prepare(cap)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        for f in gcalls:
+            f()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(torch.stack(outs), ref):
+        raise RuntimeError("graph replay differs from the eager step")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_layer = e0.elapsed_time(e1) / args.steps / R
+    cls = case.context_lens
+    kvb = kv_bytes(cls, Hkv, D, e)
+    alg = decode_algorithmic_bytes(cls, Hq, Hkv, D, BS, e, eq, int8_scales=(w == "int8"))
+    res = {"workload": w, "description": WORKLOADS[w], "replicas": R, "partition_tokens": args.partition_tokens, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_layer": round(ms_layer, 5), "tokens_per_s": round(S / (ms_layer * 1e-3), 1),
+           "kv_gbs": round(kvb / (ms_layer * 1e-3) / 1e9, 1),
+           "pct_hbm_peak": round(100.0 * alg / (ms_layer * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+           "algorithmic_bytes_per_layer": alg, "kv_bytes_per_layer": kvb, "sum_ctx": int(sum(int(x) for x in cls)),
+           "step": ("copy_blocks + " if pairs is not None else "") + "pa_decode" +
+                   (" with fused cache write" if newk is not None else "")}
+    if w == "prefix":
+        # unique bytes: every physical block's valid tokens once
+        valid = synth.valid_slots_per_block(case)
+        uniq = 2 * Hkv * D * e * int(valid.sum())
+        copy = 2 * 2 * len(case.extra["scratch"]) * Hkv * BS * D * e
+        res["unique_kv_bytes_per_layer"] = uniq
+        res["copy_bytes_per_layer"] = copy
+        res["unique_kv_gbs"] = round(uniq / (ms_layer * 1e-3) / 1e9, 1)
+        res["effective_kv_gbs_note"] = "kv_gbs counts each sequence's prefix (logical bytes)"
+    res["waste"] = waste_report(cls, BS, 2048 if w != "int8" else 32768)
     return res
 
 
@@ -301,11 +441,18 @@ def main():
     ap.add_argument("--layers", type=int, default=80, help="layers of the 70B-shaped model (80 is the workload)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--unfused", action="store_true",
+                    help="separate slot-mapping and reshape_and_cache launches instead of the fused cache write")
     ap.add_argument("--eager", dest="graph", action="store_false",
                     help="launch each call from Python instead of replaying the captured step")
     ap.add_argument("--mode", choices=["decode", "copy-calibration"], default="decode",
                     help="copy-calibration: a known-size block copy for scaling HBM byte counters")
     ap.add_argument("--copy-pairs", type=int, default=4096)
+    ap.add_argument("--partition-tokens", type=int, default=0,
+                    help="override the library's automatic split-K partition length (tuning only)")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="llama3-70b",
+                    help="the 70B-shaped 80-layer step (default; the JSON metric line) or one of the single-layer "
+                         "workloads, reported as a per-layer record")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path (asked for --gpus %d)"
@@ -314,7 +461,12 @@ def main():
     if args.layers != 80:
         print("note: --layers %d is not the 80-layer workload; the result is for tuning only" % args.layers,
               file=sys.stderr)
-    res = copy_calibration(args) if args.mode == "copy-calibration" else run(args)
+    if args.mode == "copy-calibration":
+        res = copy_calibration(args)
+    elif args.workload != "llama3-70b":
+        res = run_single_layer(args)
+    else:
+        res = run(args)
     print(json.dumps(res), flush=True)
 
 

@@ -61,7 +61,7 @@ const char* pa_status_string(pa_status s);
 /* Message of the last failure on the calling thread ("" if none). */
 const char* pa_last_error(void);
 /* ABI version of this header (incremented on any incompatible change). */
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 int32_t pa_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -107,6 +107,15 @@ int32_t pa_abi_version(void);
  * call: its contents are not needed before or after it.  Calls that may
  * run concurrently need separate workspaces.
  *
+ * Optional fused cache write: when `new_key` and `new_value` are given
+ * ([num_seqs][num_kv_heads][head_dim] of kv_dtype, device), the call first
+ * stores, for every sequence with n >= 1, the newest token's key and value
+ * into the slot of position n - 1 (block_tables[s][(n-1)/BS], slot
+ * (n-1) % BS, every kv head) and attends with them.  The result, cache
+ * bytes included, is that of pa_slot_mapping (context_lens form) +
+ * pa_reshape_and_cache + pa_decode, in one launch.  n must not exceed
+ * max_context_len.  Not available for int8 caches (PA_ERR_UNSUPPORTED).
+ *
  * `kernel` selects the implementation: 0 = automatic, 1 = vector-ALU
  * kernel (any supported case), 2 = matrix-core kernel (bf16 or int8
  * caches with bf16 queries, head_dim 128, 2..16 query heads per kv head;
@@ -119,8 +128,8 @@ typedef struct {
   pa_dtype out_dtype;
   const void* q;
   pa_dtype q_dtype;
-  const void* k_cache;
-  const void* v_cache;
+  void* k_cache;                 /* written only by the fused cache write */
+  void* v_cache;
   pa_dtype kv_dtype;
   const float* k_scales;         /* non-NULL iff kv_dtype == PA_I8 */
   const float* v_scales;
@@ -140,6 +149,8 @@ typedef struct {
   void* workspace;
   size_t workspace_bytes;
   void* stream;                  /* hipStream_t */
+  const void* new_key;           /* optional fused cache write: both or neither */
+  const void* new_value;
 } pa_decode_args;
 
 /* Host only: bytes of workspace pa_decode needs for these arguments

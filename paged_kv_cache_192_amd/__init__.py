@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_OOM, PA_ERR_STATE, PA_ERR_HIP = range(6)
 PA_F32, PA_BF16, PA_I8 = 0, 1, 2
 KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
+ABI_VERSION = 2
 
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_OOM",
                 4: "PA_ERR_STATE", 5: "PA_ERR_HIP"}
@@ -62,6 +63,8 @@ class DecodeArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
+        ("new_key", ctypes.c_void_p),
+        ("new_value", ctypes.c_void_p),
     ]
 
 
@@ -110,8 +113,8 @@ def library() -> ctypes.CDLL:
     lib.pa_pool_num_blocks.argtypes = [P]
     lib.pa_pool_num_blocks.restype = i32
     del i64
-    if lib.pa_abi_version() != 1:
-        raise RuntimeError("libpa ABI version %d, binding expects 1" % lib.pa_abi_version())
+    if lib.pa_abi_version() != ABI_VERSION:
+        raise RuntimeError("libpa ABI version %d, binding expects %d" % (lib.pa_abi_version(), ABI_VERSION))
     _lib = lib
     return lib
 
@@ -159,10 +162,12 @@ def _stream(stream) -> int:
 
 def make_decode_args(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int,
                      out=None, k_scales=None, v_scales=None, workspace=None, partition_tokens: int = 0,
-                     kernel: int = KERNEL_AUTO, stream=None, device_pointers: bool = True) -> DecodeArgs:
+                     kernel: int = KERNEL_AUTO, stream=None, device_pointers: bool = True, new_key=None,
+                     new_value=None) -> DecodeArgs:
     """Fill a DecodeArgs from tensors.  q ``[S][Hq][D]``; caches
     ``[NB][Hkv][BS][D]``; block_tables int32 ``[S][max_blocks]``;
-    context_lens int32 ``[S]``; out float32 ``[S][Hq][D]``."""
+    context_lens int32 ``[S]``; out float32 ``[S][Hq][D]``; optional
+    new_key/new_value ``[S][Hkv][D]`` for the fused cache write."""
     S, Hq, D = q.shape
     NB, Hkv, BS, D2 = k_cache.shape
     if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
@@ -196,6 +201,11 @@ def make_decode_args(q, k_cache, v_cache, block_tables, context_lens, scale: flo
     a.workspace = get(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a.stream = _stream(stream) if device_pointers else None
+    for name, t in (("new_key", new_key), ("new_value", new_value)):
+        if t is not None and tuple(t.shape) != (S, Hkv, D):
+            raise ValueError("%s must be [%d][%d][%d]" % (name, S, Hkv, D))
+    a.new_key = get(new_key)
+    a.new_value = get(new_value)
     return a
 
 
@@ -207,7 +217,7 @@ def decode_workspace_size(args: DecodeArgs) -> int:
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int, out=None,
            k_scales=None, v_scales=None, workspace=None, partition_tokens: int = 0, kernel: int = KERNEL_AUTO,
-           stream=None):
+           stream=None, new_key=None, new_value=None):
     """Paged decode attention (``pa_decode``).  Returns ``out`` (float32
     ``[S][Hq][D]``), allocated on q's device when not given.  A zeroed
     workspace is allocated when needed and none is passed; a caller-owned
@@ -218,7 +228,8 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_co
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     args = make_decode_args(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, out=out,
                             k_scales=k_scales, v_scales=v_scales, workspace=workspace,
-                            partition_tokens=partition_tokens, kernel=kernel, stream=stream)
+                            partition_tokens=partition_tokens, kernel=kernel, stream=stream, new_key=new_key,
+                            new_value=new_value)
     need = decode_workspace_size(args)
     if need and workspace is None:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
@@ -341,18 +352,20 @@ class PreparedDecode:
 
     def __init__(self, q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int, out,
                  k_scales=None, v_scales=None, workspace=None, partition_tokens: int = 0, kernel: int = KERNEL_AUTO,
-                 stream=None):
+                 stream=None, new_key=None, new_value=None):
         torch = _torch()
         self.args = make_decode_args(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
                                      out=out, k_scales=k_scales, v_scales=v_scales, workspace=workspace,
-                                     partition_tokens=partition_tokens, kernel=kernel, stream=stream)
+                                     partition_tokens=partition_tokens, kernel=kernel, stream=stream,
+                                     new_key=new_key, new_value=new_value)
         need = decode_workspace_size(self.args)
         if need and (workspace is None or self.args.workspace_bytes < need):
             workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
             self.args.workspace = workspace.data_ptr()
             self.args.workspace_bytes = need
         self.workspace_bytes = need
-        self._keep = (q, k_cache, v_cache, block_tables, context_lens, out, k_scales, v_scales, workspace)
+        self._keep = (q, k_cache, v_cache, block_tables, context_lens, out, k_scales, v_scales, workspace, new_key,
+                      new_value)
         self._fn = library().pa_decode
         self._ref = ctypes.byref(self.args)
 

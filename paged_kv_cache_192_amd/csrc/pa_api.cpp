@@ -28,11 +28,16 @@ static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 static bool valid_dtype(int t) { return t == PA_F32 || t == PA_BF16 || t == PA_I8; }
 
-// Waves a decode launch should put on the chip: about five per compute unit
-// of a 256-CU MI355X.  Measured on the 70B-shaped layer, five waves per CU
-// keep the HBM busy, while more waves per CU only compete for the CU's
-// memory pipeline (and two or three leave it short of loads in flight).
-static const int kTargetWaves = 1280;
+// Waves a decode launch should put on the chip (256 CUs on MI355X).  The
+// matrix-core kernel keeps two 16-token tiles in flight per wave: with a
+// bf16 cache that is 16 KB, and about 2.5 waves per CU (~40 KB of loads in
+// flight per CU) measured fastest on the 70B-shaped layer, while five per
+// CU lost 10 %.  Int8 tiles are half the size, so twice the waves.  The
+// vector-ALU kernel keeps one tile in flight; five waves per CU.
+static int target_waves(KernelKind kind, pa_dtype kv) {
+  if (kind == KERNEL_MFMA) return kv == PA_I8 ? 1280 : 640;
+  return 1280;
+}
 
 pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   if (!a) return fail(PA_ERR_INVALID, "pa_decode: args is NULL");
@@ -61,6 +66,10 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   if (i8 != (a->k_scales != nullptr) || i8 != (a->v_scales != nullptr))
     return fail(PA_ERR_INVALID, "pa_decode: k_scales/v_scales must be given exactly for int8 caches");
   if (!std::isfinite(a->scale)) return fail(PA_ERR_INVALID, "pa_decode: scale is not finite");
+  if ((a->new_key == nullptr) != (a->new_value == nullptr))
+    return fail(PA_ERR_INVALID, "pa_decode: give both new_key and new_value, or neither");
+  if (a->new_key && i8)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: the fused cache write needs a quantising write for int8 caches");
   if (a->max_context_len < 0 || (int64_t)a->max_context_len > (int64_t)a->max_blocks_per_seq * a->block_size)
     return fail(PA_ERR_INVALID, "pa_decode: max_context_len %d outside [0, max_blocks_per_seq*block_size]",
                 a->max_context_len);
@@ -95,10 +104,11 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   int P = a->partition_tokens;
   if (P == 0) {
     // Split each sequence into nP equal partitions so the grid holds about
-    // kTargetWaves waves, within [4 tiles, kMaxPartitionBlocks blocks] per
+    // target_waves() waves, within [4 tiles, kMaxPartitionBlocks blocks] per
     // partition and at most kMaxAutoPartitions partitions.
     const int64_t groups = (int64_t)(a->num_seqs > 0 ? a->num_seqs : 1) * a->num_kv_heads * p->head_groups;
-    int64_t nP = (kTargetWaves + groups / 2) / groups;
+    const int64_t target = target_waves(kind, a->kv_dtype);
+    int64_t nP = (target + groups / 2) / groups;
     if (nP < 1) nP = 1;
     if (nP > kMaxAutoPartitions) nP = kMaxAutoPartitions;
     if (nP > (tiles + 3) / 4) nP = (tiles + 3) / 4;
@@ -150,8 +160,9 @@ pa_status pa_decode(const pa_decode_args* a) {
   if (a->num_seqs == 0) return PA_OK;
   if (!a->out || !a->q || !a->k_cache || !a->v_cache || !a->block_tables || !a->context_lens)
     return fail(PA_ERR_INVALID, "pa_decode: a required device pointer is NULL");
-  if (!aligned(a->out, 16) || !aligned(a->q, 16) || !aligned(a->k_cache, 16) || !aligned(a->v_cache, 16))
-    return fail(PA_ERR_INVALID, "pa_decode: out, q and the caches must be 16-byte aligned");
+  if (!aligned(a->out, 16) || !aligned(a->q, 16) || !aligned(a->k_cache, 16) || !aligned(a->v_cache, 16) ||
+      !aligned(a->new_key, 16) || !aligned(a->new_value, 16))
+    return fail(PA_ERR_INVALID, "pa_decode: out, q, the caches and new_key/new_value must be 16-byte aligned");
   if (!aligned(a->block_tables, 4) || !aligned(a->context_lens, 4) ||
       (a->k_scales && (!aligned(a->k_scales, 4) || !aligned(a->v_scales, 4))))
     return fail(PA_ERR_INVALID, "pa_decode: tables, lengths and scales must be 4-byte aligned");

@@ -107,55 +107,57 @@ struct SplitK {
   float* acc;     // [S][Hq][nP][D]: unnormalised weighted sum of values
 };
 
-// Merge the np partials of rows row0 .. row0+nh-1 (row = s*Hq + h) into out.
-template <int D>
-__device__ void merge_partials(float* __restrict__ out, const SplitK& w, size_t row0, int nh, int nP, int np) {
-  constexpr int PER = D / 64;
-  const int lane = threadIdx.x;
-  for (int i = 0; i < nh; ++i) {
-    const size_t r = (row0 + i) * (size_t)nP;
-    float M = kNegInf;
-    for (int p0 = 0; p0 < np; p0 += 64)
-      if (p0 + lane < np) M = fmaxf(M, w.ml[r + p0 + lane].x);
-    M = wave_max(M);
-    float L = 0.f, a[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) a[k] = 0.f;
-    if (M != kNegInf) {
-      for (int p0 = 0; p0 < np; p0 += 64) {
-        const int cnt = min(64, np - p0);
-        float wt = 0.f;
-        if (lane < cnt) {
-          const float2 v = w.ml[r + p0 + lane];
-          wt = v.y > 0.f ? fast_exp2(v.x - M) : 0.f;
-          L = fmaf(wt, v.y, L);
-        }
-        const float* src = w.acc + (r + p0) * D + lane;
-#pragma unroll 4
-        for (int k = 0; k < cnt; ++k) {
-          const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), k));
-#pragma unroll
-          for (int q = 0; q < PER; ++q) a[q] = fmaf(wk, src[(size_t)k * D + 64 * q], a[q]);
-        }
-      }
-    }
-    L = wave_sum(L);
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    float* o = out + (row0 + i) * D + lane;
-#pragma unroll
-    for (int q = 0; q < PER; ++q) o[64 * q] = a[q] * inv;
-  }
-}
-
-// One wave per output row (s, h).
+// One wave per output row (s, h): out = sum_p 2^(m_p - M) acc_p / sum_p
+// 2^(m_p - M) l_p over the np partitions that hold tokens, in partition
+// order.  Partitions are read sixteen at a time, all loads of a group
+// issued together (one memory round trip per group); groups after the
+// first rescale the running sums to the new maximum.
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(float* __restrict__ out, SplitK ws,
                                                           const int32_t* __restrict__ context_lens, int Hq, int P,
                                                           int nP, int max_tokens) {
-  const int row = blockIdx.x;
+  constexpr int PER = D / 64;
+  constexpr int GRP = 16;
+  const int lane = threadIdx.x;
+  const size_t row = blockIdx.x;
   const int n = min(context_lens[row / Hq], max_tokens);
   const int np = n > 0 ? min(nP, (n + P - 1) / P) : 0;
-  merge_partials<D>(out, ws, row, 1, nP, np);
+  const size_t r = row * (size_t)nP;
+  float m_run = kNegInf, L = 0.f, a[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) a[q] = 0.f;
+  for (int p0 = 0; p0 < np; p0 += GRP) {
+    const int cnt = min(GRP, np - p0);
+    float part[GRP][PER];
+    const float* src = ws.acc + (r + p0) * D + lane;
+#pragma unroll
+    for (int k = 0; k < GRP; ++k)
+#pragma unroll
+      for (int q = 0; q < PER; ++q) part[k][q] = k < cnt ? src[(size_t)k * D + 64 * q] : 0.f;
+    const float2 v = lane < cnt ? ws.ml[r + p0 + lane] : float2{kNegInf, 0.f};
+    const float mc = wave_max(v.y > 0.f ? v.x : kNegInf);
+    const float m_new = fmaxf(m_run, mc);
+    if (m_new == kNegInf) continue;  // no weight anywhere yet
+    if (m_run != kNegInf && m_run != m_new) {
+      const float alpha = fast_exp2(m_run - m_new);
+      L *= alpha;
+#pragma unroll
+      for (int q = 0; q < PER; ++q) a[q] *= alpha;
+    }
+    m_run = m_new;
+    const float w = (lane < cnt && v.y > 0.f) ? fast_exp2(v.x - m_new) : 0.f;
+    L += wave_sum(w * v.y);
+#pragma unroll
+    for (int k = 0; k < GRP; ++k) {
+      const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
+#pragma unroll
+      for (int q = 0; q < PER; ++q) a[q] = fmaf(wk, part[k][q], a[q]);
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float* o = out + row * D + lane;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) o[64 * q] = a[q] * inv;
 }
 
 // ===========================================================================
@@ -188,26 +190,43 @@ struct MfmaTile {
   u32x4_t v[4];
 };
 
-// base: the tile's first row in the (block, kv head) chunk (wave-uniform);
-// koff / voff: this lane's byte offsets, the same for every tile.
+// A tile's loads are buffer loads: the tile's first row is the base of a
+// scalar resource descriptor covering exactly the 16 rows, and each lane
+// adds a constant byte offset (koff[i] / voff[i]) held in a register that is
+// never rewritten, so no load ever has to wait for an earlier one to finish
+// before its address can be formed.  An access past the 16 rows would read
+// zeros instead of touching other memory.
+constexpr int kBufferFormat = 0x00020000;  // raw buffer, 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, bytes, kBufferFormat);
+}
+__device__ __forceinline__ u32x4_t bld16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2 /* nt */));
+}
+__device__ __forceinline__ u32x2_t bld8(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2 /* nt */));
+}
+
 template <bool I8>
-__device__ __forceinline__ void mfma_load_tile(MfmaTile<I8>& T, const char* kbase, const char* vbase, unsigned koff,
-                                               unsigned voff) {
-  constexpr int ROW = I8 ? 128 : 256;  // bytes per cached token row (head_dim 128)
+__device__ __forceinline__ void mfma_load_tile(MfmaTile<I8>& T, const char* kbase, const char* vbase,
+                                               const unsigned (&koff)[4], const unsigned (&voff)[4]) {
+  constexpr int TILE = 16 * (I8 ? 128 : 256);  // bytes of 16 token rows
+  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase, TILE), rv = tile_rsrc(vbase, TILE);
   if (I8) {
-    T.k[0] = ld16(kbase + koff);
-    T.k[1] = ld16(kbase + koff + 16);
+    T.k[0] = bld16(rk, koff[0]);
+    T.k[1] = bld16(rk, koff[1]);
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) T.k[i] = ld16(kbase + koff + i * 1024);
+    for (int i = 0; i < 4; ++i) T.k[i] = bld16(rk, koff[i]);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (I8) {
-      u32x2_t w = ld8(vbase + voff + i * ROW);
+      const u32x2_t w = bld8(rv, voff[i]);
       T.v[i] = u32x4_t{w[0], w[1], 0u, 0u};
     } else {
-      T.v[i] = ld16(vbase + voff + i * ROW);
+      T.v[i] = bld16(rv, voff[i]);
     }
   }
 }
@@ -259,10 +278,10 @@ __device__ __forceinline__ void mfma_item(int bid, int nblk, int Hkv, int nP, in
 template <bool I8, int BS>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(
     float* __restrict__ out, SplitK ws,
-    const unsigned short* __restrict__ q, const char* __restrict__ k_cache, const char* __restrict__ v_cache,
+    const unsigned short* __restrict__ q, char* __restrict__ k_cache, char* __restrict__ v_cache,
     const float* __restrict__ k_scales, const float* __restrict__ v_scales, const int32_t* __restrict__ tables,
     int max_blocks, const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int NB, float qk_log2,
-    int P, int nP) {
+    int P, int nP, const char* __restrict__ new_k, const char* __restrict__ new_v) {
   constexpr int D = 128;
   constexpr int E = I8 ? 1 : 2;
   const int lane = threadIdx.x;
@@ -312,18 +331,35 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
 
   constexpr int ROW = D * E;                       // bytes per token row
   const size_t head_stride = (size_t)BS * ROW;     // bytes per (block, kv head)
+
+  // Fused cache write of the newest token (position n - 1): the wave whose
+  // partition holds it reads its K/V row (16 B chunk c per lane), stores it
+  // into the cache slot at the end and attends with it in the tile that
+  // holds the position (bf16 caches only; the host rejects int8).
+  const int tnew = n - 1;
+  const bool owns_new = !I8 && new_k != nullptr && tnew >= t_begin && tnew < t_end;  // wave-uniform
+  u32x4_t nk = {0u, 0u, 0u, 0u}, nv = {0u, 0u, 0u, 0u};
+  if (owns_new) {
+    const size_t src = ((size_t)s * Hkv + g) * ROW + (size_t)c * 16;
+    nk = *(const u32x4_t*)(new_k + src);
+    nv = *(const u32x4_t*)(new_v + src);
+  }
   // bf16 K goes through a per-wave LDS tile of 16 rows x 16 chunks of 16 B;
   // chunk ch of row r sits at position ch ^ r, so both the row-wise writes
   // and the MFMA-layout reads (16 rows, one chunk each) hit distinct banks.
   __shared__ u32x4_t ktile[I8 ? 1 : 256];
-  const unsigned koff = I8 ? c * ROW + j * 32 : lane * 16;
+  unsigned koff[4], voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    koff[i] = I8 ? c * ROW + j * 32 + 16 * (i & 1) : lane * 16 + i * 1024;
+    voff[i] = (4 * j + i) * ROW + c * 8 * E;
+  }
   int kw[4], kr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     kw[i] = (4 * i + j) * 16 + (c ^ (4 * i + j));  // write slot of load i
     kr[i] = c * 16 + ((i * 4 + j) ^ c);            // read slot of d-chunk (i*4 + j), row c
   }
-  const unsigned voff = 4 * j * ROW + c * 8 * E;
   auto tile_ptrs = [&](int ti, const char*& kb, const char*& vb, bool& ok, float& ks, float& vs) {
     const int e = (ti * 16) / BS - tbl_base;
     int b = e < 64 ? __builtin_amdgcn_readlane(tbl0, e) : __builtin_amdgcn_readlane(tbl1, e - 64);
@@ -344,9 +380,17 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   float m_run = kNegInf, l_run = 0.f;
 
   auto compute = [&](MfmaTile<I8>& T, int ti, bool ok, float ks, float vs) {
+    const bool new_tile = owns_new && ti == (tnew >> 4);  // wave-uniform
+    const int rnew = tnew & 15;
     if (!I8) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) ktile[kw[i]] = T.k[i];
+      if (new_tile) {
+        if (j == 0) ktile[rnew * 16 + (c ^ rnew)] = nk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * j + i == rnew) T.v[i] = nv;
+      }
     }
     // ---- scores
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
@@ -456,6 +500,16 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     if (++ti >= tile_end) break;
   }
 
+  if (owns_new && j == 0) {
+    const int e = tnew / BS - tbl_base;
+    const int b = e < 64 ? __builtin_amdgcn_readlane(tbl0, e) : __builtin_amdgcn_readlane(tbl1, e - 64);
+    if (b >= 0 && b < NB) {
+      const size_t dst = ((size_t)b * Hkv + g) * head_stride + (size_t)(tnew % BS) * ROW + (size_t)c * 16;
+      *(u32x4_t*)(k_cache + dst) = nk;
+      *(u32x4_t*)(v_cache + dst) = nv;
+    }
+  }
+
   const float l_tot = xor_sum_rows(l_run);
   // lane holds d = 32j + 8r + e in acc[e][r]
   if (nP == 1) {
@@ -560,10 +614,10 @@ __device__ __forceinline__ void load_q(const QT* p, float (&v)[DC]) {
 template <typename QT, typename KV, int D, int BS, int GT>
 __global__ __launch_bounds__(64) void decode_valu_kernel(
     float* __restrict__ out, SplitK ws, const QT* __restrict__ q,
-    const char* __restrict__ k_cache, const char* __restrict__ v_cache, const float* __restrict__ k_scales,
+    char* __restrict__ k_cache, char* __restrict__ v_cache, const float* __restrict__ k_scales,
     const float* __restrict__ v_scales, const int32_t* __restrict__ tables, int max_blocks,
     const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int head_groups, int NB, float qk_log2,
-    int P, int nP) {
+    int P, int nP, const char* __restrict__ new_k, const char* __restrict__ new_v) {
   constexpr int DC = D / 16;
   constexpr bool I8 = sizeof(KV) == 1;
   constexpr int E = sizeof(KV);
@@ -617,6 +671,12 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
 
   const int32_t* trow = tables + (size_t)s * max_blocks;
   const size_t head_stride = (size_t)BS * D * E;
+  // Fused cache write of the newest token (position n - 1): lanes holding
+  // that position read its K/V chunk from new_k/new_v instead of the cache;
+  // the first head group's wave stores it into the slot at the end.
+  const int tnew = n - 1;
+  const bool owns_new = !I8 && new_k != nullptr && tnew >= t_begin && tnew < t_end;  // wave-uniform
+  const size_t new_off = ((size_t)s * Hkv + g) * D * E + (size_t)c * DC * E;
   for (int t4 = t_begin; t4 < t_end; t4 += 16) {
     // one 16-token tile: four passes of four tokens
     const int lb = t4 / BS;
@@ -631,8 +691,9 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const size_t roff = off + (size_t)(row0 + 4 * r + tt) * D * E + (size_t)c * DC * E;
-      KvChunk<KV, DC>::load(k_cache + roff, kv[r]);
-      KvChunk<KV, DC>::load(v_cache + roff, vv[r]);
+      const bool from_new = owns_new && t4 + 4 * r + tt == tnew;
+      KvChunk<KV, DC>::load(from_new ? new_k + new_off : k_cache + roff, kv[r]);
+      KvChunk<KV, DC>::load(from_new ? new_v + new_off : v_cache + roff, vv[r]);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -669,6 +730,18 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
         const float pv = pw * vs;
 #pragma unroll
         for (int k = 0; k < DC; ++k) acc[i][k] = fmaf(pv, valid ? vv[r][k] : 0.f, acc[i][k]);
+      }
+    }
+  }
+
+  if (owns_new && hg == 0 && tt == (tnew & 3)) {
+    const int32_t b = trow[tnew / BS];
+    if (b >= 0 && b < NB) {
+      const size_t dst = ((size_t)b * Hkv + g) * head_stride + (size_t)(tnew % BS) * D * E + (size_t)c * DC * E;
+#pragma unroll
+      for (int k = 0; k < DC * E; k += 4) {
+        *(unsigned*)(k_cache + dst + k) = *(const unsigned*)(new_k + new_off + k);
+        *(unsigned*)(v_cache + dst + k) = *(const unsigned*)(new_v + new_off + k);
       }
     }
   }
@@ -726,10 +799,10 @@ pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipSt
   const SplitK ws = split_k(a, p);
 #define PA_MFMA_LAUNCH(I8, BS)                                                                                   \
   hipLaunchKernelGGL((decode_mfma_kernel<I8, BS>), dim3((unsigned)items), dim3(64), 0, st, (float*)a->out, ws,  \
-                     (const unsigned short*)a->q, (const char*)a->k_cache, (const char*)a->v_cache,      \
+                     (const unsigned short*)a->q, (char*)a->k_cache, (char*)a->v_cache,      \
                      a->k_scales, a->v_scales, a->block_tables, a->max_blocks_per_seq, a->context_lens,        \
                      a->num_q_heads, a->num_kv_heads, p.G, a->num_blocks, qk, p.partition_tokens,              \
-                     p.num_partitions)
+                     p.num_partitions, (const char*)a->new_key, (const char*)a->new_value)
   const bool i8 = a->kv_dtype == PA_I8;
   if (i8) {
     if (a->block_size == 16) PA_MFMA_LAUNCH(true, 16); else PA_MFMA_LAUNCH(true, 32);
@@ -746,10 +819,10 @@ static void valu_dispatch_g(const pa_decode_args* a, const DecodePlan& p, hipStr
                             const SplitK& ws, float qk) {
 #define PA_VALU_LAUNCH(GT)                                                                                    \
   hipLaunchKernelGGL((decode_valu_kernel<QT, KV, D, BS, GT>), dim3(items), dim3(64), 0, st, (float*)a->out,  \
-                     ws, (const QT*)a->q, (const char*)a->k_cache, (const char*)a->v_cache, a->k_scales, \
+                     ws, (const QT*)a->q, (char*)a->k_cache, (char*)a->v_cache, a->k_scales, \
                      a->v_scales, a->block_tables, a->max_blocks_per_seq, a->context_lens, a->num_q_heads,   \
                      a->num_kv_heads, p.G, p.head_groups, a->num_blocks, qk, p.partition_tokens,             \
-                     p.num_partitions)
+                     p.num_partitions, (const char*)a->new_key, (const char*)a->new_value)
   switch (p.heads_per_wave) {
     case 1: PA_VALU_LAUNCH(1); break;
     case 2: PA_VALU_LAUNCH(2); break;

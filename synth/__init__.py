@@ -342,3 +342,14 @@ def config5() -> DecodeCase:
     seed2 = int(rng.integers(0, 2**31))
     return make_case(CONFIG_NAMES[5], seed2, cl, 32, 8, 128, 16, q_dtype=BF16, kv_dtype=I8,
                      poison=False)
+
+
+def random_int8_cache(case: DecodeCase, seed: int = 0) -> None:
+    """Fill an int8 case with random codes in [-127, 127] and positive fp32
+    scales (timing inputs; parity tests quantise fp32 samples instead)."""
+    rng = np.random.default_rng(seed)
+    shape = case.k_cache.shape
+    case.k_cache = rng.integers(-127, 128, shape).astype(np.int8)
+    case.v_cache = rng.integers(-127, 128, shape).astype(np.int8)
+    case.k_scales = (rng.random((case.num_blocks, case.num_kv_heads)) * 0.03 + 0.005).astype(np.float32)
+    case.v_scales = (rng.random((case.num_blocks, case.num_kv_heads)) * 0.03 + 0.005).astype(np.float32)

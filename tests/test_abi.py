@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
     assert len(names) >= 16, names
     for n in names:
         assert hasattr(lib, n), "libpa.so does not export %s" % n
-    assert lib.pa_abi_version() == 1
+    assert lib.pa_abi_version() == 2
 
 
 def test_status_strings():
@@ -117,6 +117,16 @@ def test_decode_rejects_null_alignment_and_workspace_before_launch():
     assert lib.pa_decode(ctypes.byref(a)) == pa.PA_ERR_INVALID
     assert "workspace" in lib.pa_last_error().decode()
     a = _cpu_args(kernel=2, q_dtype=pa.PA_F32)
+    assert lib.pa_decode(ctypes.byref(a)) == pa.PA_ERR_UNSUPPORTED
+
+
+def test_fused_write_argument_checks():
+    lib = pa.library()
+    a = _cpu_args(new_key=0x20000)                      # new_value missing
+    assert lib.pa_decode(ctypes.byref(a)) == pa.PA_ERR_INVALID
+    a = _cpu_args(new_key=0x20000, new_value=0x20008)   # misaligned
+    assert lib.pa_decode(ctypes.byref(a)) == pa.PA_ERR_INVALID
+    a = _cpu_args(new_key=0x20000, new_value=0x30000, kv_dtype=pa.PA_I8, k_scales=64, v_scales=64)
     assert lib.pa_decode(ctypes.byref(a)) == pa.PA_ERR_UNSUPPORTED
 
 

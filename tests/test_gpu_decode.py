@@ -338,3 +338,63 @@ def test_graph_replay_matches_eager():
             f()
         torch.cuda.synchronize()
         assert torch.equal(out, ref), i
+
+
+# --------------------------------------------------------------------------
+# fused cache write (new_key / new_value)
+# --------------------------------------------------------------------------
+
+FUSED_SHAPES = [
+    (64, 8, 128, 16, synth.BF16, synth.BF16),
+    (32, 8, 128, 32, synth.BF16, synth.BF16),
+    (40, 40, 128, 16, synth.BF16, synth.BF16),
+    (16, 16, 64, 16, synth.BF16, synth.BF16),
+    (8, 8, 64, 16, synth.F32, synth.F32),
+    (8, 2, 64, 32, synth.F32, synth.F32),
+]
+
+
+@pytest.mark.parametrize("shape", FUSED_SHAPES, ids=lambda s: "Hq%d-Hkv%d-D%d-BS%d-%s-%s" % s)
+def test_fused_cache_write(shape):
+    """pa_decode with new_key/new_value == slot mapping + reshape_and_cache +
+    pa_decode: caches bit-identical (and equal to the oracle's write),
+    outputs bit-identical, and within tolerance of the oracle."""
+    Hq, Hkv, D, BS, qd, kvd = shape
+    lens = [0, 1, 16, 17, 31, 32, 33, 500, 1000, 2049]
+    case = synth.make_case("fused", 200 + FUSED_SHAPES.index(shape), lens, Hq, Hkv, D, BS, q_dtype=qd,
+                           kv_dtype=kvd, free_frac=0.1)
+    rng = np.random.default_rng(7)
+    nk = rng.standard_normal((len(lens), Hkv, D), dtype=np.float32)
+    nv = rng.standard_normal((len(lens), Hkv, D), dtype=np.float32)
+    if kvd == synth.BF16:
+        nk, nv = synth.bf16_bits(nk), synth.bf16_bits(nv)
+    # oracle: write the newest tokens, then attend
+    slots = oracle.slot_mapping(case.block_tables, case.context_lens - 1, BS)
+    exp_k, exp_v = case.k_cache.copy(), case.v_cache.copy()
+    oracle.reshape_and_cache(nk, nv, exp_k, exp_v, slots)
+    updated = synth.make_case("fused", 200 + FUSED_SHAPES.index(shape), lens, Hq, Hkv, D, BS, q_dtype=qd,
+                              kv_dtype=kvd, free_frac=0.1)
+    updated.k_cache, updated.v_cache = exp_k, exp_v
+    expect = run_oracle(updated)
+    dnk, dnv = to_dev(nk), to_dev(nv)
+    for kern in _kernels(case):
+        for P in (0, 16, 256):
+            say("fused write", shape, "kernel", kern, "partition", P)
+            a = case_on_device(case)
+            sl = pa.slot_mapping(a["bt"], BS, context_lens=a["cl"])
+            pa.reshape_and_cache(dnk, dnv, a["k"], a["v"], sl)
+            out_a = pa.decode(a["q"], a["k"], a["v"], a["bt"], a["cl"], float(case.scale), case.max_context_len,
+                              partition_tokens=P, kernel=kern)
+            b = case_on_device(case)
+            out_b = pa.decode(b["q"], b["k"], b["v"], b["bt"], b["cl"], float(case.scale), case.max_context_len,
+                              partition_tokens=P, kernel=kern, new_key=dnk, new_value=dnv)
+            torch.cuda.synchronize()
+            kb, vb = to_host(b["k"]), to_host(b["v"])
+            assert np.array_equal(kb.view(np.uint8), exp_k.view(np.uint8))
+            assert np.array_equal(vb.view(np.uint8), exp_v.view(np.uint8))
+            assert np.array_equal(to_host(a["k"]).view(np.uint8), kb.view(np.uint8))
+            oa = out_a.cpu().numpy().astype(np.float64)
+            ob = out_b.cpu().numpy().astype(np.float64)
+            assert np.array_equal(oa, ob), (kern, P)
+            err = max_err(ob, expect)
+            assert err <= tolerance(case), (kern, P, err)
