@@ -133,7 +133,8 @@ def run(args) -> dict:
                                                                      stream=stream)]
             d = pa.PreparedDecode(Q[layer], K[layer], V[layer], bt, cl, scale, ctx, outs[layer], workspace=ws,
                                   stream=stream, new_key=KN[layer] if fused else None,
-                                  new_value=VN[layer] if fused else None, partition_tokens=args.partition_tokens)
+                                  new_value=VN[layer] if fused else None, partition_tokens=args.partition_tokens,
+                                  total_context_len=int(st["context_lens"].sum()))
             layers.append((writes, d))
         return pre, layers
 
@@ -322,7 +323,8 @@ def run_single_layer(args) -> dict:
                 calls.append(pa.prepare_copy_blocks(K[r], V[r], pairs, stream=stream))
             calls.append(pa.PreparedDecode(q, K[r], V[r], bt, cl, float(case.scale), mcl, outs[r], k_scales=ks,
                                            v_scales=vs, workspace=ws, stream=stream, new_key=newk, new_value=newv,
-                                           partition_tokens=args.partition_tokens))
+                                           partition_tokens=args.partition_tokens, kernel=args.kernel,
+                                           total_context_len=int(np.sum(case.context_lens, dtype=np.int64))))
         return calls
 
     main = torch.cuda.current_stream()
@@ -354,7 +356,8 @@ def run_single_layer(args) -> dict:
     cls = case.context_lens
     kvb = kv_bytes(cls, Hkv, D, e)
     alg = decode_algorithmic_bytes(cls, Hq, Hkv, D, BS, e, eq, int8_scales=(w == "int8"))
-    res = {"workload": w, "description": WORKLOADS[w], "replicas": R, "partition_tokens": args.partition_tokens, "steps": args.steps, "warmup": args.warmup,
+    res = {"workload": w, "description": WORKLOADS[w], "replicas": R, "partition_tokens": args.partition_tokens,
+           "kernel": args.kernel, "steps": args.steps, "warmup": args.warmup,
            "ms_per_layer": round(ms_layer, 5), "tokens_per_s": round(S / (ms_layer * 1e-3), 1),
            "kv_gbs": round(kvb / (ms_layer * 1e-3) / 1e9, 1),
            "pct_hbm_peak": round(100.0 * alg / (ms_layer * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
@@ -450,6 +453,8 @@ def main():
     ap.add_argument("--copy-pairs", type=int, default=4096)
     ap.add_argument("--partition-tokens", type=int, default=0,
                     help="override the library's automatic split-K partition length (tuning only)")
+    ap.add_argument("--kernel", type=int, default=0, choices=[0, 1, 2],
+                    help="decode kernel of the one-layer workloads: 0 library's choice, 1 vector-ALU, 2 matrix-core")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="llama3-70b",
                     help="the 70B-shaped 80-layer step (default; the JSON metric line) or one of the single-layer "
                          "workloads, reported as a per-layer record")

@@ -61,7 +61,7 @@ const char* pa_status_string(pa_status s);
 /* Message of the last failure on the calling thread ("" if none). */
 const char* pa_last_error(void);
 /* ABI version of this header (incremented on any incompatible change). */
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 int32_t pa_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -101,7 +101,14 @@ int32_t pa_abi_version(void);
  *
  * Long contexts are split into partitions of `partition_tokens` tokens
  * (0 = chosen by the library), each computed by its own wave and merged by
- * a second kernel in partition order.  The merge needs `workspace` of at
+ * a second kernel in partition order.  The library's choice uses
+ * max_context_len and, when given, `total_context_len` (the sum of
+ * context_lens over the batch, known to the caller that built the tables):
+ * a batch whose lengths are close to the maximum is cut into a few long
+ * partitions per sequence; a ragged one into many short ones, so that no
+ * wave is left with a long sequence at the end.  The hint shapes only the
+ * split (and so the workspace size), never the result; 0 means unknown
+ * (every sequence taken at max_context_len).  The merge needs `workspace` of at
  * least the size pa_decode_workspace_size reports for the same arguments
  * (NULL is fine when that size is 0).  The workspace is scratch of the
  * call: its contents are not needed before or after it.  Calls that may
@@ -118,7 +125,7 @@ int32_t pa_abi_version(void);
  *
  * `kernel` selects the implementation: 0 = automatic, 1 = vector-ALU
  * kernel (any supported case), 2 = matrix-core kernel (bf16 or int8
- * caches with bf16 queries, head_dim 128, 2..16 query heads per kv head;
+ * caches with bf16 queries, head_dim 128, 1..16 query heads per kv head;
  * else PA_ERR_UNSUPPORTED).  Both compute the definition above; they
  * differ in rounding only.
  */
@@ -151,6 +158,7 @@ typedef struct {
   void* stream;                  /* hipStream_t */
   const void* new_key;           /* optional fused cache write: both or neither */
   const void* new_value;
+  int64_t total_context_len;     /* optional hint: sum of context_lens (0 = unknown), 0 <= it <= num_seqs * max_context_len */
 } pa_decode_args;
 
 /* Host only: bytes of workspace pa_decode needs for these arguments

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_OOM, PA_ERR_STATE, PA_ERR_HIP = range(6)
 PA_F32, PA_BF16, PA_I8 = 0, 1, 2
 KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_OOM",
                 4: "PA_ERR_STATE", 5: "PA_ERR_HIP"}
@@ -65,6 +65,7 @@ class DecodeArgs(ctypes.Structure):
         ("stream", ctypes.c_void_p),
         ("new_key", ctypes.c_void_p),
         ("new_value", ctypes.c_void_p),
+        ("total_context_len", ctypes.c_int64),
     ]
 
 
@@ -163,11 +164,13 @@ def _stream(stream) -> int:
 def make_decode_args(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int,
                      out=None, k_scales=None, v_scales=None, workspace=None, partition_tokens: int = 0,
                      kernel: int = KERNEL_AUTO, stream=None, device_pointers: bool = True, new_key=None,
-                     new_value=None) -> DecodeArgs:
+                     new_value=None, total_context_len: int = 0) -> DecodeArgs:
     """Fill a DecodeArgs from tensors.  q ``[S][Hq][D]``; caches
     ``[NB][Hkv][BS][D]``; block_tables int32 ``[S][max_blocks]``;
     context_lens int32 ``[S]``; out float32 ``[S][Hq][D]``; optional
-    new_key/new_value ``[S][Hkv][D]`` for the fused cache write."""
+    new_key/new_value ``[S][Hkv][D]`` for the fused cache write;
+    total_context_len: optional sum of the context lengths (partition
+    hint, 0 = unknown)."""
     S, Hq, D = q.shape
     NB, Hkv, BS, D2 = k_cache.shape
     if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
@@ -206,6 +209,7 @@ def make_decode_args(q, k_cache, v_cache, block_tables, context_lens, scale: flo
             raise ValueError("%s must be [%d][%d][%d]" % (name, S, Hkv, D))
     a.new_key = get(new_key)
     a.new_value = get(new_value)
+    a.total_context_len = int(total_context_len)
     return a
 
 
@@ -217,22 +221,21 @@ def decode_workspace_size(args: DecodeArgs) -> int:
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int, out=None,
            k_scales=None, v_scales=None, workspace=None, partition_tokens: int = 0, kernel: int = KERNEL_AUTO,
-           stream=None, new_key=None, new_value=None):
+           stream=None, new_key=None, new_value=None, total_context_len: int = 0):
     """Paged decode attention (``pa_decode``).  Returns ``out`` (float32
-    ``[S][Hq][D]``), allocated on q's device when not given.  A zeroed
-    workspace is allocated when needed and none is passed; a caller-owned
-    workspace must be zero-filled before its first use (calls leave it
-    zeroed)."""
+    ``[S][Hq][D]``), allocated on q's device when not given.  A workspace
+    is allocated when the plan needs one and none is passed (its contents
+    are scratch of the call)."""
     torch = _torch()
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     args = make_decode_args(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, out=out,
                             k_scales=k_scales, v_scales=v_scales, workspace=workspace,
                             partition_tokens=partition_tokens, kernel=kernel, stream=stream, new_key=new_key,
-                            new_value=new_value)
+                            new_value=new_value, total_context_len=total_context_len)
     need = decode_workspace_size(args)
     if need and workspace is None:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         args.workspace = workspace.data_ptr()
         args.workspace_bytes = need
     _check(library().pa_decode(ctypes.byref(args)))
@@ -352,15 +355,15 @@ class PreparedDecode:
 
     def __init__(self, q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int, out,
                  k_scales=None, v_scales=None, workspace=None, partition_tokens: int = 0, kernel: int = KERNEL_AUTO,
-                 stream=None, new_key=None, new_value=None):
+                 stream=None, new_key=None, new_value=None, total_context_len: int = 0):
         torch = _torch()
         self.args = make_decode_args(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
                                      out=out, k_scales=k_scales, v_scales=v_scales, workspace=workspace,
                                      partition_tokens=partition_tokens, kernel=kernel, stream=stream,
-                                     new_key=new_key, new_value=new_value)
+                                     new_key=new_key, new_value=new_value, total_context_len=total_context_len)
         need = decode_workspace_size(self.args)
         if need and (workspace is None or self.args.workspace_bytes < need):
-            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
             self.args.workspace = workspace.data_ptr()
             self.args.workspace_bytes = need
         self.workspace_bytes = need

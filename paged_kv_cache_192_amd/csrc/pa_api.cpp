@@ -39,6 +39,17 @@ static int target_waves(KernelKind kind, pa_dtype kv) {
   return 1280;
 }
 
+// A ragged batch (mean length under 3/4 of the maximum) is cut into short
+// partitions instead: about 20 waves per CU, which the dispatcher hands
+// out as earlier ones finish, so the long sequences no longer set the
+// kernel's end.  Measured on one-layer batches with log-normal and uniform
+// lengths (int8 and bf16 caches): ~5,000 waves of <= 16 tiles beat both
+// fewer longer waves and more shorter ones.
+constexpr int64_t kRaggedWaves = 5120;
+static bool is_ragged(const pa_decode_args* a, int64_t total) {
+  return total * 4 < (int64_t)a->num_seqs * a->max_context_len * 3;
+}
+
 pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   if (!a) return fail(PA_ERR_INVALID, "pa_decode: args is NULL");
   if (a->struct_size != sizeof(pa_decode_args))
@@ -77,6 +88,10 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
     return fail(PA_ERR_INVALID, "pa_decode: partition_tokens %d is not a multiple of 16 in [0, %d*block_size]",
                 a->partition_tokens, kMaxPartitionBlocks);
   if (a->kernel < 0 || a->kernel > 2) return fail(PA_ERR_INVALID, "pa_decode: kernel %d not in {0, 1, 2}", a->kernel);
+  const int64_t seq_tokens = (int64_t)(a->num_seqs > 0 ? a->num_seqs : 0) * a->max_context_len;
+  if (a->total_context_len < 0 || a->total_context_len > seq_tokens)
+    return fail(PA_ERR_INVALID, "pa_decode: total_context_len %lld outside [0, num_seqs * max_context_len]",
+                (long long)a->total_context_len);
 
   const bool mfma_ok = a->q_dtype == PA_BF16 && (a->kv_dtype == PA_BF16 || a->kv_dtype == PA_I8) &&
                        a->head_dim == 128;
@@ -89,7 +104,7 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   } else if (a->kernel == KERNEL_VALU) {
     kind = KERNEL_VALU;
   } else {
-    kind = (mfma_ok && G >= 4) ? KERNEL_MFMA : KERNEL_VALU;
+    kind = mfma_ok ? KERNEL_MFMA : KERNEL_VALU;
   }
 
   p->kind = kind;
@@ -102,7 +117,23 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   const int64_t tiles = a->max_context_len > 0 ? (a->max_context_len + 15) / 16 : 1;
   const int64_t max_tiles = (int64_t)kMaxPartitionBlocks * a->block_size / 16;
   int P = a->partition_tokens;
-  if (P == 0) {
+  const int64_t total = a->total_context_len > 0 ? a->total_context_len : seq_tokens;
+  if (P == 0 && a->num_seqs > 0 && is_ragged(a, total)) {
+    // Waves of one (sequence, kv head, head group): about total/P + S/2
+    // partitions each; choose P for ~kRaggedWaves waves, at least 4 tiles,
+    // at most kMaxPartitionBlocks blocks, and at most kMaxRaggedPartitions
+    // partitions per sequence.
+    const int64_t per_seq = (int64_t)a->num_kv_heads * p->head_groups;
+    int64_t room = kRaggedWaves - per_seq * a->num_seqs / 2;
+    if (room < kRaggedWaves / 4) room = kRaggedWaves / 4;
+    int64_t per = (per_seq * total + 16 * room - 1) / (16 * room);  // tiles per partition
+    const int64_t min_per = (tiles + kMaxRaggedPartitions - 1) / kMaxRaggedPartitions;
+    if (per < min_per) per = min_per;
+    if (per < 4) per = 4;
+    if (per > max_tiles) per = max_tiles;
+    if (per > tiles) per = tiles;
+    P = (int)(16 * per);
+  } else if (P == 0) {
     // Split each sequence into nP equal partitions so the grid holds about
     // target_waves() waves, within [4 tiles, kMaxPartitionBlocks blocks] per
     // partition and at most kMaxAutoPartitions partitions.

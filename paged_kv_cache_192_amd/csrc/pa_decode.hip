@@ -181,10 +181,11 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(float* __restrict__ ou
 
 template <bool I8>
 struct MfmaTile {
-  // K: bf16 -> 4 x 16 B per lane, coalesced: instruction i reads rows
-  //    4i .. 4i+3, lane l the 16 B chunk l%16 of row 4i + l/16 (staged
-  //    through LDS into the MFMA layout);
-  //    int8 -> 2 x 16 B per lane (row l%16, d = 32*(l/16) .. +31).
+  // K, coalesced and staged through LDS into the MFMA layout:
+  //    bf16 -> 4 x 16 B per lane: instruction i reads rows 4i .. 4i+3, lane
+  //    l the 16 B chunk l%16 of row 4i + l/16;
+  //    int8 -> 2 x 16 B per lane: instruction i reads rows 8i .. 8i+7, lane
+  //    l the 16 B chunk l%8 of row 8i + l/8.
   u32x4_t k[I8 ? 2 : 4];
   // V: rows 4*(l/16) + i, d = 8*(l%16) .. +7: bf16 -> 16 B per row, int8 -> 8 B.
   u32x4_t v[4];
@@ -214,8 +215,8 @@ __device__ __forceinline__ void mfma_load_tile(MfmaTile<I8>& T, const char* kbas
   constexpr int TILE = 16 * (I8 ? 128 : 256);  // bytes of 16 token rows
   const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase, TILE), rv = tile_rsrc(vbase, TILE);
   if (I8) {
-    T.k[0] = bld16(rk, koff[0]);
-    T.k[1] = bld16(rk, koff[1]);
+    T.k[0] = bld16(rk, koff[0]);  // rows 0..7
+    T.k[1] = bld16(rk, koff[1]);  // rows 8..15
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) T.k[i] = bld16(rk, koff[i]);
@@ -344,21 +345,30 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     nk = *(const u32x4_t*)(new_k + src);
     nv = *(const u32x4_t*)(new_v + src);
   }
-  // bf16 K goes through a per-wave LDS tile of 16 rows x 16 chunks of 16 B;
-  // chunk ch of row r sits at position ch ^ r, so both the row-wise writes
-  // and the MFMA-layout reads (16 rows, one chunk each) hit distinct banks.
-  __shared__ u32x4_t ktile[I8 ? 1 : 256];
+  // K goes through a per-wave LDS tile of 16 rows of 16 B chunks (16 per
+  // row for bf16, 8 for int8).  Chunk ch of row r sits at position
+  // ch ^ (r mod chunks-per-row), so the row-wise writes and the MFMA-layout
+  // reads (16 rows, one chunk each) spread over the banks.
+  constexpr int CPR = ROW / 16;  // 16 B chunks per row
+  __shared__ u32x4_t ktile[16 * CPR];
   unsigned koff[4], voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    koff[i] = I8 ? c * ROW + j * 32 + 16 * (i & 1) : lane * 16 + i * 1024;
+    koff[i] = lane * 16 + i * 1024;
     voff[i] = (4 * j + i) * ROW + c * 8 * E;
   }
   int kw[4], kr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    kw[i] = (4 * i + j) * 16 + (c ^ (4 * i + j));  // write slot of load i
-    kr[i] = c * 16 + ((i * 4 + j) ^ c);            // read slot of d-chunk (i*4 + j), row c
+    if (I8) {
+      const int r = 8 * (i & 1) + (lane >> 3), ch = lane & 7;  // load i (< 2) of this lane
+      kw[i] = r * 8 + (ch ^ (r & 7));
+      const int rc = 2 * j + (i & 1);                          // read: row c, chunk 2j + (i & 1)
+      kr[i] = c * 8 + (rc ^ (c & 7));
+    } else {
+      kw[i] = (4 * i + j) * 16 + (c ^ (4 * i + j));  // write slot of load i
+      kr[i] = c * 16 + ((i * 4 + j) ^ c);            // read slot of d-chunk (i*4 + j), row c
+    }
   }
   auto tile_ptrs = [&](int ti, const char*& kb, const char*& vb, bool& ok, float& ks, float& vs) {
     const int e = (ti * 16) / BS - tbl_base;
@@ -382,7 +392,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   auto compute = [&](MfmaTile<I8>& T, int ti, bool ok, float ks, float vs) {
     const bool new_tile = owns_new && ti == (tnew >> 4);  // wave-uniform
     const int rnew = tnew & 15;
-    if (!I8) {
+    if (I8) {
+      ktile[kw[0]] = T.k[0];
+      ktile[kw[1]] = T.k[1];
+    } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) ktile[kw[i]] = T.k[i];
       if (new_tile) {
@@ -398,7 +411,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     for (int kk = 0; kk < 4; ++kk) {
       bf16x8_t a;
       if (I8) {
-        const unsigned w0 = T.k[kk >> 1][(kk & 1) * 2], w1 = T.k[kk >> 1][(kk & 1) * 2 + 1];
+        // lane holds d = 32j .. 32j+31 of row c: chunk 2j (kk 0, 1), 2j+1 (kk 2, 3)
+        const u32x4_t chunk = ktile[kr[kk >> 1]];
+        const unsigned w0 = chunk[(kk & 1) * 2], w1 = chunk[(kk & 1) * 2 + 1];
         const u32x2_t lo = i8x4_to_bf16x4(w0), hi = i8x4_to_bf16x4(w1);
         a = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
       } else {

@@ -31,9 +31,12 @@ enum KernelKind { KERNEL_VALU = 1, KERNEL_MFMA = 2 };
 // Longest partition, in blocks: the matrix-core kernel keeps a partition's
 // table entries in two registers of 64 lanes.
 constexpr int kMaxPartitionBlocks = 128;
-// Most partitions the automatic plan splits one sequence into (the last
-// wave of each (sequence, kv head) merges them all).
+// Most partitions the automatic plan splits one sequence into: for a batch
+// of near-equal lengths, and for a ragged batch (where it bounds the
+// workspace, which holds max_context_len / partition_tokens partials per
+// row).
 constexpr int kMaxAutoPartitions = 32;
+constexpr int kMaxRaggedPartitions = 512;
 
 // Everything the launchers need, derived on the host from pa_decode_args.
 struct DecodePlan {

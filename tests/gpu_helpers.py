@@ -59,11 +59,15 @@ def quantize_case(case: synth.DecodeCase) -> None:
     synth.poison_unused(case.v_cache, case.block_tables, case.context_lens, case.free_blocks, synth.I8)
 
 
-def run_decode(case: synth.DecodeCase, dev=None, partition_tokens=0, kernel=0, max_context_len=None):
+def run_decode(case: synth.DecodeCase, dev=None, partition_tokens=0, kernel=0, max_context_len=None,
+               length_hint=False):
+    """pa_decode on the case; length_hint passes the batch's total context
+    length (the ragged-batch partition plan)."""
     d = dev or case_on_device(case)
     mcl = case.max_context_len if max_context_len is None else max_context_len
+    total = int(np.sum(case.context_lens, dtype=np.int64)) if length_hint else 0
     out = pa.decode(d["q"], d["k"], d["v"], d["bt"], d["cl"], float(case.scale), mcl, k_scales=d["ks"],
-                    v_scales=d["vs"], partition_tokens=partition_tokens, kernel=kernel)
+                    v_scales=d["vs"], partition_tokens=partition_tokens, kernel=kernel, total_context_len=total)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64)
 

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
     assert len(names) >= 16, names
     for n in names:
         assert hasattr(lib, n), "libpa.so does not export %s" % n
-    assert lib.pa_abi_version() == 2
+    assert lib.pa_abi_version() == pa.ABI_VERSION == 3
 
 
 def test_status_strings():
@@ -77,6 +77,28 @@ def test_struct_layout_and_workspace_size():
     assert st == pa.PA_ERR_INVALID and "block_size 24" in pa.library().pa_last_error().decode()
 
 
+def test_partition_plan_follows_the_length_hint():
+    """Near-equal lengths (hint absent or close to num_seqs * max): a few
+    long partitions per sequence; a ragged batch: short ones, here the
+    4-tile minimum, up to 512 per sequence."""
+    al = lambda b: (b + 255) // 256 * 256  # noqa: E731
+
+    def ws_for(nP):
+        rows = 3 * 8 * nP
+        return al(rows * 8) + al(rows * 128 * 4)
+
+    big = dict(max_blocks_per_seq=2048, num_blocks=6144, max_context_len=32768)
+    for hint in (0, 3 * 32768, 3 * 32768 - 1000):
+        st, n = _ws(_cpu_args(total_context_len=hint, **big))
+        assert st == pa.PA_OK
+        assert n == ws_for(32)                          # 1024-token partitions
+    st, n = _ws(_cpu_args(total_context_len=40000, **big))
+    assert st == pa.PA_OK and n == ws_for(512)          # 64-token partitions
+    # an explicit partition size ignores the hint
+    st, n = _ws(_cpu_args(total_context_len=40000, partition_tokens=2048, **big))
+    assert st == pa.PA_OK and n == ws_for(16)
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("struct_size", 8, pa.PA_ERR_INVALID),
     ("num_q_heads", 7, pa.PA_ERR_INVALID),            # not a multiple of 2 kv heads
@@ -97,6 +119,8 @@ def test_struct_layout_and_workspace_size():
     ("partition_tokens", 2064, pa.PA_ERR_INVALID),    # > 128 blocks
     ("kernel", 3, pa.PA_ERR_INVALID),
     ("num_seqs", -1, pa.PA_ERR_INVALID),
+    ("total_context_len", -1, pa.PA_ERR_INVALID),
+    ("total_context_len", 301, pa.PA_ERR_INVALID),    # > 3 seqs x 100
 ])
 def test_decode_rejects_bad_arguments(field, value, status):
     a = _cpu_args(**{field: value})

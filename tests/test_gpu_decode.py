@@ -33,10 +33,12 @@ def _check_all_kernels(case, partitions=(0,), expect=None):
     tol = tolerance(case)
     for kern in _kernels(case):
         for P in partitions:
-            say(case.name, "kernel", kern, "partition", P)
-            got = run_decode(case, dev, partition_tokens=P, kernel=kern)
-            err = max_err(got, expect)
-            assert err <= tol, (case.name, kern, P, err)
+            # the library's own split is taken with and without the length hint
+            for hint in ((False, True) if P == 0 else (False,)):
+                say(case.name, "kernel", kern, "partition", P, "hint", hint)
+                got = run_decode(case, dev, partition_tokens=P, kernel=kern, length_hint=hint)
+                err = max_err(got, expect)
+                assert err <= tol, (case.name, kern, P, hint, err)
     return expect
 
 
