@@ -83,6 +83,40 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
+# HBM bytes of one pa_decode call on the 70B-shaped layer (decode + merge
+# kernels, fused cache write), from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE runs: FETCH_SIZE scaled by 1.99221 and WRITE_SIZE by 1.0, the
+# ratios of a plain copy's known bytes to what the same counters read for it
+# (profiles/decode_mfma_llama3-70b_pmc_traffic.md).  Valid only for the
+# sources the counters were taken on: a changed kernel or plan reports null.
+PMC_TRAFFIC = {
+    "sources_sha256": "7163aa97ff9ea20d6fe40c957531b62d40540c38230316e6f89cbc8fdc7838d1",
+    "fetch_kib": 321000.2 + 1391.0,
+    "write_kib": 2680.0 + 640.0,
+    "fetch_factor": 1.99221,
+    "write_factor": 1.0,
+}
+PMC_SOURCES = ("paged_kv_cache_192_amd/csrc/pa_decode.hip", "paged_kv_cache_192_amd/csrc/pa_api.cpp",
+               "paged_kv_cache_192_amd/csrc/pa_internal.h")
+
+
+def sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for rel in PMC_SOURCES:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(fused: bool):
+    t = PMC_TRAFFIC
+    if not fused or t["sources_sha256"] != sources_sha256():
+        return None
+    return int(round((t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"]) * 1024))
+
+
 def run(args) -> dict:
     import numpy as np
     import torch
@@ -209,7 +243,10 @@ def run(args) -> dict:
         torch.cuda.synchronize()
         launch_ms += [a.elapsed_time(b) for a, b in evs]
     launch_ms = sorted(launch_ms)
-    launch_avg = sum(launch_ms) / len(launch_ms)
+    # average launch duration of pa_decode: with the write fused, the timed
+    # region holds exactly steps x L decode calls and nothing else; else the
+    # events around each eager call
+    launch_avg = ms_per_step / L if fused else sum(launch_ms) / len(launch_ms)
     if not torch.equal(torch.stack(outs), ref):
         raise RuntimeError("timed steps changed the result")
 
@@ -239,10 +276,13 @@ def run(args) -> dict:
         "kv_bytes_per_step": kv_step,
         "wall_s_timed_region": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(fused),
                      "kernel": "pa_decode = decode_mfma_kernel + decode_merge_kernel", "launch_ms_avg": round(launch_avg, 5),
-                     "launch_ms_p10": round(launch_ms[len(launch_ms) // 10], 5),
-                     "launch_ms_p90": round(launch_ms[(9 * len(launch_ms)) // 10], 5),
+                     "launch_ms_source": ("timed region / (steps x layers)" if fused else
+                                          "events around each eager call"),
+                     "eager_call_ms_p10": round(launch_ms[len(launch_ms) // 10], 5),
+                     "eager_call_ms_p50": round(launch_ms[len(launch_ms) // 2], 5),
+                     "eager_call_ms_p90": round(launch_ms[(9 * len(launch_ms)) // 10], 5),
                      "algorithmic_bytes_per_launch": alg_launch, "workspace_bytes": ws_bytes},
         "waste": waste_report(cls, BS, 8192),
         "step_mode": ("hip graph replay" if graph is not None else "eager prepared calls") +

@@ -52,33 +52,34 @@ __global__ void reshape_and_cache_kernel(const uint4* __restrict__ key, const ui
 }
 
 // Grid: x = chunk group inside a block, y = pair, z = 0 (K) or 1 (V).
-// Each thread copies up to kCopyUnroll 16-byte chunks of one physical
-// block; the first thread of each (pair, K/V) also copies that block's
-// per-head scales when present.
+// Each thread copies kCopyUnroll 16-byte chunks of one physical block, all
+// loads issued before the first store (a group that reaches past the
+// block's end takes a guarded path); the first threads of each (pair, K/V)
+// also copy that block's per-head scales when present.
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;
 
-__global__ void copy_blocks_kernel(uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
-                                   float* __restrict__ k_scales, float* __restrict__ v_scales,
-                                   const int64_t* __restrict__ pairs, int64_t block_chunks, int32_t Hkv,
-                                   int64_t num_blocks) {
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
+    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, float* __restrict__ k_scales,
+    float* __restrict__ v_scales, const int64_t* __restrict__ pairs, int64_t block_chunks, int32_t Hkv,
+    int64_t num_blocks) {
   const int p = blockIdx.y;
   const int64_t src = pairs[2 * p], dst = pairs[2 * p + 1];
   if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
   uint4* cache = blockIdx.z ? v_cache : k_cache;
   const uint4* from = cache + src * block_chunks;
   uint4* to = cache + dst * block_chunks;
-  const int64_t base = (int64_t)blockIdx.x * kCopyThreads * kCopyUnroll + threadIdx.x;
-  uint4 v[kCopyUnroll];
-#pragma unroll
-  for (int u = 0; u < kCopyUnroll; ++u) {
-    const int64_t c = base + (int64_t)u * kCopyThreads;
-    if (c < block_chunks) v[u] = from[c];
-  }
-#pragma unroll
-  for (int u = 0; u < kCopyUnroll; ++u) {
-    const int64_t c = base + (int64_t)u * kCopyThreads;
-    if (c < block_chunks) to[c] = v[u];
+  const int64_t group = (int64_t)blockIdx.x * kCopyThreads * kCopyUnroll;
+  const int64_t base = group + threadIdx.x;
+  if (group + kCopyThreads * kCopyUnroll <= block_chunks) {
+    const uint4 a = from[base], b = from[base + kCopyThreads];
+    const uint4 c = from[base + 2 * kCopyThreads], d = from[base + 3 * kCopyThreads];
+    to[base] = a;
+    to[base + kCopyThreads] = b;
+    to[base + 2 * kCopyThreads] = c;
+    to[base + 3 * kCopyThreads] = d;
+  } else {
+    for (int64_t i = base; i < block_chunks; i += kCopyThreads) to[i] = from[i];
   }
   float* scales = blockIdx.z ? v_scales : k_scales;
   if (scales && blockIdx.x == 0 && threadIdx.x < Hkv) scales[dst * Hkv + threadIdx.x] = scales[src * Hkv + threadIdx.x];

@@ -107,18 +107,23 @@ struct SplitK {
   float* acc;     // [S][Hq][nP][D]: unnormalised weighted sum of values
 };
 
-// One wave per output row (s, h): out = sum_p 2^(m_p - M) acc_p / sum_p
-// 2^(m_p - M) l_p over the np partitions that hold tokens, in partition
-// order.  Partitions are read sixteen at a time, all loads of a group
-// issued together (one memory round trip per group); groups after the
-// first rescale the running sums to the new maximum.
-template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(float* __restrict__ out, SplitK ws,
-                                                          const int32_t* __restrict__ context_lens, int Hq, int P,
-                                                          int nP, int max_tokens) {
+// One workgroup of W waves per output row (s, h): out = sum_p 2^(m_p - M)
+// acc_p / sum_p 2^(m_p - M) l_p over the np partitions that hold tokens, in
+// partition order.  Partitions are read sixteen at a time, all loads of a
+// group issued together (one memory round trip per group); wave w takes
+// groups w, w + W, ...; groups after a wave's first rescale its running
+// sums to the new maximum.  With W > 1 the waves' (m, L, acc) are combined
+// through LDS the same way, in wave order.  W = 1 when every row has at
+// most 16 partitions; long ragged rows get W = 4 so their merge takes a
+// quarter of the round trips.
+template <int D, int W>
+__global__ __launch_bounds__(64 * W) void decode_merge_kernel(float* __restrict__ out, SplitK ws,
+                                                              const int32_t* __restrict__ context_lens, int Hq,
+                                                              int P, int nP, int max_tokens) {
   constexpr int PER = D / 64;
   constexpr int GRP = 16;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const size_t row = blockIdx.x;
   const int n = min(context_lens[row / Hq], max_tokens);
   const int np = n > 0 ? min(nP, (n + P - 1) / P) : 0;
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(float* __restrict__ ou
   float m_run = kNegInf, L = 0.f, a[PER];
 #pragma unroll
   for (int q = 0; q < PER; ++q) a[q] = 0.f;
-  for (int p0 = 0; p0 < np; p0 += GRP) {
+  for (int p0 = GRP * wave; p0 < np; p0 += GRP * W) {
     const int cnt = min(GRP, np - p0);
     float part[GRP][PER];
     const float* src = ws.acc + (r + p0) * D + lane;
@@ -152,6 +157,34 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(float* __restrict__ ou
       const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
 #pragma unroll
       for (int q = 0; q < PER; ++q) a[q] = fmaf(wk, part[k][q], a[q]);
+    }
+  }
+  if constexpr (W > 1) {
+    __shared__ float s_ml[W][2];
+    __shared__ float s_a[W][D];
+    if (lane == 0) {
+      s_ml[wave][0] = m_run;
+      s_ml[wave][1] = L;
+    }
+#pragma unroll
+    for (int q = 0; q < PER; ++q) s_a[wave][lane + 64 * q] = a[q];
+    __syncthreads();
+    if (wave != 0) return;
+    float M = kNegInf;
+#pragma unroll
+    for (int u = 0; u < W; ++u) M = fmaxf(M, s_ml[u][0]);
+    L = 0.f;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) a[q] = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int u = 0; u < W; ++u) {
+        const float mu = s_ml[u][0];
+        const float f = mu == kNegInf ? 0.f : fast_exp2(mu - M);
+        L += f * s_ml[u][1];
+#pragma unroll
+        for (int q = 0; q < PER; ++q) a[q] = fmaf(f, s_a[u][lane + 64 * q], a[q]);
+      }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -880,16 +913,24 @@ pa_status launch_decode_valu(const pa_decode_args* a, const DecodePlan& p, hipSt
   return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode (vector-ALU kernel) launch");
 }
 
+template <int D>
+static void merge_dispatch(const pa_decode_args* a, const DecodePlan& p, hipStream_t st, unsigned rows,
+                           const SplitK& ws, int max_tokens) {
+#define PA_MERGE_LAUNCH(W)                                                                                  \
+  hipLaunchKernelGGL((decode_merge_kernel<D, W>), dim3(rows), dim3(64 * W), 0, st, (float*)a->out, ws,       \
+                     a->context_lens, a->num_q_heads, p.partition_tokens, p.num_partitions, max_tokens)
+  if (p.num_partitions <= 16) PA_MERGE_LAUNCH(1);
+  else if (p.num_partitions <= 32) PA_MERGE_LAUNCH(2);
+  else PA_MERGE_LAUNCH(4);
+#undef PA_MERGE_LAUNCH
+}
+
 pa_status launch_decode_merge(const pa_decode_args* a, const DecodePlan& p, hipStream_t st) {
   const size_t rows = (size_t)a->num_seqs * a->num_q_heads;
   const SplitK ws = split_k(a, p);
   const int max_tokens = a->max_blocks_per_seq * a->block_size;
-  if (a->head_dim == 64)
-    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3((unsigned)rows), dim3(64), 0, st, (float*)a->out, ws,
-                       a->context_lens, a->num_q_heads, p.partition_tokens, p.num_partitions, max_tokens);
-  else
-    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3((unsigned)rows), dim3(64), 0, st, (float*)a->out, ws,
-                       a->context_lens, a->num_q_heads, p.partition_tokens, p.num_partitions, max_tokens);
+  if (a->head_dim == 64) merge_dispatch<64>(a, p, st, (unsigned)rows, ws, max_tokens);
+  else merge_dispatch<128>(a, p, st, (unsigned)rows, ws, max_tokens);
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode (merge kernel) launch");
 }

@@ -154,7 +154,7 @@ def test_edge_lengths_all_kernels(shape):
     case = synth.make_case("edge", seed, EDGE_LENS, Hq, Hkv, D, BS, q_dtype=qd, kv_dtype=kvd, free_frac=0.2)
     if kvd == synth.I8:
         quantize_case(case)
-    _check_all_kernels(case, partitions=(0, 16, 256, 1024))
+    _check_all_kernels(case, partitions=(0, 16, 48, 256, 1024))
 
 
 def test_closed_forms_on_gpu(golden):
