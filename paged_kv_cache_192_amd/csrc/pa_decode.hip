@@ -108,8 +108,11 @@ struct SplitK {
 };
 
 // One workgroup of W waves per output row (s, h): out = sum_p 2^(m_p - M)
-// acc_p / sum_p 2^(m_p - M) l_p over the np partitions that hold tokens, in
-// partition order.  Partitions are read sixteen at a time, all loads of a
+// acc_p / sum_p 2^(m_p - M) l_p over the partitions that hold tokens, in
+// partition order.  Every partition of the grid leaves its (m, l), empty
+// ones (-inf, 0), so with W = 1 the row's nP partials are read without
+// first reading its length; with W > 1 (long ragged rows, most partitions
+// empty) only the ceil(n / P) that hold tokens are read.  Partitions are read sixteen at a time, all loads of a
 // group issued together (one memory round trip per group); wave w takes
 // groups w, w + W, ...; groups after a wave's first rescale its running
 // sums to the new maximum.  With W > 1 the waves' (m, L, acc) are combined
@@ -125,8 +128,11 @@ __global__ __launch_bounds__(64 * W) void decode_merge_kernel(float* __restrict_
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const size_t row = blockIdx.x;
-  const int n = min(context_lens[row / Hq], max_tokens);
-  const int np = n > 0 ? min(nP, (n + P - 1) / P) : 0;
+  int np = nP;
+  if (W > 1) {
+    const int n = min(context_lens[row / Hq], max_tokens);
+    np = n > 0 ? min(nP, (n + P - 1) / P) : 0;
+  }
   const size_t r = row * (size_t)nP;
   float m_run = kNegInf, L = 0.f, a[PER];
 #pragma unroll
@@ -154,9 +160,10 @@ __global__ __launch_bounds__(64 * W) void decode_merge_kernel(float* __restrict_
     L += wave_sum(w * v.y);
 #pragma unroll
     for (int k = 0; k < GRP; ++k) {
+      // an empty partition's acc row was never written: select, not multiply
       const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
 #pragma unroll
-      for (int q = 0; q < PER; ++q) a[q] = fmaf(wk, part[k][q], a[q]);
+      for (int q = 0; q < PER; ++q) a[q] = wk > 0.f ? fmaf(wk, part[k][q], a[q]) : a[q];
     }
   }
   if constexpr (W > 1) {
@@ -332,11 +339,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
 
   if (t_begin >= t_end) {
     // Nothing to attend to.  With one partition the output row is zero;
-    // otherwise the merge skips partitions past the context.
+    // otherwise the partial is marked empty (no weight) for the merge.
     if (nP == 1 && head_ok) {
       float4* o = (float4*)(out + ((size_t)s * Hq + h) * D + 32 * j);
 #pragma unroll
       for (int k = 0; k < 8; ++k) o[k] = float4{0.f, 0.f, 0.f, 0.f};
+    } else if (head_ok && j == 0) {
+      ws.ml[((size_t)s * Hq + h) * nP + p] = float2{kNegInf, 0.f};
     }
     return;
   }
@@ -685,12 +694,15 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
   const int nh = min(GT, G - hg * GT);
 
   if (t_begin >= t_end) {
+    // as in the matrix-core kernel: a zero row, or an empty partial
     if (nP == 1 && tt == 0) {
       for (int i = 0; i < nh; ++i) {
         float* o = out + ((size_t)s * Hq + h0 + i) * D + c * DC;
 #pragma unroll
         for (int k = 0; k < DC; ++k) o[k] = 0.f;
       }
+    } else if (lane < nh) {
+      ws.ml[((size_t)s * Hq + h0 + lane) * nP + p] = float2{kNegInf, 0.f};
     }
     return;
   }
