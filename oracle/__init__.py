@@ -11,7 +11,10 @@ built with gcc) and adds three pure-Python/NumPy pieces:
 * thin ctypes wrappers around the C functions.
 
 Element types: ``numpy.float32`` is fp32, ``numpy.uint16`` holds the bits of
-bfloat16 values, ``numpy.int8`` is int8.
+bfloat16 values, ``numpy.int8`` is int8, ``numpy.uint8`` holds OCP E4M3 fp8
+codes.  Quantised caches (int8, E4M3) come with fp32 scales laid out per
+(block, KV head) ``[NB][Hkv]`` (scale mode 0) or per token ``[NB][Hkv][BS]``
+(scale mode 1).
 
 Sources, by page and section (the pages are French web articles on the KV
 cache and PagedAttention):
@@ -41,8 +44,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pa_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libpa_oracle.so")
 
-F32, BF16, I8 = 0, 1, 2
-_DTYPE_CODE = {np.dtype(np.float32): F32, np.dtype(np.uint16): BF16, np.dtype(np.int8): I8}
+F32, BF16, I8, FP8 = 0, 1, 2, 3
+_DTYPE_CODE = {np.dtype(np.float32): F32, np.dtype(np.uint16): BF16, np.dtype(np.int8): I8,
+               np.dtype(np.uint8): FP8}
+SCALE_BLOCK, SCALE_TOKEN = 0, 1
+
+
+def scale_shape(NB: int, Hkv: int, BS: int, scale_mode: int):
+    return (NB, Hkv, BS) if scale_mode == SCALE_TOKEN else (NB, Hkv)
 
 # Status codes of the pool policy (same meaning as the library's, defined
 # here independently).
@@ -63,14 +72,23 @@ def build(force: bool = False, src: str = _SRC, out: str = _LIB_PATH) -> str:
 def _bind(lib):
     P = ctypes.c_void_p
     i32 = ctypes.c_int
-    lib.oracle_paged_decode.argtypes = [P, P, i32, P, P, i32, P, P, P, i32, P,
+    lib.oracle_paged_decode.argtypes = [P, P, i32, P, P, i32, P, P, i32, P, i32, P,
                                         i32, i32, i32, i32, i32, i32, ctypes.c_double]
     lib.oracle_paged_decode.restype = i32
+    lib.oracle_fp8_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_fp8_e4m3_value.restype = ctypes.c_double
+    lib.oracle_fp8_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.oracle_fp8_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_swap_blocks.argtypes = [P, P, P, P, P, P, P, P, i32, i32, P, i32, i32, i32, i32, i32, i32]
+    lib.oracle_swap_blocks.restype = i32
+    lib.oracle_quantize_and_cache.argtypes = [P, P, i32, P, P, i32, P, P, i32, ctypes.c_float, ctypes.c_float,
+                                              P, i32, i32, i32, i32, i32]
+    lib.oracle_quantize_and_cache.restype = i32
     lib.oracle_slot_mapping.argtypes = [P, P, i32, P, P, i32, i32]
     lib.oracle_slot_mapping.restype = None
     lib.oracle_reshape_and_cache.argtypes = [P, P, P, P, i32, P, i32, i32, i32, i32, i32]
     lib.oracle_reshape_and_cache.restype = i32
-    lib.oracle_copy_blocks.argtypes = [P, P, i32, P, P, P, i32, i32, i32, i32, i32]
+    lib.oracle_copy_blocks.argtypes = [P, P, i32, P, P, i32, P, i32, i32, i32, i32, i32]
     lib.oracle_copy_blocks.restype = i32
     lib.oracle_quantize_int8.argtypes = [P, P, P, P, i32, i32, i32, i32]
     lib.oracle_quantize_int8.restype = None
@@ -120,14 +138,33 @@ def _code(a: np.ndarray) -> int:
     try:
         return _DTYPE_CODE[a.dtype]
     except KeyError:
-        raise TypeError("oracle element type must be float32, uint16 (bf16 bits) or int8, got %s" % a.dtype)
+        raise TypeError("oracle element type must be float32, uint16 (bf16 bits), int8 or uint8 (E4M3 codes), "
+                        "got %s" % a.dtype)
+
+
+def fp8_e4m3_value(code: int) -> float:
+    """Value of one OCP E4M3 code (NaN for 0x7F / 0xFF)."""
+    return float(_load().oracle_fp8_e4m3_value(int(code) & 0xFF))
+
+
+def fp8_e4m3_encode(x: float) -> int:
+    """Nearest E4M3 code to the fp32 value x (ties to even mantissa,
+    saturating at +-448)."""
+    return int(_load().oracle_fp8_e4m3_encode(float(np.float32(x))))
+
+
+def fp8_table() -> np.ndarray:
+    """float64[256]: the value of every E4M3 code."""
+    return np.array([fp8_e4m3_value(c) for c in range(256)], dtype=np.float64)
 
 
 def as_float64(a: np.ndarray) -> np.ndarray:
-    """Exact fp64 image of an fp32 / bf16-bits / int8 array."""
+    """Exact fp64 image of an fp32 / bf16-bits / int8 / E4M3-codes array."""
     a = np.asarray(a)
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if a.dtype == np.uint8:
+        return fp8_table()[a]
     return a.astype(np.float64)
 
 
@@ -142,14 +179,15 @@ def num_threads() -> int:
 
 def paged_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                  block_tables: np.ndarray, context_lens: np.ndarray, scale: float,
-                 k_scales: Optional[np.ndarray] = None, v_scales: Optional[np.ndarray] = None
-                 ) -> np.ndarray:
+                 k_scales: Optional[np.ndarray] = None, v_scales: Optional[np.ndarray] = None,
+                 scale_mode: int = SCALE_BLOCK) -> np.ndarray:
     """fp64 paged decode attention, ``out[S][Hq][D]``.
 
     q ``[S][Hq][D]``; caches ``[NB][Hkv][BS][D]``; block_tables
-    ``int32[S][max_blocks]``; context_lens ``int32[S]``; int8 caches need
-    ``k_scales``/``v_scales`` ``float32[NB][Hkv]``.  ``scale`` is applied as
-    given (pass the fp32 value a kernel receives to compare like with like).
+    ``int32[S][max_blocks]``; context_lens ``int32[S]``; int8 and E4M3
+    caches need ``k_scales``/``v_scales`` in the layout of ``scale_mode``.
+    ``scale`` is applied as given (pass the fp32 value a kernel receives to
+    compare like with like).
     """
     lib = _load()
     q = np.ascontiguousarray(q)
@@ -162,17 +200,18 @@ def paged_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     assert D2 == D and v_cache.shape == k_cache.shape and k_cache.dtype == v_cache.dtype
     assert bt.ndim == 2 and bt.shape[0] == S and cl.shape == (S,)
     kv = _code(k_cache)
-    if kv == I8:
+    if kv in (I8, FP8):
         assert k_scales is not None and v_scales is not None
         k_scales = np.ascontiguousarray(k_scales, dtype=np.float32)
         v_scales = np.ascontiguousarray(v_scales, dtype=np.float32)
-        assert k_scales.shape == (NB, Hkv) and v_scales.shape == (NB, Hkv)
+        shp = scale_shape(NB, Hkv, BS, scale_mode)
+        assert k_scales.shape == shp and v_scales.shape == shp
     else:
         k_scales = v_scales = None
     out = np.zeros((S, Hq, D), dtype=np.float64)
     rc = lib.oracle_paged_decode(_ptr(out), _ptr(q), _code(q), _ptr(k_cache), _ptr(v_cache), kv,
-                                 _ptr(k_scales), _ptr(v_scales), _ptr(bt), bt.shape[1], _ptr(cl),
-                                 S, Hq, Hkv, D, BS, NB, float(scale))
+                                 _ptr(k_scales), _ptr(v_scales), int(scale_mode), _ptr(bt), bt.shape[1],
+                                 _ptr(cl), S, Hq, Hkv, D, BS, NB, float(scale))
     if rc != 0:
         raise ValueError("oracle_paged_decode: a table entry or context length is out of range")
     return out
@@ -213,11 +252,12 @@ def gather_logical(cache: np.ndarray, block_tables: np.ndarray, context_lens: np
                    scales: Optional[np.ndarray] = None) -> List[np.ndarray]:
     """Per-sequence contiguous fp64 copies ``[n_s][Hkv][D]`` read through the
     block tables (for building inputs of :func:`contiguous_attention` from a
-    paged cache)."""
+    paged cache); scales ``[NB][Hkv]`` or per token ``[NB][Hkv][BS]``."""
     NB, Hkv, BS, D = cache.shape
     c64 = as_float64(cache)
     if scales is not None:
-        c64 = c64 * np.asarray(scales, dtype=np.float64)[:, :, None, None]
+        sc = np.asarray(scales, dtype=np.float64)
+        c64 = c64 * (sc[:, :, :, None] if sc.ndim == 3 else sc[:, :, None, None])
     res = []
     for s, n in enumerate(np.asarray(context_lens)):
         rows = [c64[block_tables[s][t // BS], :, t % BS, :] for t in range(int(n))]
@@ -259,18 +299,65 @@ def reshape_and_cache(key: np.ndarray, value: np.ndarray, k_cache: np.ndarray, v
 
 
 def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, pairs: np.ndarray,
-                k_scales: Optional[np.ndarray] = None, v_scales: Optional[np.ndarray] = None) -> None:
+                k_scales: Optional[np.ndarray] = None, v_scales: Optional[np.ndarray] = None,
+                scale_mode: int = SCALE_BLOCK) -> None:
     """In place; ``pairs`` is ``int64[P][2]`` of (src, dst) block ids."""
     lib = _load()
     assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
     pr = np.ascontiguousarray(pairs, dtype=np.int64).reshape(-1, 2)
     NB, Hkv, BS, D = k_cache.shape
     for a in (k_scales, v_scales):
-        assert a is None or (a.flags.c_contiguous and a.dtype == np.float32 and a.shape == (NB, Hkv))
+        assert a is None or (a.flags.c_contiguous and a.dtype == np.float32 and
+                             a.shape == scale_shape(NB, Hkv, BS, scale_mode))
     rc = lib.oracle_copy_blocks(_ptr(k_cache), _ptr(v_cache), k_cache.dtype.itemsize,
-                                _ptr(k_scales), _ptr(v_scales), _ptr(pr), pr.shape[0], Hkv, D, BS, NB)
+                                _ptr(k_scales), _ptr(v_scales), int(scale_mode), _ptr(pr), pr.shape[0],
+                                Hkv, D, BS, NB)
     if rc != 0:
         raise ValueError("oracle_copy_blocks: block id out of range")
+
+
+def swap_blocks(src_k: np.ndarray, src_v: np.ndarray, dst_k: np.ndarray, dst_v: np.ndarray, pairs: np.ndarray,
+                src_ks: Optional[np.ndarray] = None, src_vs: Optional[np.ndarray] = None,
+                dst_ks: Optional[np.ndarray] = None, dst_vs: Optional[np.ndarray] = None,
+                scale_mode: int = SCALE_BLOCK) -> None:
+    """In place on the destination pool; pools ``[NB][Hkv][BS][D]`` of one
+    element type, ``pairs`` ``int64[P][2]`` of (source id, destination id)."""
+    lib = _load()
+    for a in (src_k, src_v, dst_k, dst_v):
+        assert a.flags.c_contiguous
+    assert src_k.dtype == dst_k.dtype and src_k.shape[1:] == dst_k.shape[1:]
+    pr = np.ascontiguousarray(pairs, dtype=np.int64).reshape(-1, 2)
+    sNB, Hkv, BS, D = src_k.shape
+    dNB = dst_k.shape[0]
+    rc = lib.oracle_swap_blocks(_ptr(src_k), _ptr(src_v), _ptr(src_ks), _ptr(src_vs), _ptr(dst_k), _ptr(dst_v),
+                                _ptr(dst_ks), _ptr(dst_vs), src_k.dtype.itemsize, int(scale_mode), _ptr(pr),
+                                pr.shape[0], Hkv, D, BS, sNB, dNB)
+    if rc != 0:
+        raise ValueError("oracle_swap_blocks: block id out of range")
+
+
+def quantize_and_cache(key: np.ndarray, value: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                       k_scales: np.ndarray, v_scales: np.ndarray, slots: np.ndarray, scale_mode: int,
+                       k_static: float = 0.0, v_static: float = 0.0) -> None:
+    """Quantising cache write, in place.  key/value ``[T][Hkv][D]`` float32
+    or bf16 bits; caches int8 or uint8 (E4M3 codes) ``[NB][Hkv][BS][D]``;
+    scales in the layout of ``scale_mode`` (0: static scale per layer, given
+    as k_static / v_static and stamped per (block, head); 1: per token)."""
+    lib = _load()
+    for a in (k_cache, v_cache, k_scales, v_scales):
+        assert a.flags.c_contiguous
+    key = np.ascontiguousarray(key)
+    value = np.ascontiguousarray(value)
+    sl = np.ascontiguousarray(slots, dtype=np.int64)
+    NB, Hkv, BS, D = k_cache.shape
+    assert key.dtype == value.dtype and key.shape == value.shape == (sl.shape[0], Hkv, D)
+    assert k_cache.dtype == v_cache.dtype and _code(k_cache) in (I8, FP8)
+    assert k_scales.dtype == np.float32 and k_scales.shape == scale_shape(NB, Hkv, BS, scale_mode)
+    rc = lib.oracle_quantize_and_cache(_ptr(key), _ptr(value), _code(key), _ptr(k_cache), _ptr(v_cache),
+                                       _code(k_cache), _ptr(k_scales), _ptr(v_scales), int(scale_mode),
+                                       float(k_static), float(v_static), _ptr(sl), sl.shape[0], Hkv, D, BS, NB)
+    if rc != 0:
+        raise ValueError("oracle_quantize_and_cache: slot beyond the pool or bad static scale")
 
 
 def quantize_int8(x: np.ndarray, valid: np.ndarray):

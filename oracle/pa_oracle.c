@@ -24,9 +24,19 @@
  *    logical position to physical page, pages taken page by page.
  *
  * Element types (codes shared only by convention with the callers):
- *   0 = IEEE fp32, 1 = bfloat16 (upper 16 bits of an fp32), 2 = int8.
+ *   0 = IEEE fp32, 1 = bfloat16 (upper 16 bits of an fp32), 2 = int8,
+ *   3 = fp8 E4M3 in the OCP 8-bit floating-point format (1 sign bit, 4
+ *       exponent bits with bias 7, 3 mantissa bits; no infinities, the
+ *       all-ones exponent and mantissa encode NaN; largest finite 448).
  * Every stored element is converted to the double with the same value,
- * which is exact for all three types.
+ * which is exact for all four types.
+ *
+ * Quantised caches (int8, fp8) carry fp32 scales in one of two layouts:
+ *   scale mode 0: one scale per (block, KV head), [NB][Hkv];
+ *   scale mode 1: one scale per (block, KV head, slot) = per token, [NB][Hkv][BS].
+ * (ia-vox KV-cache article, section "Quantization du KV cache": a fixed
+ * scale per layer is the static form, a scale recomputed for every token the
+ * dynamic form.)
  *
  * Parity pins for every function live in tests/test_oracle_*.py; the
  * functions here have no "parity unpinned" part.
@@ -42,8 +52,24 @@
 #define OR_F32 0
 #define OR_BF16 1
 #define OR_I8 2
+#define OR_FP8 3
+
+#define OR_SCALE_BLOCK 0
+#define OR_SCALE_TOKEN 1
 
 /* ---- element decoding (input format, not the method) ------------------ */
+
+/* Value of an OCP E4M3 code: sign, exponent field e, mantissa field m.
+ * e == 0 is subnormal: m/8 * 2^(1-7); e in 1..15 is (1 + m/8) * 2^(e-7),
+ * except e == 15 with m == 7, which is NaN. */
+double oracle_fp8_e4m3_value(uint8_t code) {
+  int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m / 8.0, 1 - 7);
+  else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -v : v;
+}
 
 static double elem_as_double(const void* base, int64_t idx, int dtype) {
   if (dtype == OR_F32) {
@@ -60,6 +86,7 @@ static double elem_as_double(const void* base, int64_t idx, int dtype) {
     memcpy(&f, &bits, 4);
     return (double)f;
   }
+  if (dtype == OR_FP8) return oracle_fp8_e4m3_value(((const uint8_t*)base)[idx]);
   /* int8 */
   return (double)((const int8_t*)base)[idx];
 }
@@ -76,7 +103,7 @@ int oracle_num_threads(void) {
 int oracle_elem_bytes(int dtype) {
   if (dtype == OR_F32) return 4;
   if (dtype == OR_BF16) return 2;
-  if (dtype == OR_I8) return 1;
+  if (dtype == OR_I8 || dtype == OR_FP8) return 1;
   return -1;
 }
 
@@ -101,14 +128,20 @@ static int64_t cache_index(int64_t b, int g, int slot, int d, int Hkv, int BS,
   return (((b * Hkv + g) * BS) + slot) * (int64_t)D + d;
 }
 
+/* Index of the scale that applies to cache[b][g][slot][:]. */
+static int64_t scale_index(int64_t b, int g, int slot, int Hkv, int BS, int scale_mode) {
+  return scale_mode == OR_SCALE_TOKEN ? (b * Hkv + g) * BS + slot : b * Hkv + g;
+}
+
 /* One key or value component of token t, dequantised when the cache holds
- * int8 codes: the stored code times the fp32 scale of its (block, KV head).
- * The product of an fp32 and an int8 is exact in double. */
+ * int8 or fp8 codes: the stored code's value times its fp32 scale.  The
+ * product of an fp32 and an int8 or E4M3 value is exact in double. */
 static double kv_value(const void* cache, const float* scales, int dtype,
-                       int64_t b, int g, int slot, int d, int Hkv, int BS,
-                       int D) {
+                       int scale_mode, int64_t b, int g, int slot, int d,
+                       int Hkv, int BS, int D) {
   double x = elem_as_double(cache, cache_index(b, g, slot, d, Hkv, BS, D), dtype);
-  if (dtype == OR_I8) x *= (double)scales[b * Hkv + g];
+  if (dtype == OR_I8 || dtype == OR_FP8)
+    x *= (double)scales[scale_index(b, g, slot, Hkv, BS, scale_mode)];
   return x;
 }
 
@@ -128,7 +161,7 @@ static double kv_value(const void* cache, const float* scales, int dtype,
 int oracle_paged_decode(double* out, const void* q, int q_dtype,
                         const void* k_cache, const void* v_cache, int kv_dtype,
                         const float* k_scales, const float* v_scales,
-                        const int32_t* block_tables, int max_blocks,
+                        int scale_mode, const int32_t* block_tables, int max_blocks,
                         const int32_t* context_lens, int S, int Hq, int Hkv,
                         int D, int BS, int NB, double scale) {
   int G, bad = 0;
@@ -156,7 +189,7 @@ int oracle_paged_decode(double* out, const void* q, int q_dtype,
       if (b < 0) { bad = 1; x[t] = 0.0; continue; }
       for (int d = 0; d < D; ++d)
         dot += elem_as_double(q, qoff + d, q_dtype) *
-               kv_value(k_cache, k_scales, kv_dtype, b, g, t % BS, d, Hkv, BS, D);
+               kv_value(k_cache, k_scales, kv_dtype, scale_mode, b, g, t % BS, d, Hkv, BS, D);
       x[t] = scale * dot;
     }
     /* softmax weights exp(x_t - max x) / sum */
@@ -170,7 +203,7 @@ int oracle_paged_decode(double* out, const void* q, int q_dtype,
       double w = x[t] / z;
       if (b < 0) continue;
       for (int d = 0; d < D; ++d)
-        o[d] += w * kv_value(v_cache, v_scales, kv_dtype, b, g, t % BS, d, Hkv, BS, D);
+        o[d] += w * kv_value(v_cache, v_scales, kv_dtype, scale_mode, b, g, t % BS, d, Hkv, BS, D);
     }
     free(x);
   }
@@ -239,23 +272,54 @@ int oracle_reshape_and_cache(const uint8_t* key, const uint8_t* value,
  * 3, scenario 01: shared pages are duplicated only when a user starts to
  * produce its own continuation).  For each pair (src, dst), in order, the
  * whole physical block -- every KV head, every slot, used or not -- of the K
- * cache and of the V cache is copied, and so are the per-(block, head)
- * scales when the caller passes them.  Returns -1 (after applying the valid
- * prefix) if an id lies outside [0, NB).
+ * cache and of the V cache is copied, and so are the block's scales (all
+ * of them in either scale layout) when the caller passes them.  Returns -1
+ * (after applying the valid prefix) if an id lies outside [0, NB).
  */
 int oracle_copy_blocks(uint8_t* k_cache, uint8_t* v_cache, int elem_bytes,
-                       float* k_scales, float* v_scales, const int64_t* pairs,
-                       int P, int Hkv, int D, int BS, int NB) {
+                       float* k_scales, float* v_scales, int scale_mode,
+                       const int64_t* pairs, int P, int Hkv, int D, int BS, int NB) {
   const int64_t block_bytes = (int64_t)Hkv * BS * D * elem_bytes;
+  const int64_t nsc = scale_mode == OR_SCALE_TOKEN ? (int64_t)Hkv * BS : Hkv;
   for (int p = 0; p < P; ++p) {
     int64_t src = pairs[2 * p], dst = pairs[2 * p + 1];
     if (src < 0 || src >= NB || dst < 0 || dst >= NB) return -1;
     memmove(k_cache + dst * block_bytes, k_cache + src * block_bytes, (size_t)block_bytes);
     memmove(v_cache + dst * block_bytes, v_cache + src * block_bytes, (size_t)block_bytes);
     if (k_scales)
-      for (int h = 0; h < Hkv; ++h) k_scales[dst * Hkv + h] = k_scales[src * Hkv + h];
+      for (int64_t i = 0; i < nsc; ++i) k_scales[dst * nsc + i] = k_scales[src * nsc + i];
     if (v_scales)
-      for (int h = 0; h < Hkv; ++h) v_scales[dst * Hkv + h] = v_scales[src * Hkv + h];
+      for (int64_t i = 0; i < nsc; ++i) v_scales[dst * nsc + i] = v_scales[src * nsc + i];
+  }
+  return 0;
+}
+
+/*
+ * Block swap between two pools of the same shape (ia-vox article, section
+ * "Offloading et stratégies hybrides CPU/GPU": cold parts of the cache move
+ * to CPU memory and back; "Cache KV en production": a preempted request's
+ * pages are released and its state restored later).  For each pair
+ * (src, dst), the whole block src of the source pool (K, V and, when given,
+ * its scales) is copied to block dst of the destination pool.  Returns -1
+ * (after applying the valid prefix) if an id lies outside its pool.
+ */
+int oracle_swap_blocks(const uint8_t* src_k, const uint8_t* src_v,
+                       const float* src_ks, const float* src_vs,
+                       uint8_t* dst_k, uint8_t* dst_v, float* dst_ks,
+                       float* dst_vs, int elem_bytes, int scale_mode,
+                       const int64_t* pairs, int P, int Hkv, int D, int BS,
+                       int src_NB, int dst_NB) {
+  const int64_t block_bytes = (int64_t)Hkv * BS * D * elem_bytes;
+  const int64_t nsc = scale_mode == OR_SCALE_TOKEN ? (int64_t)Hkv * BS : Hkv;
+  for (int p = 0; p < P; ++p) {
+    int64_t src = pairs[2 * p], dst = pairs[2 * p + 1];
+    if (src < 0 || src >= src_NB || dst < 0 || dst >= dst_NB) return -1;
+    memcpy(dst_k + dst * block_bytes, src_k + src * block_bytes, (size_t)block_bytes);
+    memcpy(dst_v + dst * block_bytes, src_v + src * block_bytes, (size_t)block_bytes);
+    if (src_ks && dst_ks)
+      for (int64_t i = 0; i < nsc; ++i) dst_ks[dst * nsc + i] = src_ks[src * nsc + i];
+    if (src_vs && dst_vs)
+      for (int64_t i = 0; i < nsc; ++i) dst_vs[dst * nsc + i] = src_vs[src * nsc + i];
   }
   return 0;
 }
@@ -297,4 +361,103 @@ void oracle_quantize_int8(int8_t* codes, float* scales, const float* x,
           codes[i] = (int8_t)r;
         }
     }
+}
+
+/* ---- quantising cache write -------------------------------------------- */
+
+/*
+ * Nearest E4M3 code to the fp32 value v: the finite code whose value is
+ * closest to v; between two equally close codes the one with an even
+ * mantissa field; |v| beyond the largest finite value (448) gives +-448
+ * (saturation); NaN gives the NaN code 0x7F.  Written as a search over all
+ * codes of v's sign, so that it follows the definition above literally.
+ */
+uint8_t oracle_fp8_e4m3_encode(float v) {
+  const int sign = signbit(v) ? 1 : 0;
+  const double a = fabs((double)v);
+  int best = 0;
+  double best_err;
+  if (isnan(v)) return 0x7F;
+  best_err = fabs(oracle_fp8_e4m3_value(0) - a);
+  for (int c = 1; c < 0x7F; ++c) { /* 0x7F is NaN */
+    double err = fabs(oracle_fp8_e4m3_value((uint8_t)c) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  if (a > 448.0) best = 0x7E;
+  return (uint8_t)(best | (sign << 7));
+}
+
+/* One element in the source format as an fp32 value (exact). */
+static float src_as_float(const void* base, int64_t idx, int dtype) {
+  return (float)elem_as_double(base, idx, dtype);
+}
+
+/*
+ * Quantising form of the cache write: each new token's key and value rows
+ * ([T][Hkv][D], fp32 or bf16) are stored as int8 or E4M3 codes with fp32
+ * scales, tokens in order, slot < 0 skipped.  Per (token, KV head), for K
+ * and V separately, in fp32:
+ *   scale mode 0 (static, one scale for the layer): s = the caller's static
+ *     scale, and scales[b][h] = s;
+ *   scale mode 1 (dynamic, per token): amax = max_d |x_d|, s = amax / qmax
+ *     (qmax = 127 for int8, 448 for E4M3), s = 1 when amax == 0, and
+ *     scales[b][h][slot % BS] = s;
+ *   code_d = int8: clamp(rint(x_d / s), -127, 127), rint rounding half to
+ *     even; E4M3: the nearest code to x_d / s (oracle_fp8_e4m3_encode).
+ * Returns -1 (after applying the valid prefix) if a slot lies beyond the
+ * pool or the static scale is not positive and finite.
+ */
+int oracle_quantize_and_cache(const void* key, const void* value, int src_dtype,
+                              void* k_cache, void* v_cache, int kv_dtype,
+                              float* k_scales, float* v_scales, int scale_mode,
+                              float k_static, float v_static,
+                              const int64_t* slots, int T, int Hkv, int D,
+                              int BS, int NB) {
+  const float qmax = kv_dtype == OR_FP8 ? 448.0f : 127.0f;
+  if (scale_mode == OR_SCALE_BLOCK &&
+      !(k_static > 0.0f && v_static > 0.0f && isfinite(k_static) && isfinite(v_static)))
+    return -1;
+  for (int t = 0; t < T; ++t) {
+    int64_t slot = slots[t], b;
+    int off;
+    if (slot < 0) continue;
+    b = slot / BS;
+    off = (int)(slot % BS);
+    if (b >= NB) return -1;
+    for (int h = 0; h < Hkv; ++h)
+      for (int kv = 0; kv < 2; ++kv) {
+        const void* src = kv ? value : key;
+        void* cache = kv ? v_cache : k_cache;
+        float* scales = kv ? v_scales : k_scales;
+        const int64_t row = ((int64_t)t * Hkv + h) * D;
+        float s;
+        if (scale_mode == OR_SCALE_BLOCK) {
+          s = kv ? v_static : k_static;
+        } else {
+          float amax = 0.0f;
+          for (int d = 0; d < D; ++d) {
+            float a = fabsf(src_as_float(src, row + d, src_dtype));
+            if (a > amax) amax = a;
+          }
+          s = amax > 0.0f ? amax / qmax : 1.0f;
+        }
+        scales[scale_index(b, h, off, Hkv, BS, scale_mode)] = s;
+        for (int d = 0; d < D; ++d) {
+          const float r = src_as_float(src, row + d, src_dtype) / s;
+          const int64_t i = cache_index(b, h, off, d, Hkv, BS, D);
+          if (kv_dtype == OR_FP8) {
+            ((uint8_t*)cache)[i] = oracle_fp8_e4m3_encode(r);
+          } else {
+            float c = rintf(r);
+            if (c > 127.0f) c = 127.0f;
+            if (c < -127.0f) c = -127.0f;
+            ((int8_t*)cache)[i] = (int8_t)c;
+          }
+        }
+      }
+  }
+  return 0;
 }

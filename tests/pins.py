@@ -431,8 +431,229 @@ def pin_quantiser_invariants():
             assert np.all(codes[b, h, n:] == 0)
 
 
+# --------------------------------------------------------------------------
+# quantised caches: E4M3 format, per-token scales, quantising write, swap
+# --------------------------------------------------------------------------
+
+def _torch_e4m3_values():
+    """float64[256] from torch's own float8_e4m3fn decoding (a library
+    routine independent of the oracle), or None if torch lacks the type."""
+    import torch
+    if not hasattr(torch, "float8_e4m3fn"):
+        return None
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def pin_fp8_format_values():
+    """The E4M3 format's closed forms: 0x38 = 1, 0x7E = 448 (largest),
+    0x01 = 2^-9 (smallest subnormal), 0x08 = 2^-6 (smallest normal),
+    0x07 = 7 * 2^-9, 0x7F and 0xFF NaN, sign bit = negation; every code
+    agrees with torch's float8_e4m3fn decoding."""
+    t = oracle.fp8_table()
+    assert t[0x38] == 1.0 and t[0x7E] == 448.0 and t[0x01] == 2.0 ** -9 and t[0x08] == 2.0 ** -6
+    assert t[0x07] == 7 * 2.0 ** -9 and t[0x3F] == 1.875 and t[0x40] == 2.0
+    assert math.isnan(t[0x7F]) and math.isnan(t[0xFF]) and np.isfinite(t).sum() == 254
+    assert np.array_equal(t[0x80:0xFF], -t[0x00:0x7F]) and math.copysign(1.0, t[0x80]) == -1.0
+    finite = t[:0x7F]
+    assert np.all(np.diff(finite) > 0)           # codes 0..0x7E are increasing
+    ref = _torch_e4m3_values()
+    if ref is not None:
+        ok = ~np.isnan(ref)
+        assert np.array_equal(np.isnan(t), ~ok) and np.array_equal(t[ok], ref[ok])
+
+
+def pin_fp8_encode():
+    """Round to the nearest code, ties to the even mantissa, saturating at
+    +-448: every finite code is a fixed point; midpoints go to the even
+    neighbour; beyond 448 gives 0x7E; NaN gives 0x7F; torch's fp32 ->
+    float8_e4m3fn conversion agrees inside the finite range."""
+    t = oracle.fp8_table()
+    for c in list(range(0, 0x7F)) + list(range(0x80, 0xFF)):
+        assert oracle.fp8_e4m3_encode(t[c]) == c, hex(c)
+    for c in range(0, 0x7E):
+        mid = (t[c] + t[c + 1]) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert oracle.fp8_e4m3_encode(mid) == even, hex(c)
+        assert oracle.fp8_e4m3_encode(-mid) == even | 0x80
+    assert oracle.fp8_e4m3_encode(449.0) == 0x7E and oracle.fp8_e4m3_encode(1e30) == 0x7E
+    assert oracle.fp8_e4m3_encode(-500.0) == 0xFE and oracle.fp8_e4m3_encode(float("nan")) == 0x7F
+    import torch
+    if hasattr(torch, "float8_e4m3fn"):
+        x = np.random.default_rng(44).uniform(-440, 440, 4000).astype(np.float32)
+        x[:1000] *= np.float32(1e-3)
+        ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        got = np.array([oracle.fp8_e4m3_encode(v) for v in x], np.uint8)
+        assert np.array_equal(got, ref)
+
+
+def pin_per_token_scales_closed_form():
+    """Per-token scales: slot 1's K code 2 with its own scale 0.5 gives the
+    logits (0, 1); V codes 4 and 6 with slot scales 0.25 and 1/3 give the
+    values e0 and 2 e1.  The other slots' scales (7, 9) must not be read.
+    The same with E4M3 codes (0x48 = 4, 0x4C = 6, 0x40 = 2)."""
+    g = golden("attention_closed_forms.json")["ctx2"]
+    D, BS = 64, 16
+    for dt, two, four, six in ((np.int8, 2, 4, 6), (np.uint8, 0x40, 0x48, 0x4C)):
+        K = np.zeros((2, 1, D), dt)
+        K[1, 0, 0] = two
+        V = np.zeros((2, 1, D), dt)
+        V[0, 0, 0] = four
+        V[1, 0, 1] = six
+        kc, bt = paginate([K], BS, 3, tables=np.array([[1]]), fill=0)
+        vc, _ = paginate([V], BS, 3, tables=bt, fill=0)
+        ks = np.full((3, 1, BS), 7.0, np.float32)
+        vs = np.full((3, 1, BS), 9.0, np.float32)
+        ks[1, 0, 1] = 0.5
+        vs[1, 0, 0] = 0.25
+        vs[1, 0, 1] = np.float32(1.0 / 3.0)
+        q = bf16_bits(unit(D, 0).reshape(1, 1, D))
+        out = oracle.paged_decode(q, kc, vc, bt, np.array([2], np.int32), 1.0, ks, vs,
+                                  scale_mode=oracle.SCALE_TOKEN)[0, 0]
+        v1 = 6.0 * float(np.float32(1.0 / 3.0))
+        assert abs(out[0] - g["out_d0"]) < 1e-15 and abs(out[1] - v1 * g["out_d1"]) < 1e-15, out[:2]
+
+
+def pin_quantised_decode_matches_contiguous():
+    """int8 and E4M3 caches, both scale layouts: the paged oracle equals
+    unpaged NumPy attention over the dequantised logical rows."""
+    rng = np.random.default_rng(45)
+    lens = [1, 17, 40]
+    Hq, Hkv, D, BS, NB = 4, 2, 64, 16, 12
+    for dt in (np.int8, np.uint8):
+        for mode in (oracle.SCALE_BLOCK, oracle.SCALE_TOKEN):
+            seqs_k = [rng.integers(-127, 128, (n, Hkv, D)).astype(np.int8) for n in lens]
+            seqs_v = [rng.integers(-127, 128, (n, Hkv, D)).astype(np.int8) for n in lens]
+            if dt == np.uint8:   # random finite E4M3 codes
+                seqs_k = [(a.view(np.uint8) & 0x77) | (a.view(np.uint8) & 0x80) for a in seqs_k]
+                seqs_v = [(a.view(np.uint8) & 0x77) | (a.view(np.uint8) & 0x80) for a in seqs_v]
+            kc, bt = paginate(seqs_k, BS, NB, rng=rng, fill=0)
+            vc, _ = paginate(seqs_v, BS, NB, tables=bt, fill=0)
+            shp = oracle.scale_shape(NB, Hkv, BS, mode)
+            ks = (rng.random(shp) * 0.05).astype(np.float32)
+            vs = (rng.random(shp) * 0.05).astype(np.float32)
+            q = rng.standard_normal((len(lens), Hq, D)).astype(np.float32)
+            cl = np.array(lens, np.int32)
+            got = oracle.paged_decode(q, kc, vc, bt, cl, 0.125, ks, vs, scale_mode=mode)
+            K64 = oracle.gather_logical(kc, bt, cl, ks)
+            V64 = oracle.gather_logical(vc, bt, cl, vs)
+            ref = oracle.contiguous_attention(q.astype(np.float64), K64, V64, 0.125)
+            assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def pin_quantising_write_hand_values():
+    """int8, per token: a row with amax 127 gets scale 1 and rint codes
+    (ties to even); an all-zero row scale 1 and codes 0.  Static: the given
+    scale (different for K and V) is stamped in the (block, head) and codes
+    saturate at +-127.  E4M3 per token: a row with amax 448 gets scale 1 and
+    the nearest codes.  Skipped slots and other slots stay untouched."""
+    NB, H, BS, D = 3, 2, 4, 4
+    key = np.zeros((3, H, D), np.float32)
+    key[0, 0] = [127.0, -63.5, 0.5, 1.5]
+    key[0, 1] = [2.49, -2.5, 3.5, -127.0]
+    val = -key
+    val[0, 1] = [0.0, 0.0, 0.0, 0.0]
+    key[1] = 5.0
+    slots = np.array([6, -1, 11], np.int64)     # block 1 slot 2, skipped, block 2 slot 3
+    kc = np.full((NB, H, BS, D), 55, np.int8)
+    vc = kc.copy()
+    ks = np.full((NB, H, BS), -1.0, np.float32)
+    vs = ks.copy()
+    oracle.quantize_and_cache(key, val, kc, vc, ks, vs, slots, oracle.SCALE_TOKEN)
+    assert list(kc[1, 0, 2]) == [127, -64, 0, 2] and ks[1, 0, 2] == 1.0
+    assert list(kc[1, 1, 2]) == [2, -2, 4, -127] and ks[1, 1, 2] == 1.0
+    assert list(vc[1, 0, 2]) == [-127, 64, 0, -2] and list(vc[1, 1, 2]) == [0, 0, 0, 0] and vs[1, 1, 2] == 1.0
+    assert np.all(kc[2, :, 3] == 0) and np.all(ks[2, :, 3] == 1.0)        # token 2 is all zeros
+    touched = np.zeros((NB, H, BS), bool)
+    touched[1, :, 2] = touched[2, :, 3] = True
+    assert np.all(kc[~touched] == 55) and np.all(ks[~touched] == -1.0)
+    # static scales per layer, stamped per (block, head)
+    kc2 = np.full((NB, H, BS, D), 55, np.int8)
+    vc2 = kc2.copy()
+    ks2 = np.full((NB, H), -1.0, np.float32)
+    vs2 = ks2.copy()
+    oracle.quantize_and_cache(key, val, kc2, vc2, ks2, vs2, slots, oracle.SCALE_BLOCK, 0.5, 2.0)
+    assert list(kc2[1, 0, 2]) == [127, -127, 1, 3] and ks2[1, 0] == 0.5 and vs2[1, 0] == 2.0
+    assert list(vc2[1, 0, 2]) == [-64, 32, 0, -1] and ks2[0, 0] == -1.0
+    # E4M3, per token: amax 448 -> scale 1
+    key3 = np.zeros((1, 1, 4), np.float32)
+    key3[0, 0] = [448.0, -1.0625, 0.3, 2.0 ** -9]
+    kc3 = np.zeros((1, 1, BS, 4), np.uint8)
+    vc3 = kc3.copy()
+    ks3 = np.zeros((1, 1, BS), np.float32)
+    vs3 = ks3.copy()
+    oracle.quantize_and_cache(key3, key3, kc3, vc3, ks3, vs3, np.array([1], np.int64), oracle.SCALE_TOKEN)
+    assert ks3[0, 0, 1] == 1.0 and list(kc3[0, 0, 1]) == [0x7E, 0xB8, oracle.fp8_e4m3_encode(0.3), 0x01]
+
+
+def pin_quantising_write_round_trip():
+    """Per-token int8: |code * s - x| <= s / 2 and the largest |x| of a row
+    maps to +-127; per-token E4M3: the largest |x| maps to +-448 and every
+    element is within half a code spacing (relative 2^-4 for normals)."""
+    rng = np.random.default_rng(46)
+    T, H, D, BS, NB = 9, 2, 32, 16, 4
+    x = (rng.standard_normal((T, H, D)) * rng.random((T, H, 1)) * 10).astype(np.float32)
+    slots = rng.permutation(NB * BS)[:T].astype(np.int64)
+    for dt, qmax in ((np.int8, 127), (np.uint8, 448)):
+        kc = np.zeros((NB, H, BS, D), dt)
+        vc = kc.copy()
+        ks = np.zeros((NB, H, BS), np.float32)
+        vs = ks.copy()
+        oracle.quantize_and_cache(x, x, kc, vc, ks, vs, slots, oracle.SCALE_TOKEN)
+        for t, sl in enumerate(slots):
+            for h in range(H):
+                row = x[t, h].astype(np.float64)
+                s = float(ks[sl // BS, h, sl % BS])
+                assert s == float(np.float32(np.float32(np.abs(x[t, h]).max()) / np.float32(qmax)))
+                codes = oracle.as_float64(kc[sl // BS, h, sl % BS])
+                assert np.max(np.abs(codes)) == qmax
+                deq = codes * s
+                if dt == np.int8:
+                    assert np.max(np.abs(deq - row)) <= 0.5 * s * (1 + 1e-6)
+                else:
+                    big = np.abs(row) >= 2.0 ** -6 * s
+                    assert np.all(np.abs(deq - row)[big] <= np.abs(row)[big] * 2.0 ** -4 * (1 + 1e-6))
+
+
+def pin_swap_blocks_exact():
+    """Swap between pools of different sizes copies whole blocks (K, V and
+    their scales in either layout) and nothing else."""
+    rng = np.random.default_rng(47)
+    H, BS, D = 2, 16, 32
+    for mode in (oracle.SCALE_BLOCK, oracle.SCALE_TOKEN):
+        sk = rng.integers(-128, 128, (6, H, BS, D)).astype(np.int8)
+        sv = rng.integers(-128, 128, (6, H, BS, D)).astype(np.int8)
+        dk = rng.integers(-128, 128, (9, H, BS, D)).astype(np.int8)
+        dv = rng.integers(-128, 128, (9, H, BS, D)).astype(np.int8)
+        sks = rng.random(oracle.scale_shape(6, H, BS, mode)).astype(np.float32)
+        svs = rng.random(oracle.scale_shape(6, H, BS, mode)).astype(np.float32)
+        dks = rng.random(oracle.scale_shape(9, H, BS, mode)).astype(np.float32)
+        dvs = rng.random(oracle.scale_shape(9, H, BS, mode)).astype(np.float32)
+        d0 = (dk.copy(), dv.copy(), dks.copy(), dvs.copy())
+        pairs = np.array([[5, 0], [2, 8], [5, 3]], np.int64)
+        oracle.swap_blocks(sk, sv, dk, dv, pairs, sks, svs, dks, dvs, scale_mode=mode)
+        for src, dst in pairs:
+            assert np.array_equal(dk[dst], sk[src]) and np.array_equal(dv[dst], sv[src])
+            assert np.array_equal(dks[dst], sks[src]) and np.array_equal(dvs[dst], svs[src])
+        for b in (1, 2, 4, 5, 6, 7):
+            assert np.array_equal(dk[b], d0[0][b]) and np.array_equal(dv[b], d0[1][b])
+            assert np.array_equal(dks[b], d0[2][b]) and np.array_equal(dvs[b], d0[3][b])
+    # copy_blocks moves per-token scales whole as well
+    kc = rng.integers(-128, 128, (4, H, BS, D)).astype(np.int8)
+    vc = kc.copy()
+    ks = rng.random((4, H, BS)).astype(np.float32)
+    vs = rng.random((4, H, BS)).astype(np.float32)
+    ks0 = ks.copy()
+    oracle.copy_blocks(kc, vc, np.array([[1, 3]], np.int64), ks, vs, scale_mode=oracle.SCALE_TOKEN)
+    assert np.array_equal(ks[3], ks0[1]) and np.array_equal(ks[:3], ks0[:3])
+
+
+QUANT_PINS = [pin_fp8_format_values, pin_fp8_encode, pin_per_token_scales_closed_form,
+              pin_quantised_decode_matches_contiguous, pin_quantising_write_hand_values,
+              pin_quantising_write_round_trip, pin_swap_blocks_exact]
+
 CACHE_PINS = [pin_slot_mapping_figure, pin_slot_mapping_edges,
               pin_reshape_writes_exactly_one_slot_per_token, pin_copy_blocks_exact,
               pin_quantiser_hand_values, pin_quantiser_invariants]
 
-ALL_PINS = DECODE_PINS + CACHE_PINS
+ALL_PINS = DECODE_PINS + CACHE_PINS + QUANT_PINS
