@@ -54,14 +54,26 @@ typedef enum {
   PA_ERR_HIP = 5          /* a HIP runtime call failed */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2 } pa_dtype;
+/* Element types.  PA_FP8_E4M3 is the OCP 8-bit floating-point E4M3 format
+ * (sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, NaN =
+ * all ones, largest finite value 448).  PA_I8 and PA_FP8_E4M3 caches are
+ * quantised: every stored code is multiplied by an fp32 scale. */
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
+
+/* Layout of the fp32 scales of a quantised cache (ia-vox KV-cache article,
+ * section "Quantization du KV cache": a fixed scale per layer is the static
+ * form, a scale recomputed for every token the dynamic form):
+ *   PA_SCALE_BLOCK: one scale per (block, kv head), [num_blocks][num_kv_heads];
+ *   PA_SCALE_TOKEN: one scale per (block, kv head, slot), i.e. per token,
+ *                   [num_blocks][num_kv_heads][block_size]. */
+typedef enum { PA_SCALE_BLOCK = 0, PA_SCALE_TOKEN = 1 } pa_scale_mode;
 
 /* Static string naming a status code. */
 const char* pa_status_string(pa_status s);
 /* Message of the last failure on the calling thread ("" if none). */
 const char* pa_last_error(void);
 /* ABI version of this header (incremented on any incompatible change). */
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 int32_t pa_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -76,16 +88,18 @@ int32_t pa_abi_version(void);
  *
  * The query of the newest token attends over all n tokens of its
  * sequence, the newest included (write it first with
- * pa_reshape_and_cache).  n = 0 gives a row of zeros.  For int8 caches the
- * stored code is multiplied by the fp32 scale of its (block, kv head):
- * K = k_scales[b][g] * code, V = v_scales[b][g] * code (the per-block form
- * between the per-layer and per-token scales of the ia-vox article,
- * section "Quantization du KV cache").
+ * pa_reshape_and_cache).  n = 0 gives a row of zeros.  For quantised
+ * caches (PA_I8, PA_FP8_E4M3) the stored code's value is multiplied by its
+ * fp32 scale, K = k_scale * code and V = v_scale * code, the scale taken
+ * per (block, kv head) or per token as kv_scale_mode says (see
+ * pa_scale_mode).
  *
  * Layouts (row-major, densely packed):
  *   q             [num_seqs][num_q_heads][head_dim]          q_dtype
  *   k/v_cache     [num_blocks][num_kv_heads][block_size][head_dim]  kv_dtype
- *   k/v_scales    [num_blocks][num_kv_heads] fp32 (int8 caches only)
+ *   k/v_scales    fp32, quantised caches only: [num_blocks][num_kv_heads]
+ *                 (PA_SCALE_BLOCK) or [num_blocks][num_kv_heads][block_size]
+ *                 (PA_SCALE_TOKEN)
  *   block_tables  [num_seqs][max_blocks_per_seq] int32; entries past
  *                 ceil(n / BS) are never read
  *   context_lens  [num_seqs] int32, 0 <= n <= max_blocks_per_seq * BS and
@@ -95,7 +109,8 @@ int32_t pa_abi_version(void);
  * names, are never read: they may hold anything, NaN included.
  *
  * Supported: head_dim in {64, 128}; block_size in {16, 32};
- * q_dtype in {PA_F32, PA_BF16}; kv_dtype in {PA_F32, PA_BF16, PA_I8};
+ * q_dtype in {PA_F32, PA_BF16}; kv_dtype in {PA_F32, PA_BF16, PA_I8,
+ * PA_FP8_E4M3};
  * out_dtype PA_F32; num_q_heads a multiple of num_kv_heads, at most 16
  * query heads per kv head.  All of q, caches and out 16-byte aligned.
  *
@@ -121,10 +136,11 @@ int32_t pa_abi_version(void);
  * (n-1) % BS, every kv head) and attends with them.  The result, cache
  * bytes included, is that of pa_slot_mapping (context_lens form) +
  * pa_reshape_and_cache + pa_decode, in one launch.  n must not exceed
- * max_context_len.  Not available for int8 caches (PA_ERR_UNSUPPORTED).
+ * max_context_len.  Not available for quantised caches (PA_ERR_UNSUPPORTED):
+ * write them with pa_quantize_and_cache first.
  *
  * `kernel` selects the implementation: 0 = automatic, 1 = vector-ALU
- * kernel (any supported case), 2 = matrix-core kernel (bf16 or int8
+ * kernel (any supported case), 2 = matrix-core kernel (bf16, int8 or E4M3
  * caches with bf16 queries, head_dim 128, 1..16 query heads per kv head;
  * else PA_ERR_UNSUPPORTED).  Both compute the definition above; they
  * differ in rounding only.
@@ -138,7 +154,7 @@ typedef struct {
   void* k_cache;                 /* written only by the fused cache write */
   void* v_cache;
   pa_dtype kv_dtype;
-  const float* k_scales;         /* non-NULL iff kv_dtype == PA_I8 */
+  const float* k_scales;         /* non-NULL iff kv_dtype is PA_I8 or PA_FP8_E4M3 */
   const float* v_scales;
   const int32_t* block_tables;
   int32_t max_blocks_per_seq;
@@ -159,6 +175,7 @@ typedef struct {
   const void* new_key;           /* optional fused cache write: both or neither */
   const void* new_value;
   int64_t total_context_len;     /* optional hint: sum of context_lens (0 = unknown), 0 <= it <= num_seqs * max_context_len */
+  int32_t kv_scale_mode;         /* pa_scale_mode of k/v_scales (quantised caches; else ignored) */
 } pa_decode_args;
 
 /* Host only: bytes of workspace pa_decode needs for these arguments
@@ -202,7 +219,8 @@ pa_status pa_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_se
  * key, value [num_tokens][num_kv_heads][head_dim] of kv_dtype, caches as in
  * pa_decode, slot_mapping [num_tokens] int64.  Slots must be distinct and
  * below num_blocks * block_size (caller's responsibility).
- * kv_dtype PA_I8 is PA_ERR_UNSUPPORTED (quantising writes are not built).
+ * Quantised caches are written with pa_quantize_and_cache; PA_I8 and
+ * PA_FP8_E4M3 here are PA_ERR_UNSUPPORTED.
  */
 pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                pa_dtype kv_dtype, const int64_t* slot_mapping, int32_t num_tokens,
@@ -220,12 +238,63 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
  * tokens into them).  block_pairs is device int64 [num_pairs][2].  All ids
  * must lie in [0, num_blocks); destinations must be distinct and disjoint
  * from the sources (caller's responsibility), so the order of the pairs
- * does not matter.  Scales: non-NULL iff kv_dtype == PA_I8.
+ * does not matter.  Scales: non-NULL iff the cache is quantised, in the
+ * layout scale_mode names (every scale of the block is copied).
  */
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, pa_dtype kv_dtype, float* k_scales,
-                         float* v_scales, const int64_t* block_pairs, int32_t num_pairs,
-                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                         int32_t num_blocks, void* stream);
+                         float* v_scales, int32_t scale_mode, const int64_t* block_pairs,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Block swap between two pools (device <-> pinned host, or device <-> device)
+ * ------------------------------------------------------------------------
+ * For each pair p: (src, dst) = (block_pairs[2p], block_pairs[2p+1]), copy
+ * the whole block src of the source pool (K, V, and the scales when given)
+ * into block dst of the destination pool.  This moves a preempted or cold
+ * request's blocks to CPU memory and back (ia-vox article, section
+ * "Offloading et stratégies hybrides CPU/GPU"; "Cache KV en production":
+ * a preempted request releases its pages and is restored later).  Both
+ * pools have the shape [*][num_kv_heads][block_size][head_dim] of kv_dtype;
+ * either may live in device memory or in pinned host memory allocated with
+ * hipHostMalloc (the kernel reads and writes it over the host link).
+ * block_pairs is device (or pinned host) int64 [num_pairs][2]; ids outside
+ * [0, src_num_blocks) / [0, dst_num_blocks) skip the pair.  Destinations
+ * must be distinct (caller's responsibility).  Scales: all four NULL, or
+ * all four given for a quantised pool, in the layout scale_mode names.
+ */
+pa_status pa_swap_blocks(const void* src_k, const void* src_v, const float* src_k_scales,
+                         const float* src_v_scales, void* dst_k, void* dst_v, float* dst_k_scales,
+                         float* dst_v_scales, pa_dtype kv_dtype, int32_t scale_mode,
+                         const int64_t* block_pairs, int32_t num_pairs, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t src_num_blocks,
+                         int32_t dst_num_blocks, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Quantising cache write (int8 or E4M3 caches)
+ * ------------------------------------------------------------------------
+ * The form of pa_reshape_and_cache for quantised caches (ia-vox article,
+ * section "Quantization du KV cache": a fixed scale per layer, or one
+ * recomputed for every token).  For t < num_tokens with slot =
+ * slot_mapping[t] >= 0, for every kv head h, for K and V separately, in
+ * fp32 with correctly rounded division:
+ *   PA_SCALE_BLOCK (static): s = k_static_scale / v_static_scale (> 0,
+ *     finite), stored as k_scales[b][h] / v_scales[b][h];
+ *   PA_SCALE_TOKEN (dynamic): amax = max_d |x_d| of the row, s = amax / Q
+ *     (Q = 127 for PA_I8, 448 for PA_FP8_E4M3; s = 1 when amax = 0),
+ *     stored as k_scales[b][h][slot % BS];
+ *   codes: PA_I8: clamp(rint(x_d / s), -127, 127), ties to even;
+ *     PA_FP8_E4M3: the E4M3 code nearest to x_d / s, ties to the even
+ *     mantissa, magnitudes above 448 saturating to 448, NaN to 0x7F.
+ * key, value [num_tokens][num_kv_heads][head_dim] of src_dtype (PA_F32 or
+ * PA_BF16); caches and scales as in pa_decode.  Slots must be distinct and
+ * below num_blocks * block_size (caller's responsibility).
+ */
+pa_status pa_quantize_and_cache(const void* key, const void* value, pa_dtype src_dtype, void* k_cache,
+                                void* v_cache, pa_dtype kv_dtype, float* k_scales, float* v_scales,
+                                int32_t scale_mode, float k_static_scale, float v_static_scale,
+                                const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t num_blocks, void* stream);
 
 /* ------------------------------------------------------------------------
  * Block pool (host only)

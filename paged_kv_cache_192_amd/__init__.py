@@ -18,9 +18,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_OOM, PA_ERR_STATE, PA_ERR_HIP = range(6)
-PA_F32, PA_BF16, PA_I8 = 0, 1, 2
+PA_F32, PA_BF16, PA_I8, PA_FP8_E4M3 = 0, 1, 2, 3
+PA_SCALE_BLOCK, PA_SCALE_TOKEN = 0, 1
 KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_OOM",
                 4: "PA_ERR_STATE", 5: "PA_ERR_HIP"}
@@ -66,6 +67,7 @@ class DecodeArgs(ctypes.Structure):
         ("new_key", ctypes.c_void_p),
         ("new_value", ctypes.c_void_p),
         ("total_context_len", ctypes.c_int64),
+        ("kv_scale_mode", ctypes.c_int32),
     ]
 
 
@@ -95,7 +97,14 @@ def library() -> ctypes.CDLL:
     lib.pa_slot_mapping.restype = ctypes.c_int
     lib.pa_reshape_and_cache.argtypes = [P, P, P, P, ctypes.c_int, P, i32, i32, i32, i32, i32, P]
     lib.pa_reshape_and_cache.restype = ctypes.c_int
-    lib.pa_copy_blocks.argtypes = [P, P, ctypes.c_int, P, P, P, i32, i32, i32, i32, i32, P]
+    lib.pa_copy_blocks.argtypes = [P, P, ctypes.c_int, P, P, i32, P, i32, i32, i32, i32, i32, P]
+    lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_swap_blocks.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int, i32, P, i32, i32, i32, i32, i32, i32, P]
+    lib.pa_swap_blocks.restype = ctypes.c_int
+    f32 = ctypes.c_float
+    lib.pa_quantize_and_cache.argtypes = [P, P, ctypes.c_int, P, P, ctypes.c_int, P, P, i32, f32, f32, P, i32, i32,
+                                          i32, i32, i32, P]
+    lib.pa_quantize_and_cache.restype = ctypes.c_int
     lib.pa_copy_blocks.restype = ctypes.c_int
     lib.pa_pool_create.argtypes = [i32, P, ctypes.POINTER(ctypes.c_void_p)]
     lib.pa_pool_create.restype = ctypes.c_int
@@ -134,10 +143,17 @@ def _torch():
 def _dtype_code(t) -> int:
     torch = _torch()
     codes = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8}
+    if hasattr(torch, "float8_e4m3fn"):
+        codes[torch.float8_e4m3fn] = PA_FP8_E4M3
     try:
         return codes[t.dtype]
     except KeyError:
-        raise TypeError("unsupported tensor dtype %s (float32, bfloat16 or int8)" % t.dtype)
+        raise TypeError("unsupported tensor dtype %s (float32, bfloat16, int8 or float8_e4m3fn)" % t.dtype)
+
+
+def scale_mode_of(k_cache, k_scales) -> int:
+    """PA_SCALE_TOKEN when the scales are ``[NB][Hkv][BS]``, else PA_SCALE_BLOCK."""
+    return PA_SCALE_TOKEN if (k_scales is not None and k_scales.dim() == 3) else PA_SCALE_BLOCK
 
 
 def _ptr(t) -> Optional[int]:
@@ -147,6 +163,17 @@ def _ptr(t) -> Optional[int]:
         raise ValueError("tensor must live on the GPU")
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _ptr_pool(t) -> Optional[int]:
+    """Device tensor, or pinned host tensor (pa_swap_blocks)."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    if not t.is_cuda and not t.is_pinned():
+        raise ValueError("host pool tensors must be pinned (pin_memory=True)")
     return t.data_ptr()
 
 
@@ -210,6 +237,7 @@ def make_decode_args(q, k_cache, v_cache, block_tables, context_lens, scale: flo
     a.new_key = get(new_key)
     a.new_value = get(new_value)
     a.total_context_len = int(total_context_len)
+    a.kv_scale_mode = scale_mode_of(k_cache, k_scales)
     return a
 
 
@@ -274,10 +302,26 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None) -
 
 def copy_blocks(k_cache, v_cache, block_pairs, k_scales=None, v_scales=None, stream=None) -> None:
     """``pa_copy_blocks``: block_pairs int64 ``[P][2]`` of (src, dst)."""
-    NB, Hkv, BS, D = k_cache.shape
-    P = block_pairs.shape[0]
-    _check(library().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), _ptr(k_scales),
-                                    _ptr(v_scales), _ptr(block_pairs), P, Hkv, D, BS, NB, _stream(stream)))
+    prepare_copy_blocks(k_cache, v_cache, block_pairs, k_scales, v_scales, stream=stream)()
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, block_pairs, src_k_scales=None, src_v_scales=None, dst_k_scales=None,
+                dst_v_scales=None, stream=None) -> None:
+    """``pa_swap_blocks``: whole blocks from one pool to another; either
+    pool may be a pinned host tensor.  block_pairs int64 ``[P][2]`` of
+    (source id, destination id), on the device or pinned."""
+    prepare_swap_blocks(src_k, src_v, dst_k, dst_v, block_pairs, src_k_scales, src_v_scales, dst_k_scales,
+                        dst_v_scales, stream=stream)()
+
+
+def quantize_and_cache(key, value, k_cache, v_cache, k_scales, v_scales, slot_mapping, k_static_scale: float = 0.0,
+                       v_static_scale: float = 0.0, stream=None) -> None:
+    """``pa_quantize_and_cache``: key/value ``[T][Hkv][D]`` (float32 or
+    bfloat16) quantised into int8 or float8_e4m3fn caches.  Scales
+    ``[NB][Hkv]`` select the static per-layer scale (k/v_static_scale);
+    ``[NB][Hkv][BS]`` the dynamic per-token scale."""
+    prepare_quantize_and_cache(key, value, k_cache, v_cache, k_scales, v_scales, slot_mapping, k_static_scale,
+                               v_static_scale, stream=stream)()
 
 
 # --------------------------------------------------------------------------
@@ -412,6 +456,34 @@ def prepare_slot_mapping(block_tables, block_size: int, out, positions=None, con
 
 def prepare_copy_blocks(k_cache, v_cache, block_pairs, k_scales=None, v_scales=None, stream=None) -> PreparedCall:
     NB, Hkv, BS, D = k_cache.shape
-    args = (_ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), _ptr(k_scales), _ptr(v_scales), _ptr(block_pairs),
-            int(block_pairs.shape[0]), Hkv, D, BS, NB, _stream(stream))
+    args = (_ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), _ptr(k_scales), _ptr(v_scales),
+            scale_mode_of(k_cache, k_scales), _ptr(block_pairs), int(block_pairs.shape[0]), Hkv, D, BS, NB,
+            _stream(stream))
     return PreparedCall("pa_copy_blocks", args, (k_cache, v_cache, block_pairs, k_scales, v_scales))
+
+
+def prepare_swap_blocks(src_k, src_v, dst_k, dst_v, block_pairs, src_k_scales=None, src_v_scales=None,
+                        dst_k_scales=None, dst_v_scales=None, stream=None) -> PreparedCall:
+    sNB, Hkv, BS, D = src_k.shape
+    dNB = dst_k.shape[0]
+    if tuple(dst_k.shape[1:]) != (Hkv, BS, D) or src_k.dtype != dst_k.dtype:
+        raise ValueError("source and destination pools differ in shape or dtype")
+    args = (_ptr_pool(src_k), _ptr_pool(src_v), _ptr_pool(src_k_scales), _ptr_pool(src_v_scales), _ptr_pool(dst_k),
+            _ptr_pool(dst_v), _ptr_pool(dst_k_scales), _ptr_pool(dst_v_scales), _dtype_code(src_k),
+            scale_mode_of(src_k, src_k_scales), _ptr_pool(block_pairs), int(block_pairs.shape[0]), Hkv, D, BS,
+            sNB, dNB, _stream(stream))
+    return PreparedCall("pa_swap_blocks", args, (src_k, src_v, dst_k, dst_v, block_pairs, src_k_scales,
+                                                 src_v_scales, dst_k_scales, dst_v_scales))
+
+
+def prepare_quantize_and_cache(key, value, k_cache, v_cache, k_scales, v_scales, slot_mapping,
+                               k_static_scale: float = 0.0, v_static_scale: float = 0.0, stream=None) -> PreparedCall:
+    NB, Hkv, BS, D = k_cache.shape
+    T = key.shape[0]
+    if tuple(key.shape) != (T, Hkv, D) or tuple(value.shape) != (T, Hkv, D):
+        raise ValueError("key/value must be [T][%d][%d]" % (Hkv, D))
+    args = (_ptr(key), _ptr(value), _dtype_code(key), _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache),
+            _ptr(k_scales), _ptr(v_scales), scale_mode_of(k_cache, k_scales), float(k_static_scale),
+            float(v_static_scale), _ptr(slot_mapping), T, Hkv, D, BS, NB, _stream(stream))
+    return PreparedCall("pa_quantize_and_cache", args, (key, value, k_cache, v_cache, k_scales, v_scales,
+                                                        slot_mapping))

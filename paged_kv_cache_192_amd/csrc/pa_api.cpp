@@ -26,7 +26,8 @@ pa_status hip_fail(hipError_t e, const char* what) {
 
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-static bool valid_dtype(int t) { return t == PA_F32 || t == PA_BF16 || t == PA_I8; }
+static bool valid_dtype(int t) { return t == PA_F32 || t == PA_BF16 || t == PA_I8 || t == PA_FP8_E4M3; }
+static bool valid_scale_mode(int m) { return m == PA_SCALE_BLOCK || m == PA_SCALE_TOKEN; }
 
 // Waves a decode launch should put on the chip (256 CUs on MI355X).  The
 // matrix-core kernel keeps two 16-token tiles in flight per wave: with a
@@ -72,15 +73,17 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   if (!valid_dtype(a->q_dtype) || !valid_dtype(a->kv_dtype) || !valid_dtype(a->out_dtype))
     return fail(PA_ERR_INVALID, "pa_decode: unknown dtype code");
   if (a->out_dtype != PA_F32) return fail(PA_ERR_UNSUPPORTED, "pa_decode: out_dtype must be PA_F32");
-  if (a->q_dtype == PA_I8) return fail(PA_ERR_UNSUPPORTED, "pa_decode: int8 queries");
-  const bool i8 = a->kv_dtype == PA_I8;
+  if (quantised(a->q_dtype)) return fail(PA_ERR_UNSUPPORTED, "pa_decode: quantised queries");
+  const bool i8 = quantised(a->kv_dtype);  // 1-byte codes with scales
   if (i8 != (a->k_scales != nullptr) || i8 != (a->v_scales != nullptr))
-    return fail(PA_ERR_INVALID, "pa_decode: k_scales/v_scales must be given exactly for int8 caches");
+    return fail(PA_ERR_INVALID, "pa_decode: k_scales/v_scales must be given exactly for quantised caches");
+  if (i8 && !valid_scale_mode(a->kv_scale_mode))
+    return fail(PA_ERR_INVALID, "pa_decode: kv_scale_mode %d not a pa_scale_mode", a->kv_scale_mode);
   if (!std::isfinite(a->scale)) return fail(PA_ERR_INVALID, "pa_decode: scale is not finite");
   if ((a->new_key == nullptr) != (a->new_value == nullptr))
     return fail(PA_ERR_INVALID, "pa_decode: give both new_key and new_value, or neither");
   if (a->new_key && i8)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: the fused cache write needs a quantising write for int8 caches");
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: no fused cache write for quantised caches");
   if (a->max_context_len < 0 || (int64_t)a->max_context_len > (int64_t)a->max_blocks_per_seq * a->block_size)
     return fail(PA_ERR_INVALID, "pa_decode: max_context_len %d outside [0, max_blocks_per_seq*block_size]",
                 a->max_context_len);
@@ -93,13 +96,12 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
     return fail(PA_ERR_INVALID, "pa_decode: total_context_len %lld outside [0, num_seqs * max_context_len]",
                 (long long)a->total_context_len);
 
-  const bool mfma_ok = a->q_dtype == PA_BF16 && (a->kv_dtype == PA_BF16 || a->kv_dtype == PA_I8) &&
-                       a->head_dim == 128;
+  const bool mfma_ok = a->q_dtype == PA_BF16 && (a->kv_dtype == PA_BF16 || i8) && a->head_dim == 128;
   KernelKind kind;
   if (a->kernel == KERNEL_MFMA) {
     if (!mfma_ok)
-      return fail(PA_ERR_UNSUPPORTED, "pa_decode: matrix-core kernel needs bf16 queries, bf16 or int8 "
-                                      "caches and head_dim 128");
+      return fail(PA_ERR_UNSUPPORTED, "pa_decode: matrix-core kernel needs bf16 queries, bf16, int8 or "
+                                      "E4M3 caches and head_dim 128");
     kind = KERNEL_MFMA;
   } else if (a->kernel == KERNEL_VALU) {
     kind = KERNEL_VALU;
@@ -194,9 +196,11 @@ pa_status pa_decode(const pa_decode_args* a) {
   if (!aligned(a->out, 16) || !aligned(a->q, 16) || !aligned(a->k_cache, 16) || !aligned(a->v_cache, 16) ||
       !aligned(a->new_key, 16) || !aligned(a->new_value, 16))
     return fail(PA_ERR_INVALID, "pa_decode: out, q, the caches and new_key/new_value must be 16-byte aligned");
+  const size_t sa = a->kv_scale_mode == PA_SCALE_TOKEN ? 16 : 4;
   if (!aligned(a->block_tables, 4) || !aligned(a->context_lens, 4) ||
-      (a->k_scales && (!aligned(a->k_scales, 4) || !aligned(a->v_scales, 4))))
-    return fail(PA_ERR_INVALID, "pa_decode: tables, lengths and scales must be 4-byte aligned");
+      (a->k_scales && (!aligned(a->k_scales, sa) || !aligned(a->v_scales, sa))))
+    return fail(PA_ERR_INVALID, "pa_decode: tables and lengths must be 4-byte aligned, scales 4-byte "
+                                "(per block) or 16-byte (per token) aligned");
   if (p.workspace_bytes) {
     if (!a->workspace || a->workspace_bytes < p.workspace_bytes)
       return fail(PA_ERR_INVALID, "pa_decode: workspace of %zu bytes needed, %zu given", p.workspace_bytes,
@@ -240,8 +244,8 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
   pa_status s = check_cache_shape("pa_reshape_and_cache", kv_dtype, num_kv_heads, head_dim, block_size, num_blocks);
   if (s != PA_OK) return s;
   if (num_tokens < 0) return fail(PA_ERR_INVALID, "pa_reshape_and_cache: num_tokens < 0");
-  if (kv_dtype == PA_I8)
-    return fail(PA_ERR_UNSUPPORTED, "pa_reshape_and_cache: int8 caches need a quantising write (not built)");
+  if (quantised(kv_dtype))
+    return fail(PA_ERR_UNSUPPORTED, "pa_reshape_and_cache: quantised caches are written by pa_quantize_and_cache");
   if (num_tokens == 0) return PA_OK;
   if (!key || !value || !k_cache || !v_cache || !slot_mapping)
     return fail(PA_ERR_INVALID, "pa_reshape_and_cache: NULL device pointer");
@@ -253,20 +257,105 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
 }
 
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, pa_dtype kv_dtype, float* k_scales, float* v_scales,
-                         const int64_t* block_pairs, int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
-                         int32_t block_size, int32_t num_blocks, void* stream) {
+                         int32_t scale_mode, const int64_t* block_pairs, int32_t num_pairs, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t num_blocks, void* stream) {
   pa_status s = check_cache_shape("pa_copy_blocks", kv_dtype, num_kv_heads, head_dim, block_size, num_blocks);
   if (s != PA_OK) return s;
   if (num_pairs < 0) return fail(PA_ERR_INVALID, "pa_copy_blocks: num_pairs < 0");
-  const bool i8 = kv_dtype == PA_I8;
-  if (i8 != (k_scales != nullptr) || i8 != (v_scales != nullptr))
-    return fail(PA_ERR_INVALID, "pa_copy_blocks: k_scales/v_scales must be given exactly for int8 caches");
+  const bool q8 = quantised(kv_dtype);
+  if (q8 != (k_scales != nullptr) || q8 != (v_scales != nullptr))
+    return fail(PA_ERR_INVALID, "pa_copy_blocks: k_scales/v_scales must be given exactly for quantised caches");
+  if (q8 && !valid_scale_mode(scale_mode))
+    return fail(PA_ERR_INVALID, "pa_copy_blocks: scale_mode %d not a pa_scale_mode", scale_mode);
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !block_pairs) return fail(PA_ERR_INVALID, "pa_copy_blocks: NULL device pointer");
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_pairs, 8))
     return fail(PA_ERR_INVALID, "pa_copy_blocks: caches must be 16-byte aligned");
-  return launch_copy_blocks(k_cache, v_cache, dtype_bytes(kv_dtype), k_scales, v_scales, block_pairs, num_pairs,
-                            num_kv_heads, head_dim, block_size, num_blocks, (hipStream_t)stream);
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * dtype_bytes(kv_dtype);
+  return launch_block_copy(k_cache, v_cache, k_scales, v_scales, k_cache, v_cache, k_scales, v_scales, block_bytes,
+                           q8 ? scales_per_block(scale_mode, num_kv_heads, block_size) : 0, block_pairs, num_pairs,
+                           num_blocks, num_blocks, (hipStream_t)stream);
+}
+
+// Address under which a kernel reaches p: device memory as is, pinned host
+// memory (hipHostMalloc) through its device mapping; NULL for anything else
+// (pageable host memory would fault the GPU, so it is refused).
+static const void* device_view(const void* p) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged || at.type == hipMemoryTypeUnified)
+    return p;
+  if (at.type == hipMemoryTypeHost) return at.devicePointer;
+  return nullptr;
+}
+
+pa_status pa_swap_blocks(const void* src_k, const void* src_v, const float* src_k_scales, const float* src_v_scales,
+                         void* dst_k, void* dst_v, float* dst_k_scales, float* dst_v_scales, pa_dtype kv_dtype,
+                         int32_t scale_mode, const int64_t* block_pairs, int32_t num_pairs, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t src_num_blocks, int32_t dst_num_blocks,
+                         void* stream) {
+  pa_status s = check_cache_shape("pa_swap_blocks", kv_dtype, num_kv_heads, head_dim, block_size,
+                                  src_num_blocks < dst_num_blocks ? src_num_blocks : dst_num_blocks);
+  if (s != PA_OK) return s;
+  if (num_pairs < 0) return fail(PA_ERR_INVALID, "pa_swap_blocks: num_pairs < 0");
+  const int given = (src_k_scales != nullptr) + (src_v_scales != nullptr) + (dst_k_scales != nullptr) +
+                    (dst_v_scales != nullptr);
+  if (given != 0 && given != 4)
+    return fail(PA_ERR_INVALID, "pa_swap_blocks: give all four scale arrays or none");
+  if (given && !quantised(kv_dtype))
+    return fail(PA_ERR_INVALID, "pa_swap_blocks: scales given for a cache that is not quantised");
+  if (given && !valid_scale_mode(scale_mode))
+    return fail(PA_ERR_INVALID, "pa_swap_blocks: scale_mode %d not a pa_scale_mode", scale_mode);
+  if (num_pairs == 0) return PA_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !block_pairs)
+    return fail(PA_ERR_INVALID, "pa_swap_blocks: NULL pointer");
+  if (!aligned(src_k, 16) || !aligned(src_v, 16) || !aligned(dst_k, 16) || !aligned(dst_v, 16) ||
+      !aligned(block_pairs, 8))
+    return fail(PA_ERR_INVALID, "pa_swap_blocks: pools must be 16-byte aligned");
+  const void* dv[9] = {src_k, src_v, dst_k, dst_v, block_pairs, src_k_scales, src_v_scales, dst_k_scales,
+                       dst_v_scales};
+  for (int i = 0; i < (given ? 9 : 5); ++i) {
+    const void* v = device_view(dv[i]);
+    if (!v) return fail(PA_ERR_INVALID, "pa_swap_blocks: argument %d is neither device nor pinned host memory", i);
+    dv[i] = v;
+  }
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * dtype_bytes(kv_dtype);
+  return launch_block_copy(dv[0], dv[1], (const float*)dv[5], (const float*)dv[6], (void*)dv[2], (void*)dv[3],
+                           (float*)dv[7], (float*)dv[8], block_bytes,
+                           given ? scales_per_block(scale_mode, num_kv_heads, block_size) : 0,
+                           (const int64_t*)dv[4], num_pairs, src_num_blocks, dst_num_blocks, (hipStream_t)stream);
+}
+
+pa_status pa_quantize_and_cache(const void* key, const void* value, pa_dtype src_dtype, void* k_cache, void* v_cache,
+                                pa_dtype kv_dtype, float* k_scales, float* v_scales, int32_t scale_mode,
+                                float k_static_scale, float v_static_scale, const int64_t* slot_mapping,
+                                int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                int32_t num_blocks, void* stream) {
+  pa_status s = check_cache_shape("pa_quantize_and_cache", kv_dtype, num_kv_heads, head_dim, block_size, num_blocks);
+  if (s != PA_OK) return s;
+  if (!quantised(kv_dtype))
+    return fail(PA_ERR_INVALID, "pa_quantize_and_cache: kv_dtype must be PA_I8 or PA_FP8_E4M3");
+  if (src_dtype != PA_F32 && src_dtype != PA_BF16)
+    return fail(PA_ERR_INVALID, "pa_quantize_and_cache: src_dtype must be PA_F32 or PA_BF16");
+  if (!valid_scale_mode(scale_mode))
+    return fail(PA_ERR_INVALID, "pa_quantize_and_cache: scale_mode %d not a pa_scale_mode", scale_mode);
+  if (scale_mode == PA_SCALE_BLOCK &&
+      !(k_static_scale > 0.f && v_static_scale > 0.f && std::isfinite(k_static_scale) &&
+        std::isfinite(v_static_scale)))
+    return fail(PA_ERR_INVALID, "pa_quantize_and_cache: static scales must be positive and finite");
+  if (num_tokens < 0) return fail(PA_ERR_INVALID, "pa_quantize_and_cache: num_tokens < 0");
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !k_scales || !v_scales || !slot_mapping)
+    return fail(PA_ERR_INVALID, "pa_quantize_and_cache: NULL device pointer");
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(k_scales, 4) || !aligned(v_scales, 4) || !aligned(slot_mapping, 8))
+    return fail(PA_ERR_INVALID, "pa_quantize_and_cache: key, value and caches must be 16-byte aligned");
+  return launch_quantize_and_cache(key, value, src_dtype, k_cache, v_cache, kv_dtype, k_scales, v_scales, scale_mode,
+                                   k_static_scale, v_static_scale, slot_mapping, num_tokens, num_kv_heads, head_dim,
+                                   block_size, num_blocks, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -1,7 +1,8 @@
-// Cache-side kernels: slot mapping, the per-token cache write and the
-// copy-on-write block copy.  All three are byte movers bound by launch
-// latency at decode batch sizes; they use 16-byte vector accesses and never
-// touch memory outside the slots or blocks they are given.
+// Cache-side kernels: slot mapping, the per-token cache write (plain and
+// quantising) and the whole-block copy used for copy-on-write and for
+// swapping blocks to and from a host pool.  They are bound by launch
+// latency at decode batch sizes (the host link for swaps) and never touch
+// memory outside the slots or blocks they are given.
 #include "pa_internal.h"
 
 namespace pa {
@@ -51,24 +52,25 @@ __global__ void reshape_and_cache_kernel(const uint4* __restrict__ key, const ui
   }
 }
 
-// Grid: x = chunk group inside a block, y = pair, z = 0 (K) or 1 (V).
-// Each thread copies kCopyUnroll 16-byte chunks of one physical block, all
-// loads issued before the first store (a group that reaches past the
-// block's end takes a guarded path); the first threads of each (pair, K/V)
-// also copy that block's per-head scales when present.
+// Whole-block copy between pools (copy-on-write inside one pool, swap
+// between a device and a pinned host pool).  Grid: x = chunk group inside
+// a block, y = pair, z = 0 (K) or 1 (V).  Each thread copies kCopyUnroll
+// 16-byte chunks of one block, all loads issued before the first store (a
+// group that reaches past the block's end takes a guarded path); the
+// x = 0 workgroup of each (pair, K/V) also copies the block's scales.
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;
 
-__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
-    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, float* __restrict__ k_scales,
-    float* __restrict__ v_scales, const int64_t* __restrict__ pairs, int64_t block_chunks, int32_t Hkv,
-    int64_t num_blocks) {
+__global__ __launch_bounds__(kCopyThreads) void block_copy_kernel(
+    const uint4* __restrict__ src_k, const uint4* __restrict__ src_v, const float* __restrict__ src_ks,
+    const float* __restrict__ src_vs, uint4* __restrict__ dst_k, uint4* __restrict__ dst_v,
+    float* __restrict__ dst_ks, float* __restrict__ dst_vs, const int64_t* __restrict__ pairs,
+    int64_t block_chunks, int64_t scales_per_blk, int64_t src_NB, int64_t dst_NB) {
   const int p = blockIdx.y;
   const int64_t src = pairs[2 * p], dst = pairs[2 * p + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  uint4* cache = blockIdx.z ? v_cache : k_cache;
-  const uint4* from = cache + src * block_chunks;
-  uint4* to = cache + dst * block_chunks;
+  if (src < 0 || src >= src_NB || dst < 0 || dst >= dst_NB) return;
+  const uint4* from = (blockIdx.z ? src_v : src_k) + src * block_chunks;
+  uint4* to = (blockIdx.z ? dst_v : dst_k) + dst * block_chunks;
   const int64_t group = (int64_t)blockIdx.x * kCopyThreads * kCopyUnroll;
   const int64_t base = group + threadIdx.x;
   if (group + kCopyThreads * kCopyUnroll <= block_chunks) {
@@ -81,8 +83,93 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
   } else {
     for (int64_t i = base; i < block_chunks; i += kCopyThreads) to[i] = from[i];
   }
-  float* scales = blockIdx.z ? v_scales : k_scales;
-  if (scales && blockIdx.x == 0 && threadIdx.x < Hkv) scales[dst * Hkv + threadIdx.x] = scales[src * Hkv + threadIdx.x];
+  const float* ssc = blockIdx.z ? src_vs : src_ks;
+  float* dsc = blockIdx.z ? dst_vs : dst_ks;
+  if (ssc && blockIdx.x == 0)
+    for (int64_t i = threadIdx.x; i < scales_per_blk; i += kCopyThreads)
+      dsc[dst * scales_per_blk + i] = ssc[src * scales_per_blk + i];
+}
+
+// ---------------------------------------------------------------------------
+// Quantising cache write.  One wave per (token, kv head); lane l holds
+// elements l + 64 i of the row (i < D / 64), for K and then V.
+// ---------------------------------------------------------------------------
+
+// Nearest OCP E4M3 code to v: ties to the even mantissa, magnitudes above
+// 448 saturate, NaN -> 0x7F.  Normal range: keep 3 of fp32's 23 mantissa
+// bits with round-to-nearest-even on the 20 dropped bits (a carry moves to
+// the exponent), then rebias the exponent from 127 to 7.  Below 2^-6 the
+// codes are the multiples of 2^-9 (code 8 being the smallest normal).
+__device__ __forceinline__ unsigned e4m3_encode(float v) {
+  const unsigned sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (a != a) return 0x7Fu;
+  if (a > 448.f) return sign | 0x7Eu;
+  unsigned code;
+  if (a < 0.015625f) {
+    code = (unsigned)rintf(a * 512.f);
+  } else {
+    const unsigned ab = __float_as_uint(a);
+    code = ((ab + 0x7FFFFu + ((ab >> 20) & 1u)) >> 20) - (120u << 3);
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ float wave_amax(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+template <typename SRC, bool FP8, int PER>
+__global__ __launch_bounds__(64) void quantize_and_cache_kernel(
+    const SRC* __restrict__ key, const SRC* __restrict__ value, unsigned char* __restrict__ k_cache,
+    unsigned char* __restrict__ v_cache, float* __restrict__ k_scales, float* __restrict__ v_scales,
+    int per_token, float k_static, float v_static, const int64_t* __restrict__ slots, int Hkv, int BS,
+    int64_t num_slots) {
+  constexpr int D = 64 * PER;
+  const int t = blockIdx.x / Hkv, h = blockIdx.x % Hkv;
+  const int lane = threadIdx.x;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t b = slot / BS;
+  const int off = (int)(slot % BS);
+  const float qmax = FP8 ? 448.f : 127.f;
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
+    const SRC* src = (kv ? value : key) + ((int64_t)t * Hkv + h) * D;
+    float x[PER];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      x[i] = (float)src[lane + 64 * i];
+      amax = fmaxf(amax, fabsf(x[i]));
+    }
+    float s;
+    if (per_token) {
+      amax = wave_amax(amax);
+      s = amax > 0.f ? amax / qmax : 1.f;
+    } else {
+      s = kv ? v_static : k_static;
+    }
+    unsigned char* dst = (kv ? v_cache : k_cache) + ((b * Hkv + h) * BS + off) * D;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const float r = x[i] / s;
+      unsigned code;
+      if (FP8) {
+        code = e4m3_encode(r);
+      } else {
+        const float c = fminf(fmaxf(rintf(r), -127.f), 127.f);
+        code = (unsigned)(int)c & 0xFFu;
+      }
+      dst[lane + 64 * i] = (unsigned char)code;
+    }
+    if (lane == 0) {
+      float* sc = kv ? v_scales : k_scales;
+      sc[per_token ? (b * Hkv + h) * BS + off : b * Hkv + h] = s;
+    }
+  }
 }
 
 pa_status launch_slot_mapping(const int32_t* block_tables, int32_t max_blocks, int32_t num_seqs, const int32_t* seq_idx,
@@ -108,16 +195,43 @@ pa_status launch_reshape_and_cache(const void* key, const void* value, void* k_c
   return e == hipSuccess ? PA_OK : hip_fail(e, "pa_reshape_and_cache launch");
 }
 
-pa_status launch_copy_blocks(void* k_cache, void* v_cache, int elem_bytes, float* k_scales, float* v_scales,
-                             const int64_t* pairs, int32_t P, int32_t Hkv, int32_t D, int32_t BS,
-                             int32_t NB, hipStream_t st) {
-  const int64_t block_chunks = (int64_t)Hkv * BS * D * elem_bytes / 16;
+pa_status launch_block_copy(const void* src_k, const void* src_v, const float* src_ks, const float* src_vs,
+                            void* dst_k, void* dst_v, float* dst_ks, float* dst_vs, int64_t block_bytes,
+                            int64_t scales_per_blk, const int64_t* pairs, int32_t P, int32_t src_NB,
+                            int32_t dst_NB, hipStream_t st) {
+  const int64_t block_chunks = block_bytes / 16;
   const int64_t per_group = (int64_t)kCopyThreads * kCopyUnroll;
   dim3 grid((unsigned)((block_chunks + per_group - 1) / per_group), (unsigned)P, 2);
-  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kCopyThreads), 0, st, (uint4*)k_cache, (uint4*)v_cache, k_scales,
-                     v_scales, pairs, block_chunks, Hkv, (int64_t)NB);
+  hipLaunchKernelGGL(block_copy_kernel, grid, dim3(kCopyThreads), 0, st, (const uint4*)src_k, (const uint4*)src_v,
+                     src_ks, src_vs, (uint4*)dst_k, (uint4*)dst_v, dst_ks, dst_vs, pairs, block_chunks,
+                     scales_per_blk, (int64_t)src_NB, (int64_t)dst_NB);
   hipError_t e = hipGetLastError();
-  return e == hipSuccess ? PA_OK : hip_fail(e, "pa_copy_blocks launch");
+  return e == hipSuccess ? PA_OK : hip_fail(e, "block copy launch");
+}
+
+pa_status launch_quantize_and_cache(const void* key, const void* value, pa_dtype src_dtype, void* k_cache,
+                                    void* v_cache, pa_dtype kv_dtype, float* k_scales, float* v_scales,
+                                    int32_t scale_mode, float k_static, float v_static, const int64_t* slots,
+                                    int32_t T, int32_t Hkv, int32_t D, int32_t BS, int32_t NB, hipStream_t st) {
+  const size_t waves = (size_t)T * Hkv;
+  if (waves > 0x7fffffffu) return fail(PA_ERR_UNSUPPORTED, "pa_quantize_and_cache: grid too large");
+  const int per_token = scale_mode == PA_SCALE_TOKEN;
+  const int64_t num_slots = (int64_t)NB * BS;
+#define PA_QUANT_LAUNCH(SRC, FP8, PER)                                                                         \
+  hipLaunchKernelGGL((quantize_and_cache_kernel<SRC, FP8, PER>), dim3((unsigned)waves), dim3(64), 0, st,      \
+                     (const SRC*)key, (const SRC*)value, (unsigned char*)k_cache, (unsigned char*)v_cache,    \
+                     k_scales, v_scales, per_token, k_static, v_static, slots, Hkv, BS, num_slots)
+  const bool fp8 = kv_dtype == PA_FP8_E4M3;
+  if (src_dtype == PA_F32) {
+    if (fp8) { if (D == 64) PA_QUANT_LAUNCH(float, true, 1); else PA_QUANT_LAUNCH(float, true, 2); }
+    else { if (D == 64) PA_QUANT_LAUNCH(float, false, 1); else PA_QUANT_LAUNCH(float, false, 2); }
+  } else {
+    if (fp8) { if (D == 64) PA_QUANT_LAUNCH(__bf16, true, 1); else PA_QUANT_LAUNCH(__bf16, true, 2); }
+    else { if (D == 64) PA_QUANT_LAUNCH(__bf16, false, 1); else PA_QUANT_LAUNCH(__bf16, false, 2); }
+  }
+#undef PA_QUANT_LAUNCH
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PA_OK : hip_fail(e, "pa_quantize_and_cache launch");
 }
 
 }  // namespace pa

@@ -20,6 +20,8 @@
 // exceeds it by more than kRescaleThreshold (results are exact for any
 // reference; the threshold bounds weights by 2^8 and makes rescaling of
 // the accumulators rare).
+#include <type_traits>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -280,6 +282,26 @@ __device__ __forceinline__ u32x2_t i8x4_to_bf16x4(unsigned w) {
   return u32x2_t{__builtin_amdgcn_perm(f1, f0, 0x07060302u), __builtin_amdgcn_perm(f3, f2, 0x07060302u)};
 }
 
+// E4M3 -> bf16 for 4 consecutive codes packed in w: the hardware converts
+// two codes at a time to fp32 (OCP E4M3, exact), and every E4M3 value fits
+// bf16 exactly (3 mantissa bits, exponents 2^-9 .. 2^8), so the fp32's upper
+// half is the bf16.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2_t e4m3x4_to_bf16x4(unsigned w) {
+  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  return u32x2_t{__builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]), 0x07060302u),
+                 __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u)};
+}
+
+// Cache element kinds of the matrix-core kernel.
+constexpr int kKvBf16 = 0, kKvI8 = 1, kKvFp8 = 2;
+template <int KV>
+__device__ __forceinline__ u32x2_t codes_to_bf16x4(unsigned w) {
+  if constexpr (KV == kKvFp8) return e4m3x4_to_bf16x4(w);
+  else return i8x4_to_bf16x4(w);
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t w) { return __builtin_bit_cast(bf16x8_t, w); }
 __device__ __forceinline__ i16x4_t as_i16x4(unsigned a, unsigned b) {
   return __builtin_bit_cast(i16x4_t, u32x2_t{a, b});
@@ -316,7 +338,9 @@ __device__ __forceinline__ void mfma_item(int bid, int nblk, int Hkv, int nP, in
   }
 }
 
-template <bool I8, int BS>
+// KV: kKvBf16, kKvI8 or kKvFp8 cache; TOKSC: quantised cache with one scale
+// per token ([NB][Hkv][BS]) instead of one per (block, kv head).
+template <int KV, int BS, bool TOKSC>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(
     float* __restrict__ out, SplitK ws,
     const unsigned short* __restrict__ q, char* __restrict__ k_cache, char* __restrict__ v_cache,
@@ -324,7 +348,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     int max_blocks, const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int NB, float qk_log2,
     int P, int nP, const char* __restrict__ new_k, const char* __restrict__ new_v) {
   constexpr int D = 128;
+  constexpr bool I8 = KV != kKvBf16;  // 1-byte codes with fp32 scales
   constexpr int E = I8 ? 1 : 2;
+  // scales of a tile: the (block, head) scale, or the lane's four tokens'
+  using Sc = typename std::conditional<TOKSC, f32x4_t, float>::type;
   const int lane = threadIdx.x;
   const int j = lane >> 4;
   const int c = lane & 15;
@@ -412,7 +439,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       kr[i] = c * 16 + ((i * 4 + j) ^ c);            // read slot of d-chunk (i*4 + j), row c
     }
   }
-  auto tile_ptrs = [&](int ti, const char*& kb, const char*& vb, bool& ok, float& ks, float& vs) {
+  auto tile_ptrs = [&](int ti, const char*& kb, const char*& vb, bool& ok, Sc& ks, Sc& vs) {
     const int e = (ti * 16) / BS - tbl_base;
     int b = e < 64 ? __builtin_amdgcn_readlane(tbl0, e) : __builtin_amdgcn_readlane(tbl1, e - 64);
     ok = b >= 0 && b < NB;
@@ -420,7 +447,12 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     const size_t off = ((size_t)b * Hkv + g) * head_stride + (size_t)((ti * 16) % BS) * ROW;
     kb = k_cache + off;
     vb = v_cache + off;
-    if (I8) {
+    if constexpr (TOKSC) {
+      // tokens 4j .. 4j+3 of the tile: 16 aligned bytes of the scale row
+      const size_t si = ((size_t)b * Hkv + g) * BS + (size_t)((ti * 16) % BS) + 4 * j;
+      ks = *(const f32x4_t*)(k_scales + si);
+      vs = *(const f32x4_t*)(v_scales + si);
+    } else if (I8) {
       ks = k_scales[(size_t)b * Hkv + g];
       vs = v_scales[(size_t)b * Hkv + g];
     }
@@ -431,7 +463,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   for (int e = 0; e < 8; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
 
-  auto compute = [&](MfmaTile<I8>& T, int ti, bool ok, float ks, float vs) {
+  auto compute = [&](MfmaTile<I8>& T, int ti, bool ok, const Sc& ks, const Sc& vs) {
     const bool new_tile = owns_new && ti == (tnew >> 4);  // wave-uniform
     const int rnew = tnew & 15;
     if (I8) {
@@ -456,18 +488,22 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
         // lane holds d = 32j .. 32j+31 of row c: chunk 2j (kk 0, 1), 2j+1 (kk 2, 3)
         const u32x4_t chunk = ktile[kr[kk >> 1]];
         const unsigned w0 = chunk[(kk & 1) * 2], w1 = chunk[(kk & 1) * 2 + 1];
-        const u32x2_t lo = i8x4_to_bf16x4(w0), hi = i8x4_to_bf16x4(w1);
+        const u32x2_t lo = codes_to_bf16x4<KV>(w0), hi = codes_to_bf16x4<KV>(w1);
         a = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
       } else {
         a = as_bf16x8(ktile[kr[kk]]);
       }
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], sc, 0, 0, 0);
     }
-    const float xs = I8 ? qk_log2 * ks : qk_log2;
     const int tok0 = ti * 16 + 4 * j;
     float x[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = (ok && tok0 + r < t_end) ? sc[r] * xs : kNegInf;
+    for (int r = 0; r < 4; ++r) {
+      float xs = qk_log2;
+      if constexpr (TOKSC) xs *= ks[r];
+      else if (I8) xs *= ks;
+      x[r] = (ok && tok0 + r < t_end) ? sc[r] * xs : kNegInf;
+    }
     float mloc = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mloc = xor_max_rows(mloc);
     // ---- lazy rescale of the running reference
@@ -484,7 +520,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) pw[r] = x[r] == kNegInf ? 0.f : fast_exp2(x[r] - m_run);
     l_run += (pw[0] + pw[1]) + (pw[2] + pw[3]);
-    if (I8) {
+    if constexpr (TOKSC) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pw[r] *= vs[r];
+    } else if (I8) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) pw[r] *= vs;
     }
@@ -512,7 +551,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (I8) {
-        const u32x2_t a = i8x4_to_bf16x4(T.v[i][0]), b = i8x4_to_bf16x4(T.v[i][1]);
+        const u32x2_t a = codes_to_bf16x4<KV>(T.v[i][0]), b = codes_to_bf16x4<KV>(T.v[i][1]);
         vw[i][0] = a[0];
         vw[i][1] = a[1];
         vw[i][2] = b[0];
@@ -542,7 +581,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   MfmaTile<I8> A, B;
   const char *kA, *vA, *kB, *vB;
   bool okA, okB;
-  float ksA = 1.f, vsA = 1.f, ksB = 1.f, vsB = 1.f;
+  Sc ksA{}, vsA{}, ksB{}, vsB{};
   int ti = tile_begin;
   tile_ptrs(ti, kA, vA, okA, ksA, vsA);
   mfma_load_tile<I8>(A, kA, vA, koff, voff);
@@ -656,6 +695,37 @@ struct KvChunk<signed char, DC> {
   }
 };
 
+// Tag type of E4M3 cache elements (one byte each).
+struct E4M3 {
+  unsigned char bits;
+};
+
+template <int DC>
+struct KvChunk<E4M3, DC> {
+  static __device__ __forceinline__ void load(const char* p, float (&v)[DC]) {
+    if constexpr (DC == 8) {
+      u32x2_t w = ld8(p);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
+        const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
+        v[4 * k] = lo[0];
+        v[4 * k + 1] = lo[1];
+        v[4 * k + 2] = hi[0];
+        v[4 * k + 3] = hi[1];
+      }
+    } else {
+      const unsigned w = ld4(p);
+      const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+      const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+      v[0] = lo[0];
+      v[1] = lo[1];
+      v[2] = hi[0];
+      v[3] = hi[1];
+    }
+  }
+};
+
 template <typename QT, int DC>
 __device__ __forceinline__ void load_q(const QT* p, float (&v)[DC]) {
   if constexpr (sizeof(QT) == 4) {
@@ -674,7 +744,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
     char* __restrict__ k_cache, char* __restrict__ v_cache, const float* __restrict__ k_scales,
     const float* __restrict__ v_scales, const int32_t* __restrict__ tables, int max_blocks,
     const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int head_groups, int NB, float qk_log2,
-    int P, int nP, const char* __restrict__ new_k, const char* __restrict__ new_v) {
+    int P, int nP, const char* __restrict__ new_k, const char* __restrict__ new_v, int tok_scales) {
   constexpr int DC = D / 16;
   constexpr bool I8 = sizeof(KV) == 1;
   constexpr int E = sizeof(KV);
@@ -744,9 +814,18 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
     const bool ok = b >= 0 && b < NB;
     if (!ok) b = 0;
     const size_t off = ((size_t)b * Hkv + g) * head_stride;
-    const float ks = I8 ? k_scales[(size_t)b * Hkv + g] : 1.f;
-    const float vs = I8 ? v_scales[(size_t)b * Hkv + g] : 1.f;
     const int row0 = t4 % BS;
+    // scale of each of the lane's four tokens: per (block, head) or per token
+    float ksr[4], vsr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      ksr[r] = vsr[r] = 1.f;
+      if (I8) {
+        const size_t si = tok_scales ? ((size_t)b * Hkv + g) * BS + row0 + 4 * r + tt : (size_t)b * Hkv + g;
+        ksr[r] = k_scales[si];
+        vsr[r] = v_scales[si];
+      }
+    }
     float kv[4][DC], vv[4][DC];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -766,7 +845,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
 #pragma unroll
         for (int k = 0; k < DC; ++k) d = fmaf(qv[i][k], kv[r][k], d);
         d = row_sum16(d);
-        x[i] = valid ? d * ks : kNegInf;
+        x[i] = valid ? d * ksr[r] : kNegInf;
       }
       bool need = false;
 #pragma unroll
@@ -787,7 +866,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
       for (int i = 0; i < GT; ++i) {
         const float pw = valid ? fast_exp2(x[i] - m[i]) : 0.f;
         l[i] += pw;
-        const float pv = pw * vs;
+        const float pv = pw * vsr[r];
 #pragma unroll
         for (int k = 0; k < DC; ++k) acc[i][k] = fmaf(pv, valid ? vv[r][k] : 0.f, acc[i][k]);
       }
@@ -857,18 +936,28 @@ pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipSt
   if (items > 0x7fffffffu) return fail(PA_ERR_UNSUPPORTED, "pa_decode: grid too large");
   const float qk = a->scale * kLog2e;
   const SplitK ws = split_k(a, p);
-#define PA_MFMA_LAUNCH(I8, BS)                                                                                   \
-  hipLaunchKernelGGL((decode_mfma_kernel<I8, BS>), dim3((unsigned)items), dim3(64), 0, st, (float*)a->out, ws,  \
-                     (const unsigned short*)a->q, (char*)a->k_cache, (char*)a->v_cache,      \
+#define PA_MFMA_LAUNCH(KV, BS, TOKSC)                                                                           \
+  hipLaunchKernelGGL((decode_mfma_kernel<KV, BS, TOKSC>), dim3((unsigned)items), dim3(64), 0, st,               \
+                     (float*)a->out, ws, (const unsigned short*)a->q, (char*)a->k_cache, (char*)a->v_cache,      \
                      a->k_scales, a->v_scales, a->block_tables, a->max_blocks_per_seq, a->context_lens,        \
                      a->num_q_heads, a->num_kv_heads, p.G, a->num_blocks, qk, p.partition_tokens,              \
                      p.num_partitions, (const char*)a->new_key, (const char*)a->new_value)
-  const bool i8 = a->kv_dtype == PA_I8;
-  if (i8) {
-    if (a->block_size == 16) PA_MFMA_LAUNCH(true, 16); else PA_MFMA_LAUNCH(true, 32);
-  } else {
-    if (a->block_size == 16) PA_MFMA_LAUNCH(false, 16); else PA_MFMA_LAUNCH(false, 32);
+#define PA_MFMA_BS(KV, TOKSC)                              \
+  if (a->block_size == 16) PA_MFMA_LAUNCH(KV, 16, TOKSC); \
+  else PA_MFMA_LAUNCH(KV, 32, TOKSC)
+  const bool tok = a->kv_scale_mode == PA_SCALE_TOKEN;
+  switch (a->kv_dtype) {
+    case PA_I8:
+      if (tok) { PA_MFMA_BS(kKvI8, true); } else { PA_MFMA_BS(kKvI8, false); }
+      break;
+    case PA_FP8_E4M3:
+      if (tok) { PA_MFMA_BS(kKvFp8, true); } else { PA_MFMA_BS(kKvFp8, false); }
+      break;
+    default:
+      PA_MFMA_BS(kKvBf16, false);
+      break;
   }
+#undef PA_MFMA_BS
 #undef PA_MFMA_LAUNCH
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode (matrix-core kernel) launch");
@@ -882,7 +971,8 @@ static void valu_dispatch_g(const pa_decode_args* a, const DecodePlan& p, hipStr
                      ws, (const QT*)a->q, (char*)a->k_cache, (char*)a->v_cache, a->k_scales, \
                      a->v_scales, a->block_tables, a->max_blocks_per_seq, a->context_lens, a->num_q_heads,   \
                      a->num_kv_heads, p.G, p.head_groups, a->num_blocks, qk, p.partition_tokens,             \
-                     p.num_partitions, (const char*)a->new_key, (const char*)a->new_value)
+                     p.num_partitions, (const char*)a->new_key, (const char*)a->new_value,                \
+                     a->kv_scale_mode == PA_SCALE_TOKEN ? 1 : 0)
   switch (p.heads_per_wave) {
     case 1: PA_VALU_LAUNCH(1); break;
     case 2: PA_VALU_LAUNCH(2); break;
@@ -910,6 +1000,7 @@ static void valu_dispatch_kv(const pa_decode_args* a, const DecodePlan& p, hipSt
   switch (a->kv_dtype) {
     case PA_F32: valu_dispatch_shape<QT, float>(a, p, st, items, ws, qk); break;
     case PA_BF16: valu_dispatch_shape<QT, __bf16>(a, p, st, items, ws, qk); break;
+    case PA_FP8_E4M3: valu_dispatch_shape<QT, E4M3>(a, p, st, items, ws, qk); break;
     default: valu_dispatch_shape<QT, signed char>(a, p, st, items, ws, qk); break;
   }
 }

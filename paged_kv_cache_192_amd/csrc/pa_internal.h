@@ -20,8 +20,17 @@ inline int dtype_bytes(pa_dtype t) {
     case PA_F32: return 4;
     case PA_BF16: return 2;
     case PA_I8: return 1;
+    case PA_FP8_E4M3: return 1;
   }
   return 0;
+}
+
+// int8 and E4M3 caches carry fp32 scales.
+inline bool quantised(pa_dtype t) { return t == PA_I8 || t == PA_FP8_E4M3; }
+
+// fp32 scales per physical block (all kv heads) in a scale layout.
+inline int64_t scales_per_block(int32_t mode, int32_t Hkv, int32_t BS) {
+  return mode == PA_SCALE_TOKEN ? (int64_t)Hkv * BS : (int64_t)Hkv;
 }
 
 // ---- decode planning -----------------------------------------------------
@@ -82,8 +91,15 @@ pa_status launch_slot_mapping(const int32_t* block_tables, int32_t max_blocks, i
 pa_status launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                    int elem_bytes, const int64_t* slots, int32_t T, int32_t Hkv,
                                    int32_t D, int32_t BS, int32_t NB, hipStream_t st);
-pa_status launch_copy_blocks(void* k_cache, void* v_cache, int elem_bytes, float* k_scales,
-                             float* v_scales, const int64_t* pairs, int32_t P, int32_t Hkv, int32_t D,
-                             int32_t BS, int32_t NB, hipStream_t st);
+// Whole-block copies from pool `src` to pool `dst` (the same pool for
+// copy-on-write); scales_per_blk fp32 scales follow each block when given.
+pa_status launch_block_copy(const void* src_k, const void* src_v, const float* src_ks, const float* src_vs,
+                            void* dst_k, void* dst_v, float* dst_ks, float* dst_vs, int64_t block_bytes,
+                            int64_t scales_per_blk, const int64_t* pairs, int32_t P, int32_t src_NB,
+                            int32_t dst_NB, hipStream_t st);
+pa_status launch_quantize_and_cache(const void* key, const void* value, pa_dtype src_dtype, void* k_cache,
+                                    void* v_cache, pa_dtype kv_dtype, float* k_scales, float* v_scales,
+                                    int32_t scale_mode, float k_static, float v_static, const int64_t* slots,
+                                    int32_t T, int32_t Hkv, int32_t D, int32_t BS, int32_t NB, hipStream_t st);
 
 }  // namespace pa

@@ -24,11 +24,12 @@ from typing import Dict, List, Optional
 
 import numpy as np
 
-F32, BF16, I8 = "f32", "bf16", "i8"
+F32, BF16, I8, FP8 = "f32", "bf16", "i8", "fp8"   # fp8: OCP E4M3 codes held as uint8
 
 BF16_NAN = np.uint16(0x7FC0)
 F32_NAN = np.float32("nan")
 I8_POISON = np.int8(127)
+FP8_POISON = np.uint8(0x7F)   # the E4M3 NaN code
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -84,7 +85,7 @@ def _values(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
 
 
 def _poison_value(dtype: str):
-    return {F32: F32_NAN, BF16: BF16_NAN, I8: I8_POISON}[dtype]
+    return {F32: F32_NAN, BF16: BF16_NAN, I8: I8_POISON, FP8: FP8_POISON}[dtype]
 
 
 def assign_tables(rng: np.random.Generator, num_blocks: int, blocks_per_seq: List[int],
@@ -125,9 +126,10 @@ def make_case(name: str, seed: int, context_lens, num_q_heads: int, num_kv_heads
               q_dtype: str = BF16, kv_dtype: str = BF16, scale: Optional[float] = None,
               poison: bool = True, free_frac: float = 0.0, max_blocks: Optional[int] = None
               ) -> DecodeCase:
-    """Generic seeded decode batch.  For int8 caches the fp32 samples are
-    returned in ``extra['k_f32']``/``extra['v_f32']`` with zero codes; the
-    caller quantises them (the quantiser is not input generation)."""
+    """Generic seeded decode batch.  For int8 and E4M3 caches the fp32
+    samples are returned in ``extra['k_f32']``/``extra['v_f32']`` with zero
+    codes; the caller quantises them (the quantiser is not input
+    generation)."""
     rng = np.random.default_rng(seed)
     cl = np.asarray(context_lens, dtype=np.int32)
     S = cl.shape[0]
@@ -138,15 +140,15 @@ def make_case(name: str, seed: int, context_lens, num_q_heads: int, num_kv_heads
     shape = (NB, num_kv_heads, block_size, head_dim)
     q = _values(rng, (S, num_q_heads, head_dim), q_dtype)
     extra: Dict[str, object] = {}
-    if kv_dtype == I8:
+    if kv_dtype in (I8, FP8):
         extra["k_f32"] = rng.standard_normal(shape, dtype=np.float32)
         extra["v_f32"] = rng.standard_normal(shape, dtype=np.float32)
-        k = np.zeros(shape, np.int8)
-        v = np.zeros(shape, np.int8)
+        k = np.zeros(shape, np.int8 if kv_dtype == I8 else np.uint8)
+        v = np.zeros_like(k)
     else:
         k = _values(rng, shape, kv_dtype)
         v = _values(rng, shape, kv_dtype)
-    if poison and kv_dtype != I8:
+    if poison and kv_dtype not in (I8, FP8):
         poison_unused(k, tables, cl, free, kv_dtype)
         poison_unused(v, tables, cl, free, kv_dtype)
     sc = np.float32(1.0 / math.sqrt(head_dim)) if scale is None else np.float32(scale)
@@ -344,12 +346,37 @@ def config5() -> DecodeCase:
                      poison=False)
 
 
-def random_int8_cache(case: DecodeCase, seed: int = 0) -> None:
+def random_int8_cache(case: DecodeCase, seed: int = 0, per_token: bool = False) -> None:
     """Fill an int8 case with random codes in [-127, 127] and positive fp32
-    scales (timing inputs; parity tests quantise fp32 samples instead)."""
+    scales, per (block, head) or per token (timing inputs; parity tests
+    quantise fp32 samples instead)."""
     rng = np.random.default_rng(seed)
     shape = case.k_cache.shape
     case.k_cache = rng.integers(-127, 128, shape).astype(np.int8)
     case.v_cache = rng.integers(-127, 128, shape).astype(np.int8)
-    case.k_scales = (rng.random((case.num_blocks, case.num_kv_heads)) * 0.03 + 0.005).astype(np.float32)
-    case.v_scales = (rng.random((case.num_blocks, case.num_kv_heads)) * 0.03 + 0.005).astype(np.float32)
+    sshape = shape[:3] if per_token else shape[:2]
+    case.k_scales = (rng.random(sshape) * 0.03 + 0.005).astype(np.float32)
+    case.v_scales = (rng.random(sshape) * 0.03 + 0.005).astype(np.float32)
+
+
+def random_fp8_cache(case: DecodeCase, seed: int = 0, per_token: bool = False) -> None:
+    """Fill a case with random finite E4M3 codes (exponent field 0..14) and
+    positive fp32 scales (timing inputs)."""
+    rng = np.random.default_rng(seed)
+    shape = case.k_cache.shape
+    case.k_cache = rng.integers(0, 256, shape).astype(np.uint8) & np.uint8(0xF7)
+    case.v_cache = rng.integers(0, 256, shape).astype(np.uint8) & np.uint8(0xF7)
+    case.kv_dtype = FP8
+    sshape = shape[:3] if per_token else shape[:2]
+    case.k_scales = (rng.random(sshape) * 0.01 + 0.002).astype(np.float32)
+    case.v_scales = (rng.random(sshape) * 0.01 + 0.002).astype(np.float32)
+
+
+def token_slots(case: DecodeCase) -> np.ndarray:
+    """int64[sum n_s]: the slot of every cached token, sequence by sequence."""
+    BS = case.block_size
+    out = []
+    for s, n in enumerate(case.context_lens):
+        for t in range(int(n)):
+            out.append(int(case.block_tables[s, t // BS]) * BS + t % BS)
+    return np.asarray(out, np.int64)

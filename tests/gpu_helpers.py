@@ -26,18 +26,24 @@ def say(*a):
 
 
 def to_dev(a: np.ndarray) -> torch.Tensor:
-    """numpy -> device tensor; uint16 arrays are bfloat16 bit patterns."""
+    """numpy -> device tensor; uint16 arrays are bfloat16 bit patterns and
+    uint8 arrays E4M3 codes."""
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    if a.dtype == np.uint8:
+        return torch.from_numpy(a).to(DEV).view(torch.float8_e4m3fn)
     return torch.from_numpy(a).to(DEV)
 
 
 def to_host(t: torch.Tensor) -> np.ndarray:
-    """device tensor -> numpy; bfloat16 comes back as uint16 bits."""
+    """device tensor -> numpy; bfloat16 comes back as uint16 bits, E4M3 as
+    uint8 codes."""
     t = t.detach().contiguous().cpu()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16).copy()
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy().copy()
     return t.numpy().copy()
 
 
@@ -57,6 +63,28 @@ def quantize_case(case: synth.DecodeCase) -> None:
     case.v_cache, case.v_scales = oracle.quantize_int8(case.extra["v_f32"], valid)
     synth.poison_unused(case.k_cache, case.block_tables, case.context_lens, case.free_blocks, synth.I8)
     synth.poison_unused(case.v_cache, case.block_tables, case.context_lens, case.free_blocks, synth.I8)
+
+
+def quantize_case_by_token(case: synth.DecodeCase, scale_mode: int, static=(0.03, 0.03)) -> None:
+    """int8 / E4M3 cases: every cached token's fp32 row quantised by the
+    oracle's quantising write, per token (dynamic) or with static per-layer
+    scales; unused slots keep poison codes and scales."""
+    slots = synth.token_slots(case)
+    NB, Hkv, BS, D = case.k_cache.shape
+    kf = case.extra["k_f32"]
+    vf = case.extra["v_f32"]
+    # the fp32 row of each token, in slot order
+    key = np.stack([kf[sl // BS, :, sl % BS, :] for sl in slots]) if len(slots) else np.zeros((0, Hkv, D), np.float32)
+    val = np.stack([vf[sl // BS, :, sl % BS, :] for sl in slots]) if len(slots) else np.zeros((0, Hkv, D), np.float32)
+    dt = np.int8 if case.kv_dtype == synth.I8 else np.uint8
+    case.k_cache = np.full(case.k_cache.shape, synth._poison_value(case.kv_dtype), dt)
+    case.v_cache = case.k_cache.copy()
+    sshape = oracle.scale_shape(NB, Hkv, BS, scale_mode)
+    case.k_scales = np.full(sshape, 1e30, np.float32)
+    case.v_scales = np.full(sshape, 1e30, np.float32)
+    if len(slots):
+        oracle.quantize_and_cache(key, val, case.k_cache, case.v_cache, case.k_scales, case.v_scales, slots,
+                                  scale_mode, static[0], static[1])
 
 
 def run_decode(case: synth.DecodeCase, dev=None, partition_tokens=0, kernel=0, max_context_len=None,

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
     assert len(names) >= 16, names
     for n in names:
         assert hasattr(lib, n), "libpa.so does not export %s" % n
-    assert lib.pa_abi_version() == pa.ABI_VERSION == 3
+    assert lib.pa_abi_version() == pa.ABI_VERSION == 4
 
 
 def test_status_strings():
@@ -121,6 +121,7 @@ def test_partition_plan_follows_the_length_hint():
     ("num_seqs", -1, pa.PA_ERR_INVALID),
     ("total_context_len", -1, pa.PA_ERR_INVALID),
     ("total_context_len", 301, pa.PA_ERR_INVALID),    # > 3 seqs x 100
+    ("kv_dtype", pa.PA_FP8_E4M3, pa.PA_ERR_INVALID),  # E4M3 without scales
 ])
 def test_decode_rejects_bad_arguments(field, value, status):
     a = _cpu_args(**{field: value})
@@ -162,19 +163,48 @@ def test_zero_sequences_is_a_no_op():
 def test_cache_ops_reject_bad_arguments():
     lib = pa.library()
     P = 0x10000
-    # reshape: int8 is not built, bad shapes, misalignment
+    # reshape: quantised caches go through pa_quantize_and_cache; bad shapes, misalignment
     assert lib.pa_reshape_and_cache(P, P, P, P, pa.PA_I8, P, 1, 8, 128, 16, 10, None) == pa.PA_ERR_UNSUPPORTED
+    assert lib.pa_reshape_and_cache(P, P, P, P, pa.PA_FP8_E4M3, P, 1, 8, 128, 16, 10, None) == pa.PA_ERR_UNSUPPORTED
     assert lib.pa_reshape_and_cache(P, P, P, P, pa.PA_BF16, P, 1, 8, 96, 16, 10, None) == pa.PA_ERR_INVALID
     assert lib.pa_reshape_and_cache(P, P, P, P, pa.PA_BF16, P, 1, 8, 128, 12, 10, None) == pa.PA_ERR_INVALID
     assert lib.pa_reshape_and_cache(P, P, P, P, pa.PA_BF16, P, -1, 8, 128, 16, 10, None) == pa.PA_ERR_INVALID
     assert lib.pa_reshape_and_cache(P + 4, P, P, P, pa.PA_BF16, P, 1, 8, 128, 16, 10, None) == pa.PA_ERR_INVALID
     assert lib.pa_reshape_and_cache(None, P, P, P, pa.PA_BF16, P, 1, 8, 128, 16, 10, None) == pa.PA_ERR_INVALID
     assert lib.pa_reshape_and_cache(None, None, None, None, pa.PA_BF16, None, 0, 8, 128, 16, 10, None) == pa.PA_OK
-    # copy: scales exactly for int8
-    assert lib.pa_copy_blocks(P, P, pa.PA_BF16, P, P, P, 1, 8, 128, 16, 10, None) == pa.PA_ERR_INVALID
-    assert lib.pa_copy_blocks(P, P, pa.PA_I8, None, None, P, 1, 8, 128, 16, 10, None) == pa.PA_ERR_INVALID
-    assert lib.pa_copy_blocks(P, P, pa.PA_BF16, None, None, P, -2, 8, 128, 16, 10, None) == pa.PA_ERR_INVALID
-    assert lib.pa_copy_blocks(P, P, pa.PA_BF16, None, None, None, 0, 8, 128, 16, 10, None) == pa.PA_OK
+    # copy: scales exactly for quantised caches, a known scale layout
+    B, T = pa.PA_SCALE_BLOCK, pa.PA_SCALE_TOKEN
+    assert lib.pa_copy_blocks(P, P, pa.PA_BF16, P, P, B, P, 1, 8, 128, 16, 10, None) == pa.PA_ERR_INVALID
+    assert lib.pa_copy_blocks(P, P, pa.PA_I8, None, None, B, P, 1, 8, 128, 16, 10, None) == pa.PA_ERR_INVALID
+    assert lib.pa_copy_blocks(P, P, pa.PA_FP8_E4M3, None, None, T, P, 1, 8, 128, 16, 10, None) == pa.PA_ERR_INVALID
+    assert lib.pa_copy_blocks(P, P, pa.PA_I8, P, P, 7, P, 1, 8, 128, 16, 10, None) == pa.PA_ERR_INVALID
+    assert lib.pa_copy_blocks(P, P, pa.PA_BF16, None, None, B, P, -2, 8, 128, 16, 10, None) == pa.PA_ERR_INVALID
+    assert lib.pa_copy_blocks(P, P, pa.PA_BF16, None, None, B, None, 0, 8, 128, 16, 10, None) == pa.PA_OK
+    assert lib.pa_copy_blocks(P, P, pa.PA_I8, P, P, T, None, 0, 8, 128, 16, 10, None) == pa.PA_OK
+    # swap: scales all or none and only for quantised pools; pool ids; empty is fine
+    sw = lib.pa_swap_blocks
+    assert sw(P, P, P, None, P, P, P, P, pa.PA_I8, B, P, 1, 8, 128, 16, 10, 10, None) == pa.PA_ERR_INVALID
+    assert sw(P, P, P, P, P, P, P, P, pa.PA_BF16, B, P, 1, 8, 128, 16, 10, 10, None) == pa.PA_ERR_INVALID
+    assert sw(P, P, P, P, P, P, P, P, pa.PA_I8, 5, P, 1, 8, 128, 16, 10, 10, None) == pa.PA_ERR_INVALID
+    assert sw(P, P, None, None, P, P, None, None, pa.PA_BF16, B, P, 1, 8, 128, 16, 0, 10, None) == pa.PA_ERR_INVALID
+    assert sw(P, P, None, None, P, P, None, None, pa.PA_BF16, B, P, -1, 8, 128, 16, 4, 10, None) == pa.PA_ERR_INVALID
+    assert sw(P + 8, P, None, None, P, P, None, None, pa.PA_BF16, B, P, 1, 8, 128, 16, 4, 10, None) == \
+        pa.PA_ERR_INVALID
+    assert sw(None, None, None, None, None, None, None, None, pa.PA_BF16, B, None, 0, 8, 128, 16, 4, 10, None) == pa.PA_OK
+    # quantising write: quantised cache, fp32/bf16 source, valid static scales
+    qc = lib.pa_quantize_and_cache
+    assert qc(P, P, pa.PA_BF16, P, P, pa.PA_BF16, P, P, T, 0.0, 0.0, P, 1, 8, 128, 16, 10, None) == pa.PA_ERR_INVALID
+    assert qc(P, P, pa.PA_I8, P, P, pa.PA_I8, P, P, T, 0.0, 0.0, P, 1, 8, 128, 16, 10, None) == pa.PA_ERR_INVALID
+    assert qc(P, P, pa.PA_BF16, P, P, pa.PA_I8, P, P, B, 0.0, 1.0, P, 1, 8, 128, 16, 10, None) == pa.PA_ERR_INVALID
+    assert qc(P, P, pa.PA_BF16, P, P, pa.PA_I8, P, P, B, 1.0, float("inf"), P, 1, 8, 128, 16, 10, None) == \
+        pa.PA_ERR_INVALID
+    assert qc(P, P, pa.PA_BF16, P, P, pa.PA_I8, P, P, 3, 1.0, 1.0, P, 1, 8, 128, 16, 10, None) == pa.PA_ERR_INVALID
+    assert qc(P, P, pa.PA_BF16, P, P, pa.PA_I8, None, P, T, 0.0, 0.0, P, 1, 8, 128, 16, 10, None) == \
+        pa.PA_ERR_INVALID
+    assert qc(P, P, pa.PA_F32, P, P, pa.PA_FP8_E4M3, P, P, T, 0.0, 0.0, P, 1, 8, 96, 16, 10, None) == \
+        pa.PA_ERR_INVALID
+    assert qc(None, None, pa.PA_F32, None, None, pa.PA_FP8_E4M3, None, None, T, 0.0, 0.0, None, 0, 8, 128, 16, 10,
+              None) == pa.PA_OK
     # slot mapping: exactly one of positions / context_lens
     assert lib.pa_slot_mapping(P, 4, 2, None, P, P, 2, 16, P, None) == pa.PA_ERR_INVALID
     assert lib.pa_slot_mapping(P, 4, 2, None, None, None, 2, 16, P, None) == pa.PA_ERR_INVALID
