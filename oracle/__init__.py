@@ -75,6 +75,9 @@ def _bind(lib):
     lib.oracle_paged_decode.argtypes = [P, P, i32, P, P, i32, P, P, i32, P, i32, P,
                                         i32, i32, i32, i32, i32, i32, ctypes.c_double]
     lib.oracle_paged_decode.restype = i32
+    lib.oracle_paged_attention.argtypes = [P, P, i32, P, P, i32, P, P, i32, P, i32, P, P,
+                                           i32, i32, i32, i32, i32, i32, ctypes.c_double]
+    lib.oracle_paged_attention.restype = i32
     lib.oracle_fp8_e4m3_value.argtypes = [ctypes.c_uint8]
     lib.oracle_fp8_e4m3_value.restype = ctypes.c_double
     lib.oracle_fp8_e4m3_encode.argtypes = [ctypes.c_float]
@@ -214,6 +217,39 @@ def paged_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                                  _ptr(cl), S, Hq, Hkv, D, BS, NB, float(scale))
     if rc != 0:
         raise ValueError("oracle_paged_decode: a table entry or context length is out of range")
+    return out
+
+
+def paged_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                    block_tables: np.ndarray, context_lens: np.ndarray, query_start_loc: np.ndarray,
+                    scale: float, k_scales: Optional[np.ndarray] = None, v_scales: Optional[np.ndarray] = None,
+                    scale_mode: int = SCALE_BLOCK) -> np.ndarray:
+    """fp64 paged attention with several causal query rows per sequence,
+    ``out[R][Hq][D]``; ``q [R][Hq][D]``, ``query_start_loc int32[S+1]`` from
+    0 to R: the rows of sequence s are its last L_s tokens."""
+    lib = _load()
+    q = np.ascontiguousarray(q)
+    k_cache = np.ascontiguousarray(k_cache)
+    v_cache = np.ascontiguousarray(v_cache)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    qsl = np.ascontiguousarray(query_start_loc, dtype=np.int32)
+    R, Hq, D = q.shape
+    NB, Hkv, BS, _ = k_cache.shape
+    S = cl.shape[0]
+    assert qsl.shape == (S + 1,) and qsl[0] == 0 and qsl[-1] == R
+    kv = _code(k_cache)
+    if kv in (I8, FP8):
+        k_scales = np.ascontiguousarray(k_scales, dtype=np.float32)
+        v_scales = np.ascontiguousarray(v_scales, dtype=np.float32)
+    else:
+        k_scales = v_scales = None
+    out = np.zeros((R, Hq, D), dtype=np.float64)
+    rc = lib.oracle_paged_attention(_ptr(out), _ptr(q), _code(q), _ptr(k_cache), _ptr(v_cache), kv,
+                                    _ptr(k_scales), _ptr(v_scales), int(scale_mode), _ptr(bt), bt.shape[1],
+                                    _ptr(cl), _ptr(qsl), S, Hq, Hkv, D, BS, NB, float(scale))
+    if rc != 0:
+        raise ValueError("oracle_paged_attention: bad table entry, length or offsets")
     return out
 
 

@@ -148,33 +148,57 @@ static double kv_value(const void* cache, const float* scales, int dtype,
 /* ---- decode attention -------------------------------------------------- */
 
 /*
- * out[s][h][:] = sum_t softmax_t(scale * <q[s][h], K_s[t]>) * V_s[t]
- * over t = 0 .. context_lens[s]-1, with query head h reading KV head
- * h / (Hq / Hkv) (grouped-query heads in contiguous groups).  A sequence of
- * context length 0 gets a row of zeros.  All arithmetic in double; exp()
- * from libm.
+ * out[r][h][:] = sum_t softmax_t(scale * <q[r][h], K_s[t]>) * V_s[t]
+ * with query head h reading KV head h / (Hq / Hkv) (grouped-query heads in
+ * contiguous groups).
  *
- * Returns 0, or -1 if some table entry a sequence needs is outside
- * [0, NB) or a context length exceeds max_blocks * BS (nothing is read out
- * of bounds in that case; out is left partially written).
+ * Decode (query_start_loc NULL): one query row per sequence, r = s, over
+ * t = 0 .. context_lens[s]-1.
+ * Several query rows per sequence (query_start_loc non-NULL, S + 1
+ * offsets from 0): rows query_start_loc[s] .. query_start_loc[s+1]-1 are the last
+ * L = query_start_loc[s+1] - query_start_loc[s] tokens of sequence s, whose
+ * context length n counts them; row i of them sits at position n - L + i
+ * and attends causally to t = 0 .. n - L + i (chunked prefill, and the
+ * checking of several drafted tokens in one pass: "Cache KV en
+ * production", section "Les leviers"; forum thread, answer on chunked
+ * prefill).  A row with nothing to attend to gets zeros.
+ *
+ * All arithmetic in double; exp() from libm.  Returns 0, or -1 if some
+ * table entry a sequence needs is outside [0, NB), a context length exceeds
+ * max_blocks * BS, or the offsets do not start at 0 or decrease (nothing is read out of bounds
+ * in that case; out is left partially written).
  */
-int oracle_paged_decode(double* out, const void* q, int q_dtype,
-                        const void* k_cache, const void* v_cache, int kv_dtype,
-                        const float* k_scales, const float* v_scales,
-                        int scale_mode, const int32_t* block_tables, int max_blocks,
-                        const int32_t* context_lens, int S, int Hq, int Hkv,
-                        int D, int BS, int NB, double scale) {
+int oracle_paged_attention(double* out, const void* q, int q_dtype,
+                           const void* k_cache, const void* v_cache, int kv_dtype,
+                           const float* k_scales, const float* v_scales,
+                           int scale_mode, const int32_t* block_tables, int max_blocks,
+                           const int32_t* context_lens, const int32_t* query_start_loc,
+                           int S, int Hq, int Hkv, int D, int BS, int NB, double scale) {
   int G, bad = 0;
-  int64_t row;
+  int64_t row, R;
   if (S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || BS <= 0 || Hq % Hkv) return -1;
   G = Hq / Hkv;
-  for (int s = 0; s < S; ++s)
+  if (query_start_loc && query_start_loc[0] != 0) return -1;
+  for (int s = 0; s < S; ++s) {
     if (context_lens[s] < 0 || context_lens[s] > (int64_t)max_blocks * BS) return -1;
+    if (query_start_loc && query_start_loc[s + 1] < query_start_loc[s]) return -1;
+  }
+  R = query_start_loc ? (int64_t)query_start_loc[S] : S;
 
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
-  for (row = 0; row < (int64_t)S * Hq; ++row) {
-    int s = (int)(row / Hq), h = (int)(row % Hq), g = h / G;
-    int n = context_lens[s];
+  for (row = 0; row < R * Hq; ++row) {
+    int r = (int)(row / Hq), h = (int)(row % Hq), g = h / G;
+    int s = r, n, L = 1, i = 0;
+    if (query_start_loc) { /* the sequence holding query row r */
+      s = 0;
+      while (query_start_loc[s + 1] <= r) ++s;
+      L = query_start_loc[s + 1] - query_start_loc[s];
+      i = r - query_start_loc[s];
+    }
+    /* tokens visible to this row: positions 0 .. n - L + i */
+    n = context_lens[s] - L + i + 1;
+    if (n > context_lens[s]) n = context_lens[s];
+    if (n < 0) n = 0;
     const int64_t qoff = row * D;
     double* o = out + row * D;
     double* x;
@@ -208,6 +232,17 @@ int oracle_paged_decode(double* out, const void* q, int q_dtype,
     free(x);
   }
   return bad ? -1 : 0;
+}
+
+/* Decode: one query row per sequence. */
+int oracle_paged_decode(double* out, const void* q, int q_dtype,
+                        const void* k_cache, const void* v_cache, int kv_dtype,
+                        const float* k_scales, const float* v_scales,
+                        int scale_mode, const int32_t* block_tables, int max_blocks,
+                        const int32_t* context_lens, int S, int Hq, int Hkv,
+                        int D, int BS, int NB, double scale) {
+  return oracle_paged_attention(out, q, q_dtype, k_cache, v_cache, kv_dtype, k_scales, v_scales, scale_mode,
+                                block_tables, max_blocks, context_lens, NULL, S, Hq, Hkv, D, BS, NB, scale);
 }
 
 /* ---- slot mapping -------------------------------------------------------- */

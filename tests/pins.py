@@ -648,6 +648,54 @@ def pin_swap_blocks_exact():
     assert np.array_equal(ks[3], ks0[1]) and np.array_equal(ks[:3], ks0[:3])
 
 
+# --------------------------------------------------------------------------
+# several causal query rows per sequence
+# --------------------------------------------------------------------------
+
+def pin_multi_query_closed_forms():
+    """Three cached tokens, the last two of them queries (k_t = t e0, v_t =
+    e_t, q = e0, scale 1): the first query row sits at position 1 and sees
+    logits (0, 1); the second sees (0, 1, 2).  A one-token sequence before
+    it (one query row, context 1) returns its v0."""
+    g = golden("attention_closed_forms.json")
+    D, BS = 64, 2
+    K = np.stack([t * unit(D, 0) for t in range(3)])[:, None, :]
+    V = np.stack([unit(D, t) for t in range(3)])[:, None, :]
+    K0 = np.zeros((1, 1, D), np.float32)
+    V0 = (3.0 * unit(D, 5))[None, None, :]
+    kc, bt = paginate([K0, K], BS, 5, tables=np.array([[4, -1], [3, 1]]), fill=np.nan)
+    vc, _ = paginate([V0, V], BS, 5, tables=bt, fill=np.nan)
+    q = np.stack([unit(D, 0), unit(D, 0), unit(D, 0)])[:, None, :]
+    out = oracle.paged_attention(q, kc, vc, bt, np.array([1, 3], np.int32), np.array([0, 1, 3], np.int32), 1.0)
+    assert out[0, 0, 5] == 3.0 and np.count_nonzero(out[0, 0]) == 1
+    assert abs(out[1, 0, 0] - g["ctx2"]["out_d0"]) < 1e-15 and abs(out[1, 0, 1] - g["ctx2"]["out_d1"]) < 1e-15
+    assert np.all(out[1, 0, 2:] == 0.0)
+    assert np.max(np.abs(out[2, 0, :3] - np.array(g["ctx3"]["out"]))) < 1e-15
+
+
+def pin_multi_query_rows_are_prefix_decodes():
+    """Row i of a sequence with L query rows and context n is the one-query
+    decode of the same sequence cut to n - L + i + 1 tokens (rows that see
+    nothing are zero), for every row of a random batch."""
+    rng = np.random.default_rng(48)
+    lens = [5, 17, 33, 3]
+    qlens = [1, 4, 16, 5]            # the last sequence has more rows than tokens
+    Hq, Hkv, D, BS, NB = 4, 2, 32, 16, 12
+    ks = [rng.standard_normal((n, Hkv, D)).astype(np.float32) for n in lens]
+    vs = [rng.standard_normal((n, Hkv, D)).astype(np.float32) for n in lens]
+    kc, bt = paginate(ks, BS, NB, rng=rng)
+    vc, _ = paginate(vs, BS, NB, tables=bt)
+    qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = rng.standard_normal((int(qsl[-1]), Hq, D)).astype(np.float32)
+    out = oracle.paged_attention(q, kc, vc, bt, np.array(lens, np.int32), qsl, 0.25)
+    for s, (n, L) in enumerate(zip(lens, qlens)):
+        for i in range(L):
+            r = int(qsl[s]) + i
+            m = max(0, n - L + i + 1)
+            one = oracle.paged_decode(q[r:r + 1], kc, vc, bt[s:s + 1], np.array([m], np.int32), 0.25)
+            assert np.array_equal(out[r], one[0]), (s, i)
+
+
 QUANT_PINS = [pin_fp8_format_values, pin_fp8_encode, pin_per_token_scales_closed_form,
               pin_quantised_decode_matches_contiguous, pin_quantising_write_hand_values,
               pin_quantising_write_round_trip, pin_swap_blocks_exact]
@@ -656,4 +704,6 @@ CACHE_PINS = [pin_slot_mapping_figure, pin_slot_mapping_edges,
               pin_reshape_writes_exactly_one_slot_per_token, pin_copy_blocks_exact,
               pin_quantiser_hand_values, pin_quantiser_invariants]
 
-ALL_PINS = DECODE_PINS + CACHE_PINS + QUANT_PINS
+MULTI_QUERY_PINS = [pin_multi_query_closed_forms, pin_multi_query_rows_are_prefix_decodes]
+
+ALL_PINS = DECODE_PINS + CACHE_PINS + QUANT_PINS + MULTI_QUERY_PINS

@@ -56,6 +56,10 @@ MUTANTS = [
     ("swap copies V from the K pool",
      "memcpy(dst_v + dst * block_bytes, src_v + src * block_bytes",
      "memcpy(dst_v + dst * block_bytes, src_k + src * block_bytes"),
+    ("causal limit one token short", "n = context_lens[s] - L + i + 1;", "n = context_lens[s] - L + i;"),
+    ("query row found in the next sequence", "while (query_start_loc[s + 1] <= r) ++s;",
+     "while (query_start_loc[s + 1] < r) ++s;"),
+    ("query rows counted from the chunk's end", "i = r - query_start_loc[s];", "i = query_start_loc[s + 1] - 1 - r;"),
     ("swap skips the destination scales",
      "for (int64_t i = 0; i < nsc; ++i) dst_ks[dst * nsc + i] = src_ks[src * nsc + i];", ""),
     ("quantiser truncates", "r = rintf(x[i] / s);", "r = truncf(x[i] / s);"),
