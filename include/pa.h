@@ -73,7 +73,7 @@ const char* pa_status_string(pa_status s);
 /* Message of the last failure on the calling thread ("" if none). */
 const char* pa_last_error(void);
 /* ABI version of this header (incremented on any incompatible change). */
-#define PA_ABI_VERSION 4
+#define PA_ABI_VERSION 5
 int32_t pa_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -139,6 +139,19 @@ int32_t pa_abi_version(void);
  * max_context_len.  Not available for quantised caches (PA_ERR_UNSUPPORTED):
  * write them with pa_quantize_and_cache first.
  *
+ * Several query rows per sequence (chunked prefill, or checking several
+ * drafted tokens in one pass: "Cache KV en production", section "Les
+ * leviers"; forum thread, answer on chunked prefill): with query_start_loc
+ * (device int32 [num_seqs + 1], 0 = query_start_loc[0] <= ... <=
+ * query_start_loc[num_seqs] = num_queries), q and out are
+ * [num_queries][num_q_heads][head_dim] and rows query_start_loc[s] ..
+ * query_start_loc[s+1]-1 are the last L_s tokens of sequence s, already in
+ * the cache and counted in context_lens[s] = n.  Row i of them sits at
+ * position n - L_s + i and attends causally to positions 0 .. n - L_s + i
+ * (a row that would see no token gets zeros).  max_query_len (host) bounds
+ * L_s.  Matrix-core kernel only (bf16 queries, head_dim 128); no fused
+ * cache write.
+ *
  * `kernel` selects the implementation: 0 = automatic, 1 = vector-ALU
  * kernel (any supported case), 2 = matrix-core kernel (bf16, int8 or E4M3
  * caches with bf16 queries, head_dim 128, 1..16 query heads per kv head;
@@ -176,6 +189,9 @@ typedef struct {
   const void* new_value;
   int64_t total_context_len;     /* optional hint: sum of context_lens (0 = unknown), 0 <= it <= num_seqs * max_context_len */
   int32_t kv_scale_mode;         /* pa_scale_mode of k/v_scales (quantised caches; else ignored) */
+  const int32_t* query_start_loc; /* NULL = one query row per sequence; else [num_seqs + 1] row offsets */
+  int32_t num_queries;           /* with query_start_loc: total query rows (= query_start_loc[num_seqs]) */
+  int32_t max_query_len;         /* with query_start_loc: host bound on the rows of one sequence, >= 1 */
 } pa_decode_args;
 
 /* Host only: bytes of workspace pa_decode needs for these arguments

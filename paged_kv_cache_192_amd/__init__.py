@@ -21,7 +21,7 @@ PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_OOM, PA_ERR_STATE, PA_ERR_HIP 
 PA_F32, PA_BF16, PA_I8, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_SCALE_BLOCK, PA_SCALE_TOKEN = 0, 1
 KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_OOM",
                 4: "PA_ERR_STATE", 5: "PA_ERR_HIP"}
@@ -68,6 +68,9 @@ class DecodeArgs(ctypes.Structure):
         ("new_value", ctypes.c_void_p),
         ("total_context_len", ctypes.c_int64),
         ("kv_scale_mode", ctypes.c_int32),
+        ("query_start_loc", ctypes.c_void_p),
+        ("num_queries", ctypes.c_int32),
+        ("max_query_len", ctypes.c_int32),
     ]
 
 
@@ -191,14 +194,19 @@ def _stream(stream) -> int:
 def make_decode_args(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int,
                      out=None, k_scales=None, v_scales=None, workspace=None, partition_tokens: int = 0,
                      kernel: int = KERNEL_AUTO, stream=None, device_pointers: bool = True, new_key=None,
-                     new_value=None, total_context_len: int = 0) -> DecodeArgs:
+                     new_value=None, total_context_len: int = 0, query_start_loc=None,
+                     max_query_len: int = 0) -> DecodeArgs:
     """Fill a DecodeArgs from tensors.  q ``[S][Hq][D]``; caches
     ``[NB][Hkv][BS][D]``; block_tables int32 ``[S][max_blocks]``;
     context_lens int32 ``[S]``; out float32 ``[S][Hq][D]``; optional
     new_key/new_value ``[S][Hkv][D]`` for the fused cache write;
     total_context_len: optional sum of the context lengths (partition
-    hint, 0 = unknown)."""
-    S, Hq, D = q.shape
+    hint, 0 = unknown); query_start_loc int32 ``[S+1]`` with max_query_len:
+    several causal query rows per sequence (q and out ``[R][Hq][D]``)."""
+    R, Hq, D = q.shape
+    S = int(context_lens.shape[0])
+    if query_start_loc is None and R != S:
+        raise ValueError("q has %d rows for %d sequences (pass query_start_loc for several rows each)" % (R, S))
     NB, Hkv, BS, D2 = k_cache.shape
     if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("cache shapes %s / %s do not match q %s" % (tuple(k_cache.shape), tuple(v_cache.shape),
@@ -238,6 +246,12 @@ def make_decode_args(q, k_cache, v_cache, block_tables, context_lens, scale: flo
     a.new_value = get(new_value)
     a.total_context_len = int(total_context_len)
     a.kv_scale_mode = scale_mode_of(k_cache, k_scales)
+    if query_start_loc is not None:
+        if tuple(query_start_loc.shape) != (S + 1,):
+            raise ValueError("query_start_loc must be int32 [%d]" % (S + 1))
+        a.query_start_loc = get(query_start_loc)
+        a.num_queries = R
+        a.max_query_len = int(max_query_len)
     return a
 
 
@@ -249,7 +263,8 @@ def decode_workspace_size(args: DecodeArgs) -> int:
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int, out=None,
            k_scales=None, v_scales=None, workspace=None, partition_tokens: int = 0, kernel: int = KERNEL_AUTO,
-           stream=None, new_key=None, new_value=None, total_context_len: int = 0):
+           stream=None, new_key=None, new_value=None, total_context_len: int = 0, query_start_loc=None,
+           max_query_len: int = 0):
     """Paged decode attention (``pa_decode``).  Returns ``out`` (float32
     ``[S][Hq][D]``), allocated on q's device when not given.  A workspace
     is allocated when the plan needs one and none is passed (its contents
@@ -260,7 +275,8 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_co
     args = make_decode_args(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, out=out,
                             k_scales=k_scales, v_scales=v_scales, workspace=workspace,
                             partition_tokens=partition_tokens, kernel=kernel, stream=stream, new_key=new_key,
-                            new_value=new_value, total_context_len=total_context_len)
+                            new_value=new_value, total_context_len=total_context_len,
+                            query_start_loc=query_start_loc, max_query_len=max_query_len)
     need = decode_workspace_size(args)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -399,12 +415,14 @@ class PreparedDecode:
 
     def __init__(self, q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int, out,
                  k_scales=None, v_scales=None, workspace=None, partition_tokens: int = 0, kernel: int = KERNEL_AUTO,
-                 stream=None, new_key=None, new_value=None, total_context_len: int = 0):
+                 stream=None, new_key=None, new_value=None, total_context_len: int = 0, query_start_loc=None,
+                 max_query_len: int = 0):
         torch = _torch()
         self.args = make_decode_args(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
                                      out=out, k_scales=k_scales, v_scales=v_scales, workspace=workspace,
                                      partition_tokens=partition_tokens, kernel=kernel, stream=stream,
-                                     new_key=new_key, new_value=new_value, total_context_len=total_context_len)
+                                     new_key=new_key, new_value=new_value, total_context_len=total_context_len,
+                                     query_start_loc=query_start_loc, max_query_len=max_query_len)
         need = decode_workspace_size(self.args)
         if need and (workspace is None or self.args.workspace_bytes < need):
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -412,7 +430,7 @@ class PreparedDecode:
             self.args.workspace_bytes = need
         self.workspace_bytes = need
         self._keep = (q, k_cache, v_cache, block_tables, context_lens, out, k_scales, v_scales, workspace, new_key,
-                      new_value)
+                      new_value, query_start_loc)
         self._fn = library().pa_decode
         self._ref = ctypes.byref(self.args)
 

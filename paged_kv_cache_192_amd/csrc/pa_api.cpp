@@ -91,12 +91,20 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
     return fail(PA_ERR_INVALID, "pa_decode: partition_tokens %d is not a multiple of 16 in [0, %d*block_size]",
                 a->partition_tokens, kMaxPartitionBlocks);
   if (a->kernel < 0 || a->kernel > 2) return fail(PA_ERR_INVALID, "pa_decode: kernel %d not in {0, 1, 2}", a->kernel);
+  const bool mq = a->query_start_loc != nullptr;
+  if (mq && (a->num_queries < 0 || a->max_query_len < 1))
+    return fail(PA_ERR_INVALID, "pa_decode: with query_start_loc, num_queries >= 0 and max_query_len >= 1");
+  if (mq && a->new_key)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: no fused cache write with several query rows per sequence");
   const int64_t seq_tokens = (int64_t)(a->num_seqs > 0 ? a->num_seqs : 0) * a->max_context_len;
   if (a->total_context_len < 0 || a->total_context_len > seq_tokens)
     return fail(PA_ERR_INVALID, "pa_decode: total_context_len %lld outside [0, num_seqs * max_context_len]",
                 (long long)a->total_context_len);
 
   const bool mfma_ok = a->q_dtype == PA_BF16 && (a->kv_dtype == PA_BF16 || i8) && a->head_dim == 128;
+  if (mq && (!mfma_ok || a->kernel == KERNEL_VALU))
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: several query rows per sequence need the matrix-core kernel "
+                                    "(bf16 queries, bf16/int8/E4M3 cache, head_dim 128)");
   KernelKind kind;
   if (a->kernel == KERNEL_MFMA) {
     if (!mfma_ok)
@@ -115,12 +123,17 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   while (hpw < G && hpw < 8) hpw *= 2;
   p->heads_per_wave = kind == KERNEL_VALU ? hpw : G;
   p->head_groups = kind == KERNEL_VALU ? (G + hpw - 1) / hpw : 1;
+  // columns of the MFMA kernel: G heads x up to max_query_len rows, 16 at a time
+  const int64_t cg = mq ? ((int64_t)G * a->max_query_len + 15) / 16 : 1;
+  if (cg > 4096) return fail(PA_ERR_UNSUPPORTED, "pa_decode: max_query_len %d too large", a->max_query_len);
+  p->cgroups = (int)cg;
+  p->rows = (int64_t)(mq ? a->num_queries : (a->num_seqs > 0 ? a->num_seqs : 0)) * a->num_q_heads;
 
   const int64_t tiles = a->max_context_len > 0 ? (a->max_context_len + 15) / 16 : 1;
   const int64_t max_tiles = (int64_t)kMaxPartitionBlocks * a->block_size / 16;
   int P = a->partition_tokens;
   const int64_t total = a->total_context_len > 0 ? a->total_context_len : seq_tokens;
-  if (P == 0 && a->num_seqs > 0 && is_ragged(a, total)) {
+  if (P == 0 && a->num_seqs > 0 && !mq && is_ragged(a, total)) {
     // Waves of one (sequence, kv head, head group): about total/P + S/2
     // partitions each; choose P for ~kRaggedWaves waves, at least 4 tiles,
     // at most kMaxPartitionBlocks blocks, and at most kMaxRaggedPartitions
@@ -139,7 +152,8 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
     // Split each sequence into nP equal partitions so the grid holds about
     // target_waves() waves, within [4 tiles, kMaxPartitionBlocks blocks] per
     // partition and at most kMaxAutoPartitions partitions.
-    const int64_t groups = (int64_t)(a->num_seqs > 0 ? a->num_seqs : 1) * a->num_kv_heads * p->head_groups;
+    const int64_t groups =
+        (int64_t)(a->num_seqs > 0 ? a->num_seqs : 1) * a->num_kv_heads * p->head_groups * p->cgroups;
     const int64_t target = target_waves(kind, a->kv_dtype);
     int64_t nP = (target + groups / 2) / groups;
     if (nP < 1) nP = 1;
@@ -193,6 +207,8 @@ pa_status pa_decode(const pa_decode_args* a) {
   if (a->num_seqs == 0) return PA_OK;
   if (!a->out || !a->q || !a->k_cache || !a->v_cache || !a->block_tables || !a->context_lens)
     return fail(PA_ERR_INVALID, "pa_decode: a required device pointer is NULL");
+  if (a->query_start_loc && !aligned(a->query_start_loc, 4))
+    return fail(PA_ERR_INVALID, "pa_decode: query_start_loc must be 4-byte aligned");
   if (!aligned(a->out, 16) || !aligned(a->q, 16) || !aligned(a->k_cache, 16) || !aligned(a->v_cache, 16) ||
       !aligned(a->new_key, 16) || !aligned(a->new_value, 16))
     return fail(PA_ERR_INVALID, "pa_decode: out, q, the caches and new_key/new_value must be 16-byte aligned");

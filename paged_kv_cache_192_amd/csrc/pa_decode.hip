@@ -109,12 +109,13 @@ struct SplitK {
   float* acc;     // [S][Hq][nP][D]: unnormalised weighted sum of values
 };
 
-// One workgroup of W waves per output row (s, h): out = sum_p 2^(m_p - M)
-// acc_p / sum_p 2^(m_p - M) l_p over the partitions that hold tokens, in
-// partition order.  Every partition of the grid leaves its (m, l), empty
-// ones (-inf, 0), so with W = 1 the row's nP partials are read without
-// first reading its length; with W > 1 (long ragged rows, most partitions
-// empty) only the ceil(n / P) that hold tokens are read.  Partitions are read sixteen at a time, all loads of a
+// One workgroup of W waves per output row (query row, head): out = sum_p
+// 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p over the partitions that hold
+// tokens, in partition order.  Every partition of the grid leaves its
+// (m, l), empty ones (-inf, 0), so a row's nP partials can be read without
+// first reading its length.  With lengths given (decode rows) and W > 1
+// (long ragged rows, most partitions empty) only the ceil(n / P) that hold
+// tokens are read.  Partitions are read sixteen at a time, all loads of a
 // group issued together (one memory round trip per group); wave w takes
 // groups w, w + W, ...; groups after a wave's first rescale its running
 // sums to the new maximum.  With W > 1 the waves' (m, L, acc) are combined
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(64 * W) void decode_merge_kernel(float* __restrict_
   const int wave = threadIdx.x >> 6;
   const size_t row = blockIdx.x;
   int np = nP;
-  if (W > 1) {
+  if (W > 1 && context_lens) {
     const int n = min(context_lens[row / Hq], max_tokens);
     np = n > 0 ? min(nP, (n + P - 1) / P) : 0;
   }
@@ -317,7 +318,8 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
 // fastest on the 70B-shaped layer).
 constexpr int kItemOrder = 1;     // 0: p fastest; 1: g fastest
 constexpr bool kXcdRemap = false;  // give each XCD a contiguous range of items
-__device__ __forceinline__ void mfma_item(int bid, int nblk, int Hkv, int nP, int& s, int& g, int& p) {
+__device__ __forceinline__ void mfma_item(int bid, int nblk, int Hkv, int nP, int CG, int& s, int& g, int& p,
+                                          int& cg) {
   int item = bid;
   if (kXcdRemap) {
     // workgroups are dispatched round-robin over the 8 XCDs: XCD x runs
@@ -329,10 +331,14 @@ __device__ __forceinline__ void mfma_item(int bid, int nblk, int Hkv, int nP, in
     p = item % nP;
     const int sg = item / nP;
     g = sg % Hkv;
-    s = sg / Hkv;
+    const int sc = sg / Hkv;
+    cg = sc % CG;
+    s = sc / CG;
   } else {
     g = item % Hkv;
-    const int sp = item / Hkv;
+    const int rest = item / Hkv;
+    cg = rest % CG;
+    const int sp = rest / CG;
     p = sp % nP;
     s = sp / nP;
   }
@@ -340,13 +346,22 @@ __device__ __forceinline__ void mfma_item(int bid, int nblk, int Hkv, int nP, in
 
 // KV: kKvBf16, kKvI8 or kKvFp8 cache; TOKSC: quantised cache with one scale
 // per token ([NB][Hkv][BS]) instead of one per (block, kv head).
+//
+// Columns of the MFMA B operand.  Decode (qsl == NULL): column c is query
+// head g*G + c of the sequence's one query row.  Several causal query rows
+// per sequence (qsl = row offsets): the sequence's L rows times G heads are
+// numbered row-major, col = 16*cg + c -> (row i = col / G, head col % G),
+// and column group cg of the work item takes 16 of them; row i sits at
+// position n - L + i and sees tokens up to it, so each lane column masks
+// its own limit.
 template <int KV, int BS, bool TOKSC>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(
     float* __restrict__ out, SplitK ws,
     const unsigned short* __restrict__ q, char* __restrict__ k_cache, char* __restrict__ v_cache,
     const float* __restrict__ k_scales, const float* __restrict__ v_scales, const int32_t* __restrict__ tables,
     int max_blocks, const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int NB, float qk_log2,
-    int P, int nP, const char* __restrict__ new_k, const char* __restrict__ new_v) {
+    int P, int nP, const char* __restrict__ new_k, const char* __restrict__ new_v,
+    const int32_t* __restrict__ qsl, int CG) {
   constexpr int D = 128;
   constexpr bool I8 = KV != kKvBf16;  // 1-byte codes with fp32 scales
   constexpr int E = I8 ? 1 : 2;
@@ -355,24 +370,40 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   const int lane = threadIdx.x;
   const int j = lane >> 4;
   const int c = lane & 15;
-  int s, g, p;
-  mfma_item(blockIdx.x, gridDim.x, Hkv, nP, s, g, p);
+  int s, g, p, cg;
+  mfma_item(blockIdx.x, gridDim.x, Hkv, nP, CG, s, g, p, cg);
   // a length past the table row is a caller error; never read beyond the row
   const int n = min(context_lens[s], max_blocks * BS);
   const int t_begin = p * P;
   const int t_end = min(n, t_begin + P);
-  const bool head_ok = c < G;
-  const int h = g * G + c;
+  // this lane's column: query row qrow, head h, visible tokens < lim
+  bool head_ok;
+  int h, qrow, lim;
+  if (qsl) {
+    const int q0 = qsl[s], L = qsl[s + 1] - q0;
+    const int col = 16 * cg + c, i = col / G;
+    head_ok = i < L;
+    h = g * G + col % G;
+    qrow = q0 + i;
+    lim = max(0, min(t_end, n - L + i + 1));
+    if (16 * cg >= G * L) return;  // no column of this group exists
+  } else {
+    head_ok = c < G;
+    h = g * G + c;
+    qrow = s;
+    lim = t_end;
+  }
+  const size_t orow = (size_t)qrow * Hq + h;  // output / partial row
 
   if (t_begin >= t_end) {
     // Nothing to attend to.  With one partition the output row is zero;
     // otherwise the partial is marked empty (no weight) for the merge.
     if (nP == 1 && head_ok) {
-      float4* o = (float4*)(out + ((size_t)s * Hq + h) * D + 32 * j);
+      float4* o = (float4*)(out + orow * D + 32 * j);
 #pragma unroll
       for (int k = 0; k < 8; ++k) o[k] = float4{0.f, 0.f, 0.f, 0.f};
     } else if (head_ok && j == 0) {
-      ws.ml[((size_t)s * Hq + h) * nP + p] = float2{kNegInf, 0.f};
+      ws.ml[orow * nP + p] = float2{kNegInf, 0.f};
     }
     return;
   }
@@ -384,7 +415,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   for (int kk = 0; kk < 4; ++kk) {
     const int chunk = I8 ? j * 4 + kk : kk * 4 + j;
     u32x4_t w = {0u, 0u, 0u, 0u};
-    if (head_ok) w = *(const u32x4_t*)(q + ((size_t)s * Hq + h) * D + chunk * 8);
+    if (head_ok) w = *(const u32x4_t*)(q + orow * D + chunk * 8);
     qf[kk] = as_bf16x8(w);
   }
 
@@ -502,7 +533,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       float xs = qk_log2;
       if constexpr (TOKSC) xs *= ks[r];
       else if (I8) xs *= ks;
-      x[r] = (ok && tok0 + r < t_end) ? sc[r] * xs : kNegInf;
+      x[r] = (ok && tok0 + r < lim) ? sc[r] * xs : kNegInf;
     }
     float mloc = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mloc = xor_max_rows(mloc);
@@ -611,7 +642,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   if (nP == 1) {
     if (!head_ok) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    float* o = out + ((size_t)s * Hq + h) * D + 32 * j;
+    float* o = out + orow * D + 32 * j;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       *(float4*)(o + 8 * r) = float4{acc[0][r] * inv, acc[1][r] * inv, acc[2][r] * inv, acc[3][r] * inv};
@@ -620,7 +651,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     return;
   }
   if (head_ok) {
-    const size_t row_id = ((size_t)s * Hq + h) * nP + p;
+    const size_t row_id = orow * nP + p;
     float* o = ws.acc + row_id * D + 32 * j;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -932,7 +963,7 @@ static inline SplitK split_k(const pa_decode_args* a, const DecodePlan& p) {
 }
 
 pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipStream_t st) {
-  const size_t items = (size_t)a->num_seqs * a->num_kv_heads * p.num_partitions;
+  const size_t items = (size_t)a->num_seqs * a->num_kv_heads * p.num_partitions * p.cgroups;
   if (items > 0x7fffffffu) return fail(PA_ERR_UNSUPPORTED, "pa_decode: grid too large");
   const float qk = a->scale * kLog2e;
   const SplitK ws = split_k(a, p);
@@ -941,7 +972,8 @@ pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipSt
                      (float*)a->out, ws, (const unsigned short*)a->q, (char*)a->k_cache, (char*)a->v_cache,      \
                      a->k_scales, a->v_scales, a->block_tables, a->max_blocks_per_seq, a->context_lens,        \
                      a->num_q_heads, a->num_kv_heads, p.G, a->num_blocks, qk, p.partition_tokens,              \
-                     p.num_partitions, (const char*)a->new_key, (const char*)a->new_value)
+                     p.num_partitions, (const char*)a->new_key, (const char*)a->new_value,                     \
+                     a->query_start_loc, p.cgroups)
 #define PA_MFMA_BS(KV, TOKSC)                              \
   if (a->block_size == 16) PA_MFMA_LAUNCH(KV, 16, TOKSC); \
   else PA_MFMA_LAUNCH(KV, 32, TOKSC)
@@ -1021,7 +1053,8 @@ static void merge_dispatch(const pa_decode_args* a, const DecodePlan& p, hipStre
                            const SplitK& ws, int max_tokens) {
 #define PA_MERGE_LAUNCH(W)                                                                                  \
   hipLaunchKernelGGL((decode_merge_kernel<D, W>), dim3(rows), dim3(64 * W), 0, st, (float*)a->out, ws,       \
-                     a->context_lens, a->num_q_heads, p.partition_tokens, p.num_partitions, max_tokens)
+                     a->query_start_loc ? nullptr : a->context_lens, a->num_q_heads, p.partition_tokens,        \
+                     p.num_partitions, max_tokens)
   if (p.num_partitions <= 16) PA_MERGE_LAUNCH(1);
   else if (p.num_partitions <= 32) PA_MERGE_LAUNCH(2);
   else PA_MERGE_LAUNCH(4);
@@ -1029,7 +1062,8 @@ static void merge_dispatch(const pa_decode_args* a, const DecodePlan& p, hipStre
 }
 
 pa_status launch_decode_merge(const pa_decode_args* a, const DecodePlan& p, hipStream_t st) {
-  const size_t rows = (size_t)a->num_seqs * a->num_q_heads;
+  const size_t rows = (size_t)p.rows;
+  if (rows == 0) return PA_OK;
   const SplitK ws = split_k(a, p);
   const int max_tokens = a->max_blocks_per_seq * a->block_size;
   if (a->head_dim == 64) merge_dispatch<64>(a, p, st, (unsigned)rows, ws, max_tokens);

@@ -55,6 +55,8 @@ struct DecodePlan {
   int head_groups;       // VALU: ceil(G / heads_per_wave)
   int partition_tokens;  // multiple of 16
   int num_partitions;    // ceil(max_context_len / partition_tokens), >= 1
+  int cgroups;           // MFMA: groups of 16 (query row, head) columns per (sequence, kv head)
+  int64_t rows;          // output rows: query rows (num_seqs, or num_queries) x num_q_heads
   size_t workspace_bytes;
 };
 
@@ -74,7 +76,7 @@ inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 inline WorkspaceLayout workspace_layout(const pa_decode_args* a, const DecodePlan& p) {
   WorkspaceLayout L{0, 0, 0};
   if (p.num_partitions <= 1) return L;
-  const size_t rows = (size_t)a->num_seqs * a->num_q_heads * p.num_partitions;
+  const size_t rows = (size_t)p.rows * p.num_partitions;
   L.ml_offset = 0;
   L.acc_offset = align256(rows * 2 * sizeof(float));
   L.bytes = L.acc_offset + align256(rows * a->head_dim * sizeof(float));

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
     assert len(names) >= 16, names
     for n in names:
         assert hasattr(lib, n), "libpa.so does not export %s" % n
-    assert lib.pa_abi_version() == pa.ABI_VERSION == 4
+    assert lib.pa_abi_version() == pa.ABI_VERSION == 5
 
 
 def test_status_strings():
@@ -143,6 +143,25 @@ def test_decode_rejects_null_alignment_and_workspace_before_launch():
     assert "workspace" in lib.pa_last_error().decode()
     a = _cpu_args(kernel=2, q_dtype=pa.PA_F32)
     assert lib.pa_decode(ctypes.byref(a)) == pa.PA_ERR_UNSUPPORTED
+
+
+def test_multi_query_argument_checks():
+    lib = pa.library()
+    qsl = 0x30000
+    a = _cpu_args(query_start_loc=qsl, num_queries=5, max_query_len=0)
+    assert lib.pa_decode(ctypes.byref(a)) == pa.PA_ERR_INVALID
+    a = _cpu_args(query_start_loc=qsl, num_queries=-1, max_query_len=2)
+    assert lib.pa_decode(ctypes.byref(a)) == pa.PA_ERR_INVALID
+    a = _cpu_args(query_start_loc=qsl, num_queries=5, max_query_len=2, kernel=pa.KERNEL_VALU)
+    assert lib.pa_decode(ctypes.byref(a)) == pa.PA_ERR_UNSUPPORTED
+    a = _cpu_args(query_start_loc=qsl, num_queries=5, max_query_len=2, q_dtype=pa.PA_F32)
+    assert lib.pa_decode(ctypes.byref(a)) == pa.PA_ERR_UNSUPPORTED
+    a = _cpu_args(query_start_loc=qsl, num_queries=5, max_query_len=2, new_key=0x20000, new_value=0x30000)
+    assert lib.pa_decode(ctypes.byref(a)) == pa.PA_ERR_UNSUPPORTED
+    # workspace rows are query rows: 5 rows x 8 heads x 2 partitions of 64 tokens
+    st, n = _ws(_cpu_args(query_start_loc=qsl, num_queries=5, max_query_len=3, partition_tokens=64))
+    al = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    assert st == pa.PA_OK and n == al(5 * 8 * 2 * 8) + al(5 * 8 * 2 * 128 * 4)
 
 
 def test_fused_write_argument_checks():
