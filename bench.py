@@ -44,16 +44,21 @@ def kv_bytes(context_lens, num_kv_heads: int, head_dim: int, elem_bytes: int, la
 
 
 def decode_algorithmic_bytes(context_lens, num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
-                             kv_elem: int, q_elem: int, int8_scales: bool = False) -> int:
+                             kv_elem: int, q_elem: int, int8_scales: bool = False, token_scales: bool = False,
+                             query_rows: int = 0) -> int:
     """Bytes one decode call must move at least: K and V of every token
-    (not padded to the block), the per-(block, head) scales of int8 caches,
-    the table entries in use, the context lengths, q and the fp32 output."""
+    (not padded to the block), the scales of quantised caches (per (block,
+    head), or per token), the table entries in use, the context lengths, q
+    and the fp32 output (query_rows rows when several per sequence)."""
     S = len(context_lens)
+    rows = query_rows or S
     blocks = sum(-(-int(n) // block_size) for n in context_lens)
     b = kv_bytes(context_lens, num_kv_heads, head_dim, kv_elem)
-    if int8_scales:
+    if token_scales:
+        b += sum(int(n) for n in context_lens) * num_kv_heads * 2 * 4
+    elif int8_scales:
         b += blocks * num_kv_heads * 2 * 4
-    b += blocks * 4 + S * 4 + S * num_q_heads * head_dim * (q_elem + 4)
+    b += blocks * 4 + S * 4 + rows * num_q_heads * head_dim * (q_elem + 4)
     return b
 
 
@@ -294,6 +299,14 @@ def run(args) -> dict:
 
 
 WORKLOADS = {
+    "int8-token": "int8 KV with per-token scales: pa_quantize_and_cache of each new token, then decode (64 seqs, "
+                  "log-normal lengths, 32/8 heads)",
+    "fp8": "E4M3 fp8 KV with per-token scales: pa_quantize_and_cache of each new token, then decode (64 seqs, "
+           "log-normal lengths, 32/8 heads)",
+    "spec-decode": "70B-shaped layer (20 x 8,000 tokens, 64/8 heads, bf16) with 4 causal query rows per sequence "
+                   "(checking 3 drafted tokens)",
+    "chunked-prefill": "70B-shaped layer (20 x 8,000 tokens, 64/8 heads, bf16) with a 64-row causal prefill chunk "
+                       "per sequence",
     "llama3-70b": "70B-shaped GQA decode, 80 layers (20 x 8,000 tokens, 64/8 heads, bf16, block 16)",
     "tiny": "tiny fp32 decode (4 seqs of 17/33/100/200 tokens, 8 heads of 64, block 16)",
     "llama13b": "13B-shaped MHA decode, one layer (32 seqs, U[200,2048] tokens, 40 heads of 128, bf16)",
@@ -417,6 +430,185 @@ def run_single_layer(args) -> dict:
     return res
 
 
+def _timed_graph(prepare, steps: int, warmup: int, outs):
+    """Capture prepare()'s calls once as a graph, check one replay against
+    the eager result bit for bit, and return the mean replay time in ms."""
+    import torch
+
+    main = torch.cuda.current_stream()
+    for f in prepare(main):
+        f()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    cap = torch.cuda.Stream()
+    cap.wait_stream(main)
+    gcalls = prepare(cap)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        for f in gcalls:
+            f()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    if not all(torch.equal(a, b) for a, b in zip(outs, ref)):
+        raise RuntimeError("graph replay differs from the eager step")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def run_next_workload(args) -> dict:
+    """Workloads of the quantised and multi-query paths, one layer per
+    replica (R replicas so that >= 1 GB is touched between reuses):
+      int8-token / fp8: the int8 workload's batch with per-token scales; a
+        step is pa_quantize_and_cache of every sequence's new token (codes
+        and scales computed in-kernel) then pa_decode;
+      spec-decode / chunked-prefill: the 70B-shaped layer with L causal
+        query rows per sequence (the last L tokens of each context)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_192_amd as pa
+    import synth
+
+    pa.library()
+    dev = torch.device("cuda:0")
+    w = args.workload
+    res = {"workload": w, "description": WORKLOADS[w], "steps": args.steps, "warmup": args.warmup,
+           "partition_tokens": args.partition_tokens}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(91)
+    if w in ("int8-token", "fp8"):
+        case = synth.config5()
+        if w == "fp8":
+            synth.random_fp8_cache(case, seed=56, per_token=True)
+        else:
+            synth.random_int8_cache(case, seed=56, per_token=True)
+        S, Hq, Hkv, D, BS = case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim, case.block_size
+        layer_bytes = 2 * case.k_cache.nbytes
+        R = max(1, -(-(1 << 30) // layer_bytes))
+
+        def put(a):
+            t = torch.from_numpy(np.ascontiguousarray(a))
+            if a.dtype == np.uint16:
+                t = t.view(torch.int16).view(torch.bfloat16)
+            t = t.to(dev)
+            return t.view(torch.float8_e4m3fn) if a.dtype == np.uint8 else t
+
+        q, bt, cl = put(case.q), put(case.block_tables), put(case.context_lens)
+        K = [put(case.k_cache) for _ in range(R)]
+        V = [put(case.v_cache) for _ in range(R)]
+        KS = [put(case.k_scales) for _ in range(R)]
+        VS = [put(case.v_scales) for _ in range(R)]
+        newk = torch.randn(S, Hkv, D, generator=gen, device=dev).to(torch.bfloat16)
+        newv = torch.randn(S, Hkv, D, generator=gen, device=dev).to(torch.bfloat16)
+        slots = pa.slot_mapping(bt, BS, context_lens=cl)
+        outs = [torch.empty(S, Hq, D, dtype=torch.float32, device=dev) for _ in range(R)]
+        ws = torch.empty(1 << 27, dtype=torch.uint8, device=dev)
+        total = int(np.sum(case.context_lens, dtype=np.int64))
+
+        def prepare(stream):
+            calls = []
+            for r in range(R):
+                calls.append(pa.prepare_quantize_and_cache(newk, newv, K[r], V[r], KS[r], VS[r], slots,
+                                                           stream=stream))
+                calls.append(pa.PreparedDecode(q, K[r], V[r], bt, cl, float(case.scale), case.max_context_len,
+                                               outs[r], k_scales=KS[r], v_scales=VS[r], workspace=ws, stream=stream,
+                                               partition_tokens=args.partition_tokens, total_context_len=total))
+            return calls
+
+        ms = _timed_graph(prepare, args.steps, args.warmup, outs) / R
+        cls = case.context_lens
+        alg = decode_algorithmic_bytes(cls, Hq, Hkv, D, BS, 1, 2, token_scales=True)
+        kvb = kv_bytes(cls, Hkv, D, 1)
+        res.update({"replicas": R, "ms_per_layer": round(ms, 5), "tokens_per_s": round(S / (ms * 1e-3), 1),
+                    "kv_gbs": round(kvb / (ms * 1e-3) / 1e9, 1),
+                    "pct_hbm_peak": round(100.0 * alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                    "algorithmic_bytes_per_layer": alg, "sum_ctx": int(np.sum(cls)),
+                    "step": "pa_quantize_and_cache (new token, per-token scales) + pa_decode"})
+        return res
+    # multi-query rows on the 70B-shaped layer
+    L = 4 if w == "spec-decode" else 64
+    st = synth.config3_structure()
+    c = synth.CFG3
+    S, Hq, Hkv, D, BS = c["num_seqs"], c["num_q_heads"], c["num_kv_heads"], c["head_dim"], c["block_size"]
+    R = 2
+    bt = torch.from_numpy(st["block_tables"]).to(dev)
+    cl = torch.from_numpy(st["context_lens"]).to(dev)
+    layers = [synth.config3_layer_values(r, dev) for r in range(R)]
+    qsl = torch.arange(0, S * L + 1, L, dtype=torch.int32, device=dev)
+    qs = [torch.randn(S * L, Hq, D, generator=gen, device=dev).to(torch.bfloat16) for _ in range(R)]
+    outs = [torch.empty(S * L, Hq, D, dtype=torch.float32, device=dev) for _ in range(R)]
+    ws = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+    ctx = int(st["context_lens"][0])
+
+    def prepare(stream):
+        return [pa.PreparedDecode(qs[r], layers[r][1], layers[r][2], bt, cl, float(st["scale"]), ctx, outs[r],
+                                  workspace=ws, stream=stream, partition_tokens=args.partition_tokens,
+                                  query_start_loc=qsl, max_query_len=L) for r in range(R)]
+
+    ms = _timed_graph(prepare, args.steps, args.warmup, outs) / R
+    cls = st["context_lens"]
+    alg = decode_algorithmic_bytes(cls, Hq, Hkv, D, BS, 2, 2, query_rows=S * L)
+    visible = sum(sum(int(n) - L + i + 1 for i in range(L)) for n in cls)
+    flops = 4 * Hq * D * visible
+    res.update({"replicas": R, "query_rows_per_seq": L, "ms_per_layer": round(ms, 5),
+                "query_tokens_per_s": round(S * L / (ms * 1e-3), 1),
+                "kv_gbs": round(kv_bytes(cls, Hkv, D, 2) / (ms * 1e-3) / 1e9, 1),
+                "pct_hbm_peak": round(100.0 * alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "algorithmic_bytes_per_layer": alg,
+                "step": "pa_decode with query_start_loc (%d causal rows per sequence)" % L})
+    return res
+
+
+def run_swap(args) -> dict:
+    """pa_swap_blocks bandwidth: --swap-blocks blocks of the 70B-shaped
+    layer's shape (8 heads x 16 slots x 128 bf16 = 32 KB per K or V block)
+    out to a pinned host pool and back in, as separate timed calls."""
+    import torch
+
+    import paged_kv_cache_192_amd as pa
+
+    pa.library()
+    dev = torch.device("cuda:0")
+    n = args.swap_blocks
+    shape = (n, 8, 16, 128)
+    dk = torch.randn(shape, device=dev).to(torch.bfloat16)
+    dv = torch.randn(shape, device=dev).to(torch.bfloat16)
+    hk = torch.empty(shape, dtype=torch.bfloat16).pin_memory()
+    hv = torch.empty(shape, dtype=torch.bfloat16).pin_memory()
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(5))
+    pairs = torch.stack([torch.arange(n), perm], dim=1).to(torch.int64).to(dev)
+    back = torch.stack([perm, torch.arange(n)], dim=1).to(torch.int64).to(dev)
+    out_call = pa.prepare_swap_blocks(dk, dv, hk, hv, pairs)
+    in_call = pa.prepare_swap_blocks(hk, hv, dk, dv, back)
+    res = {"mode": "swap", "blocks": n, "bytes_per_direction": 2 * dk.numel() * 2}
+    for name, f in (("device_to_host", out_call), ("host_to_device", in_call)):
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        res[name] = {"ms": round(ms, 4), "gbs": round(res["bytes_per_direction"] / (ms * 1e-3) / 1e9, 1)}
+    ref = torch.randn(shape, device=dev).to(torch.bfloat16)
+    dk.copy_(ref)
+    out_call()
+    dk.zero_()
+    in_call()
+    torch.cuda.synchronize()
+    res["round_trip_exact"] = bool(torch.equal(dk, ref))
+    return res
+
+
 def cpu_baseline(args, K, V, Q, st, L) -> dict:
     """The CPU oracle (fp64, OpenMP over (sequence, head) rows) on a bounded
     sample of the same workload: whole layers, all 20 sequences, copied back
@@ -488,8 +680,10 @@ def main():
                     help="separate slot-mapping and reshape_and_cache launches instead of the fused cache write")
     ap.add_argument("--eager", dest="graph", action="store_false",
                     help="launch each call from Python instead of replaying the captured step")
-    ap.add_argument("--mode", choices=["decode", "copy-calibration"], default="decode",
-                    help="copy-calibration: a known-size block copy for scaling HBM byte counters")
+    ap.add_argument("--mode", choices=["decode", "copy-calibration", "swap"], default="decode",
+                    help="copy-calibration: a known-size block copy for scaling HBM byte counters; swap: "
+                         "pa_swap_blocks bandwidth between the device and a pinned host pool")
+    ap.add_argument("--swap-blocks", type=int, default=4096, help="blocks per swap call (--mode swap)")
     ap.add_argument("--copy-pairs", type=int, default=4096)
     ap.add_argument("--partition-tokens", type=int, default=0,
                     help="override the library's automatic split-K partition length (tuning only)")
@@ -508,6 +702,10 @@ def main():
               file=sys.stderr)
     if args.mode == "copy-calibration":
         res = copy_calibration(args)
+    elif args.mode == "swap":
+        res = run_swap(args)
+    elif args.workload in ("int8-token", "fp8", "spec-decode", "chunked-prefill"):
+        res = run_next_workload(args)
     elif args.workload != "llama3-70b":
         res = run_single_layer(args)
     else:
