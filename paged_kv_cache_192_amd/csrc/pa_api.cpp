@@ -127,6 +127,8 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   const int64_t cg = mq ? ((int64_t)G * a->max_query_len + 15) / 16 : 1;
   if (cg > 4096) return fail(PA_ERR_UNSUPPORTED, "pa_decode: max_query_len %d too large", a->max_query_len);
   p->cgroups = (int)cg;
+  p->ncg = cg >= 2 ? 2 : 1;
+  p->cg_waves = (int)((cg + p->ncg - 1) / p->ncg);
   p->rows = (int64_t)(mq ? a->num_queries : (a->num_seqs > 0 ? a->num_seqs : 0)) * a->num_q_heads;
 
   const int64_t tiles = a->max_context_len > 0 ? (a->max_context_len + 15) / 16 : 1;
@@ -153,8 +155,10 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
     // target_waves() waves, within [4 tiles, kMaxPartitionBlocks blocks] per
     // partition and at most kMaxAutoPartitions partitions.
     const int64_t groups =
-        (int64_t)(a->num_seqs > 0 ? a->num_seqs : 1) * a->num_kv_heads * p->head_groups * p->cgroups;
-    const int64_t target = target_waves(kind, a->kv_dtype);
+        (int64_t)(a->num_seqs > 0 ? a->num_seqs : 1) * a->num_kv_heads * p->head_groups * p->cg_waves;
+    // a wave carrying two column groups does twice the arithmetic per tile:
+    // twice the waves keep the same bytes in flight per unit of compute
+    const int64_t target = target_waves(kind, a->kv_dtype) * p->ncg;
     int64_t nP = (target + groups / 2) / groups;
     if (nP < 1) nP = 1;
     if (nP > kMaxAutoPartitions) nP = kMaxAutoPartitions;

@@ -351,10 +351,12 @@ __device__ __forceinline__ void mfma_item(int bid, int nblk, int Hkv, int nP, in
 // head g*G + c of the sequence's one query row.  Several causal query rows
 // per sequence (qsl = row offsets): the sequence's L rows times G heads are
 // numbered row-major, col = 16*cg + c -> (row i = col / G, head col % G),
-// and column group cg of the work item takes 16 of them; row i sits at
-// position n - L + i and sees tokens up to it, so each lane column masks
-// its own limit.
-template <int KV, int BS, bool TOKSC>
+// and column group cg takes 16 of them; row i sits at position n - L + i
+// and sees tokens up to it, so each lane column masks its own limit.  A
+// wave carries NCG consecutive column groups over the same K/V tiles (one
+// score MFMA chain, softmax state and accumulator set per group, V^T
+// operands built once), so K/V are read once per NCG groups.
+template <int KV, int BS, bool TOKSC, int NCG>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(
     float* __restrict__ out, SplitK ws,
     const unsigned short* __restrict__ q, char* __restrict__ k_cache, char* __restrict__ v_cache,
@@ -370,54 +372,65 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   const int lane = threadIdx.x;
   const int j = lane >> 4;
   const int c = lane & 15;
-  int s, g, p, cg;
-  mfma_item(blockIdx.x, gridDim.x, Hkv, nP, CG, s, g, p, cg);
+  int s, g, p, cgw;
+  mfma_item(blockIdx.x, gridDim.x, Hkv, nP, CG, s, g, p, cgw);
   // a length past the table row is a caller error; never read beyond the row
   const int n = min(context_lens[s], max_blocks * BS);
   const int t_begin = p * P;
   const int t_end = min(n, t_begin + P);
-  // this lane's column: query row qrow, head h, visible tokens < lim
-  bool head_ok;
-  int h, qrow, lim;
-  if (qsl) {
-    const int q0 = qsl[s], L = qsl[s + 1] - q0;
-    const int col = 16 * cg + c, i = col / G;
-    head_ok = i < L;
-    h = g * G + col % G;
-    qrow = q0 + i;
-    lim = max(0, min(t_end, n - L + i + 1));
-    if (16 * cg >= G * L) return;  // no column of this group exists
-  } else {
-    head_ok = c < G;
-    h = g * G + c;
-    qrow = s;
-    lim = t_end;
+  // this lane's column in each group u: output / partial row orow[u],
+  // visible tokens < lim[u]
+  bool head_ok[NCG];
+  size_t orow[NCG];
+  int lim[NCG];
+#pragma unroll
+  for (int u = 0; u < NCG; ++u) {
+    int h, qrow;
+    if (qsl) {
+      const int q0 = qsl[s], L = qsl[s + 1] - q0;
+      const int col = 16 * (cgw * NCG + u) + c, i = col / G;
+      head_ok[u] = i < L;
+      h = g * G + col % G;
+      qrow = q0 + i;
+      lim[u] = head_ok[u] ? max(0, min(t_end, n - L + i + 1)) : 0;
+      if (u == 0 && 16 * cgw * NCG >= G * L) return;  // no column of these groups exists
+    } else {
+      head_ok[u] = c < G;
+      h = g * G + c;
+      qrow = s;
+      lim[u] = t_end;
+    }
+    orow[u] = (size_t)qrow * Hq + h;
   }
-  const size_t orow = (size_t)qrow * Hq + h;  // output / partial row
 
   if (t_begin >= t_end) {
     // Nothing to attend to.  With one partition the output row is zero;
     // otherwise the partial is marked empty (no weight) for the merge.
-    if (nP == 1 && head_ok) {
-      float4* o = (float4*)(out + orow * D + 32 * j);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) o[k] = float4{0.f, 0.f, 0.f, 0.f};
-    } else if (head_ok && j == 0) {
-      ws.ml[orow * nP + p] = float2{kNegInf, 0.f};
+    for (int u = 0; u < NCG; ++u) {
+      if (nP == 1 && head_ok[u]) {
+        float4* o = (float4*)(out + orow[u] * D + 32 * j);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = float4{0.f, 0.f, 0.f, 0.f};
+      } else if (nP > 1 && head_ok[u] && j == 0) {
+        ws.ml[orow[u] * nP + p] = float2{kNegInf, 0.f};
+      }
     }
     return;
   }
 
-  // Queries of the group as the B operand: column = head c, the 8 values of
-  // d-chunk (kk*4 + j) [bf16 cache] or (j*4 + kk) [int8 cache].
-  bf16x8_t qf[4];
+  // Queries as the B operand: column c of group u, the 8 values of d-chunk
+  // (kk*4 + j) [bf16 cache] or (j*4 + kk) [1-byte cache].
+  bf16x8_t qf[NCG][4];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int chunk = I8 ? j * 4 + kk : kk * 4 + j;
-    u32x4_t w = {0u, 0u, 0u, 0u};
-    if (head_ok) w = *(const u32x4_t*)(q + orow * D + chunk * 8);
-    qf[kk] = as_bf16x8(w);
-  }
+  for (int u = 0; u < NCG; ++u)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int chunk = I8 ? j * 4 + kk : kk * 4 + j;
+      u32x4_t w = {0u, 0u, 0u, 0u};
+      if (head_ok[u]) w = *(const u32x4_t*)(q + orow[u] * D + chunk * 8);
+      qf[u][kk] = as_bf16x8(w);
+    }
 
   const int32_t* trow = tables + (size_t)s * max_blocks;
   const int tile_begin = t_begin >> 4;
@@ -489,10 +502,15 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     }
   };
 
-  f32x4_t acc[8];
+  f32x4_t acc[NCG][8];
+  float m_run[NCG], l_run[NCG];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.f;
+  for (int u = 0; u < NCG; ++u) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[u][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[u] = kNegInf;
+    l_run[u] = 0.f;
+  }
 
   auto compute = [&](MfmaTile<I8>& T, int ti, bool ok, const Sc& ks, const Sc& vs) {
     const bool new_tile = owns_new && ti == (tnew >> 4);  // wave-uniform
@@ -510,63 +528,68 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
           if (4 * j + i == rnew) T.v[i] = nv;
       }
     }
-    // ---- scores
-    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+    // ---- scores, one MFMA chain per column group over the same K operands
+    bf16x8_t ka[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      bf16x8_t a;
       if (I8) {
         // lane holds d = 32j .. 32j+31 of row c: chunk 2j (kk 0, 1), 2j+1 (kk 2, 3)
         const u32x4_t chunk = ktile[kr[kk >> 1]];
         const unsigned w0 = chunk[(kk & 1) * 2], w1 = chunk[(kk & 1) * 2 + 1];
         const u32x2_t lo = codes_to_bf16x4<KV>(w0), hi = codes_to_bf16x4<KV>(w1);
-        a = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+        ka[kk] = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
       } else {
-        a = as_bf16x8(ktile[kr[kk]]);
+        ka[kk] = as_bf16x8(ktile[kr[kk]]);
       }
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kk], sc, 0, 0, 0);
     }
     const int tok0 = ti * 16 + 4 * j;
-    float x[4];
+    i16x4_t Phi[NCG], Plo[NCG];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float xs = qk_log2;
-      if constexpr (TOKSC) xs *= ks[r];
-      else if (I8) xs *= ks;
-      x[r] = (ok && tok0 + r < lim) ? sc[r] * xs : kNegInf;
+    for (int u = 0; u < NCG; ++u) {
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qf[u][kk], sc, 0, 0, 0);
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float xs = qk_log2;
+        if constexpr (TOKSC) xs *= ks[r];
+        else if (I8) xs *= ks;
+        x[r] = (ok && tok0 + r < lim[u]) ? sc[r] * xs : kNegInf;
+      }
+      float mloc = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      mloc = xor_max_rows(mloc);
+      // ---- lazy rescale of the running reference
+      const bool need = mloc > m_run[u] + kRescaleThreshold;
+      if (__any(need)) {
+        const float m_new = need ? mloc : m_run[u];
+        const float alpha = need ? fast_exp2(m_run[u] - m_new) : 1.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[u][e] *= alpha;
+        l_run[u] *= alpha;
+        m_run[u] = m_new;
+      }
+      float pw[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pw[r] = x[r] == kNegInf ? 0.f : fast_exp2(x[r] - m_run[u]);
+      l_run[u] += (pw[0] + pw[1]) + (pw[2] + pw[3]);
+      if constexpr (TOKSC) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pw[r] *= vs[r];
+      } else if (I8) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pw[r] *= vs;
+      }
+      // ---- P as bf16 hi + lo, B operand of the P.V MFMA
+      float lo[4];
+      unsigned hi01 = pack_bf16x2(pw[0], pw[1]), hi23 = pack_bf16x2(pw[2], pw[3]);
+      lo[0] = pw[0] - bf16_lo(hi01);
+      lo[1] = pw[1] - bf16_hi(hi01);
+      lo[2] = pw[2] - bf16_lo(hi23);
+      lo[3] = pw[3] - bf16_hi(hi23);
+      Phi[u] = as_i16x4(hi01, hi23);
+      Plo[u] = as_i16x4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
     }
-    float mloc = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mloc = xor_max_rows(mloc);
-    // ---- lazy rescale of the running reference
-    const bool need = mloc > m_run + kRescaleThreshold;
-    if (__any(need)) {
-      const float m_new = need ? mloc : m_run;
-      const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    float pw[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pw[r] = x[r] == kNegInf ? 0.f : fast_exp2(x[r] - m_run);
-    l_run += (pw[0] + pw[1]) + (pw[2] + pw[3]);
-    if constexpr (TOKSC) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pw[r] *= vs[r];
-    } else if (I8) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pw[r] *= vs;
-    }
-    // ---- P as bf16 hi + lo, B operand of the P.V MFMA
-    float lo[4];
-    unsigned hi01 = pack_bf16x2(pw[0], pw[1]), hi23 = pack_bf16x2(pw[2], pw[3]);
-    lo[0] = pw[0] - bf16_lo(hi01);
-    lo[1] = pw[1] - bf16_hi(hi01);
-    lo[2] = pw[2] - bf16_lo(hi23);
-    lo[3] = pw[3] - bf16_hi(hi23);
-    const i16x4_t Phi = as_i16x4(hi01, hi23);
-    const i16x4_t Plo = as_i16x4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
     // ---- V^T operands: rows 4j+i of this lane; rows past the context are
     // zeroed (they may hold NaN and would poison 0 * NaN in the MFMA)
     const bool partial = !ok || ti * 16 + 15 >= t_end;  // wave-uniform
@@ -599,10 +622,14 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
                                       __builtin_amdgcn_perm(vw[3][w], vw[2][w], 0x05040100u));
       const i16x4_t a_odd = as_i16x4(__builtin_amdgcn_perm(vw[1][w], vw[0][w], 0x07060302u),
                                      __builtin_amdgcn_perm(vw[3][w], vw[2][w], 0x07060302u));
-      acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_even, Phi, acc[2 * w], 0, 0, 0);
-      acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_even, Plo, acc[2 * w], 0, 0, 0);
-      acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_odd, Phi, acc[2 * w + 1], 0, 0, 0);
-      acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_odd, Plo, acc[2 * w + 1], 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < NCG; ++u) {
+        f32x4_t* au = acc[u];
+        au[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_even, Phi[u], au[2 * w], 0, 0, 0);
+        au[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_even, Plo[u], au[2 * w], 0, 0, 0);
+        au[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_odd, Phi[u], au[2 * w + 1], 0, 0, 0);
+        au[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_odd, Plo[u], au[2 * w + 1], 0, 0, 0);
+      }
     }
   };
 
@@ -637,28 +664,30 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     }
   }
 
-  const float l_tot = xor_sum_rows(l_run);
-  // lane holds d = 32j + 8r + e in acc[e][r]
-  if (nP == 1) {
-    if (!head_ok) return;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    float* o = out + orow * D + 32 * j;
+  // lane holds d = 32j + 8r + e in acc[u][e][r]
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      *(float4*)(o + 8 * r) = float4{acc[0][r] * inv, acc[1][r] * inv, acc[2][r] * inv, acc[3][r] * inv};
-      *(float4*)(o + 8 * r + 4) = float4{acc[4][r] * inv, acc[5][r] * inv, acc[6][r] * inv, acc[7][r] * inv};
-    }
-    return;
-  }
-  if (head_ok) {
-    const size_t row_id = orow * nP + p;
-    float* o = ws.acc + row_id * D + 32 * j;
+  for (int u = 0; u < NCG; ++u) {
+    const float l_tot = xor_sum_rows(l_run[u]);
+    const f32x4_t* a = acc[u];
+    if (!head_ok[u]) continue;
+    if (nP == 1) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      float* o = out + orow[u] * D + 32 * j;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      *(float4*)(o + 8 * r) = float4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
-      *(float4*)(o + 8 * r + 4) = float4{acc[4][r], acc[5][r], acc[6][r], acc[7][r]};
+      for (int r = 0; r < 4; ++r) {
+        *(float4*)(o + 8 * r) = float4{a[0][r] * inv, a[1][r] * inv, a[2][r] * inv, a[3][r] * inv};
+        *(float4*)(o + 8 * r + 4) = float4{a[4][r] * inv, a[5][r] * inv, a[6][r] * inv, a[7][r] * inv};
+      }
+    } else {
+      const size_t row_id = orow[u] * nP + p;
+      float* o = ws.acc + row_id * D + 32 * j;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        *(float4*)(o + 8 * r) = float4{a[0][r], a[1][r], a[2][r], a[3][r]};
+        *(float4*)(o + 8 * r + 4) = float4{a[4][r], a[5][r], a[6][r], a[7][r]};
+      }
+      if (j == 0) ws.ml[row_id] = float2{m_run[u], l_tot};
     }
-    if (j == 0) ws.ml[row_id] = float2{m_run, l_tot};
   }
 }
 
@@ -963,17 +992,23 @@ static inline SplitK split_k(const pa_decode_args* a, const DecodePlan& p) {
 }
 
 pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipStream_t st) {
-  const size_t items = (size_t)a->num_seqs * a->num_kv_heads * p.num_partitions * p.cgroups;
+  const int ncg = p.ncg, cgw = p.cg_waves;
+  const size_t items = (size_t)a->num_seqs * a->num_kv_heads * p.num_partitions * cgw;
   if (items > 0x7fffffffu) return fail(PA_ERR_UNSUPPORTED, "pa_decode: grid too large");
   const float qk = a->scale * kLog2e;
   const SplitK ws = split_k(a, p);
-#define PA_MFMA_LAUNCH(KV, BS, TOKSC)                                                                           \
-  hipLaunchKernelGGL((decode_mfma_kernel<KV, BS, TOKSC>), dim3((unsigned)items), dim3(64), 0, st,               \
+#define PA_MFMA_LAUNCH1(KV, BS, TOKSC, NCG)                                                                     \
+  hipLaunchKernelGGL((decode_mfma_kernel<KV, BS, TOKSC, NCG>), dim3((unsigned)items), dim3(64), 0, st,          \
                      (float*)a->out, ws, (const unsigned short*)a->q, (char*)a->k_cache, (char*)a->v_cache,      \
                      a->k_scales, a->v_scales, a->block_tables, a->max_blocks_per_seq, a->context_lens,        \
                      a->num_q_heads, a->num_kv_heads, p.G, a->num_blocks, qk, p.partition_tokens,              \
                      p.num_partitions, (const char*)a->new_key, (const char*)a->new_value,                     \
-                     a->query_start_loc, p.cgroups)
+                     a->query_start_loc, cgw)
+#define PA_MFMA_LAUNCH(KV, BS, TOKSC)                                          \
+  do {                                                                         \
+    if (ncg == 2) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 2);                           \
+    else PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1);                                    \
+  } while (0)
 #define PA_MFMA_BS(KV, TOKSC)                              \
   if (a->block_size == 16) PA_MFMA_LAUNCH(KV, 16, TOKSC); \
   else PA_MFMA_LAUNCH(KV, 32, TOKSC)
@@ -991,6 +1026,7 @@ pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipSt
   }
 #undef PA_MFMA_BS
 #undef PA_MFMA_LAUNCH
+#undef PA_MFMA_LAUNCH1
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode (matrix-core kernel) launch");
 }

@@ -56,6 +56,8 @@ struct DecodePlan {
   int partition_tokens;  // multiple of 16
   int num_partitions;    // ceil(max_context_len / partition_tokens), >= 1
   int cgroups;           // MFMA: groups of 16 (query row, head) columns per (sequence, kv head)
+  int ncg;               // MFMA: column groups carried by one wave (1 or 2)
+  int cg_waves;          // MFMA: waves per (sequence, kv head, partition) = ceil(cgroups / ncg)
   int64_t rows;          // output rows: query rows (num_seqs, or num_queries) x num_q_heads
   size_t workspace_bytes;
 };
