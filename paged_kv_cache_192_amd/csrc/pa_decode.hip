@@ -356,7 +356,7 @@ __device__ __forceinline__ void mfma_item(int bid, int nblk, int Hkv, int nP, in
 // wave carries NCG consecutive column groups over the same K/V tiles (one
 // score MFMA chain, softmax state and accumulator set per group, V^T
 // operands built once), so K/V are read once per NCG groups.
-template <int KV, int BS, bool TOKSC, int NCG>
+template <int KV, int BS, bool TOKSC, int NCG, bool MQ>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(
     float* __restrict__ out, SplitK ws,
     const unsigned short* __restrict__ q, char* __restrict__ k_cache, char* __restrict__ v_cache,
@@ -379,14 +379,14 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   const int t_begin = p * P;
   const int t_end = min(n, t_begin + P);
   // this lane's column in each group u: output / partial row orow[u],
-  // visible tokens < lim[u]
+  // visible tokens < lim[u] (MQ: several rows per sequence, qsl given)
   bool head_ok[NCG];
   size_t orow[NCG];
   int lim[NCG];
 #pragma unroll
   for (int u = 0; u < NCG; ++u) {
     int h, qrow;
-    if (qsl) {
+    if constexpr (MQ) {
       const int q0 = qsl[s], L = qsl[s + 1] - q0;
       const int col = 16 * (cgw * NCG + u) + c, i = col / G;
       head_ok[u] = i < L;
@@ -555,7 +555,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
         float xs = qk_log2;
         if constexpr (TOKSC) xs *= ks[r];
         else if (I8) xs *= ks;
-        x[r] = (ok && tok0 + r < lim[u]) ? sc[r] * xs : kNegInf;
+        x[r] = (ok && tok0 + r < (MQ ? lim[u] : t_end)) ? sc[r] * xs : kNegInf;
       }
       float mloc = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       mloc = xor_max_rows(mloc);
@@ -997,8 +997,8 @@ pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipSt
   if (items > 0x7fffffffu) return fail(PA_ERR_UNSUPPORTED, "pa_decode: grid too large");
   const float qk = a->scale * kLog2e;
   const SplitK ws = split_k(a, p);
-#define PA_MFMA_LAUNCH1(KV, BS, TOKSC, NCG)                                                                     \
-  hipLaunchKernelGGL((decode_mfma_kernel<KV, BS, TOKSC, NCG>), dim3((unsigned)items), dim3(64), 0, st,          \
+#define PA_MFMA_LAUNCH1(KV, BS, TOKSC, NCG, MQ)                                                                 \
+  hipLaunchKernelGGL((decode_mfma_kernel<KV, BS, TOKSC, NCG, MQ>), dim3((unsigned)items), dim3(64), 0, st,      \
                      (float*)a->out, ws, (const unsigned short*)a->q, (char*)a->k_cache, (char*)a->v_cache,      \
                      a->k_scales, a->v_scales, a->block_tables, a->max_blocks_per_seq, a->context_lens,        \
                      a->num_q_heads, a->num_kv_heads, p.G, a->num_blocks, qk, p.partition_tokens,              \
@@ -1006,8 +1006,9 @@ pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipSt
                      a->query_start_loc, cgw)
 #define PA_MFMA_LAUNCH(KV, BS, TOKSC)                                          \
   do {                                                                         \
-    if (ncg == 2) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 2);                           \
-    else PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1);                                    \
+    if (!a->query_start_loc) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, false);         \
+    else if (ncg == 2) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 2, true);                \
+    else PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, true);                              \
   } while (0)
 #define PA_MFMA_BS(KV, TOKSC)                              \
   if (a->block_size == 16) PA_MFMA_LAUNCH(KV, 16, TOKSC); \
