@@ -33,10 +33,13 @@ static bool valid_scale_mode(int m) { return m == PA_SCALE_BLOCK || m == PA_SCAL
 // matrix-core kernel keeps two 16-token tiles in flight per wave: with a
 // bf16 cache that is 16 KB, and about 2.5 waves per CU (~40 KB of loads in
 // flight per CU) measured fastest on the 70B-shaped layer, while five per
-// CU lost 10 %.  Int8 tiles are half the size, so twice the waves.  The
-// vector-ALU kernel keeps one tile in flight; five waves per CU.
+// CU lost 10 %.  1-byte tiles carry half the bytes for the same arithmetic:
+// on the same layer with int8 or E4M3 codes, 10 waves per CU (512-token
+// partitions) measured 61-65 % of peak against 52-58 % at 5 per CU and
+// 38-49 % at 2.5.  The vector-ALU kernel keeps one tile in flight; five
+// waves per CU.
 static int target_waves(KernelKind kind, pa_dtype kv) {
-  if (kind == KERNEL_MFMA) return kv == PA_I8 ? 1280 : 640;
+  if (kind == KERNEL_MFMA) return quantised(kv) ? 2560 : 640;
   return 1280;
 }
 
