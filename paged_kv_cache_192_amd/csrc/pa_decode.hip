@@ -120,8 +120,8 @@ struct SplitK {
 // groups w, w + W, ...; groups after a wave's first rescale its running
 // sums to the new maximum.  With W > 1 the waves' (m, L, acc) are combined
 // through LDS the same way, in wave order.  W = 1 when every row has at
-// most 16 partitions; long ragged rows get W = 4 so their merge takes a
-// quarter of the round trips.
+// most 16 partitions; plans with up to 32, 64 or more partitions get W = 2,
+// 4 or 8, so a long ragged row needs about one round trip per wave.
 template <int D, int W>
 __global__ __launch_bounds__(64 * W) void decode_merge_kernel(float* __restrict__ out, SplitK ws,
                                                               const int32_t* __restrict__ context_lens, int Hq,
@@ -1094,7 +1094,8 @@ static void merge_dispatch(const pa_decode_args* a, const DecodePlan& p, hipStre
                      p.num_partitions, max_tokens)
   if (p.num_partitions <= 16) PA_MERGE_LAUNCH(1);
   else if (p.num_partitions <= 32) PA_MERGE_LAUNCH(2);
-  else PA_MERGE_LAUNCH(4);
+  else if (p.num_partitions <= 64) PA_MERGE_LAUNCH(4);
+  else PA_MERGE_LAUNCH(8);
 #undef PA_MERGE_LAUNCH
 }
 

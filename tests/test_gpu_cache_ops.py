@@ -112,6 +112,27 @@ def test_copy_blocks_bit_exact(dt, H, BS, D):
         assert np.array_equal(to_host(dks), ks) and np.array_equal(to_host(dvs), vs)
 
 
+@pytest.mark.parametrize("dt", [np.int8, np.uint8], ids=["i8", "e4m3"])
+def test_copy_blocks_per_token_scales(dt):
+    """Quantised caches with one scale per token: every scale of a copied
+    block moves with it ([NB][Hkv][BS] layout), others stay."""
+    rng = np.random.default_rng(31 + (dt == np.uint8))
+    NB, H, BS, D = 64, 8, 16, 128
+    kc = rng.integers(0, 256, (NB, H, BS, D), dtype=np.uint8).view(dt)
+    vc = rng.integers(0, 256, (NB, H, BS, D), dtype=np.uint8).view(dt)
+    ks = rng.random((NB, H, BS)).astype(np.float32)
+    vs = rng.random((NB, H, BS)).astype(np.float32)
+    ids = rng.permutation(NB)
+    pairs = np.stack([ids[:20], ids[20:40]], axis=1).astype(np.int64)
+    say("copy_blocks per-token scales", dt.__name__)
+    dk, dv, dks, dvs = to_dev(kc), to_dev(vc), to_dev(ks), to_dev(vs)
+    pa.copy_blocks(dk, dv, to_dev(pairs), dks, dvs)
+    oracle.copy_blocks(kc, vc, pairs, ks, vs, scale_mode=oracle.SCALE_TOKEN)
+    assert np.array_equal(to_host(dk).view(np.uint8), kc.view(np.uint8))
+    assert np.array_equal(to_host(dv).view(np.uint8), vc.view(np.uint8))
+    assert np.array_equal(to_host(dks), ks) and np.array_equal(to_host(dvs), vs)
+
+
 def test_copy_blocks_skips_out_of_range_pairs():
     rng = np.random.default_rng(9)
     NB, H, BS, D = 6, 2, 16, 64
