@@ -90,15 +90,15 @@ def cpu_model() -> str:
 
 # HBM bytes of one pa_decode call on the 70B-shaped layer (decode + merge
 # kernels, fused cache write), from rocprofv3 --pmc FETCH_SIZE and
-# WRITE_SIZE runs: FETCH_SIZE scaled by 1.99221 and WRITE_SIZE by 1.0, the
+# WRITE_SIZE runs: FETCH_SIZE scaled by 1.99226 and WRITE_SIZE by 1.0, the
 # ratios of a plain copy's known bytes to what the same counters read for it
 # (profiles/decode_mfma_llama3-70b_pmc_traffic.md).  Valid only for the
 # sources the counters were taken on: a changed kernel or plan reports null.
 PMC_TRAFFIC = {
-    "sources_sha256": "7163aa97ff9ea20d6fe40c957531b62d40540c38230316e6f89cbc8fdc7838d1",
-    "fetch_kib": 321000.2 + 1391.0,
+    "sources_sha256": "adf1320b868a469157b40e39712171e54757f85fd121622c1d938213ef6b9683",
+    "fetch_kib": 320978.8 + 1384.5,
     "write_kib": 2680.0 + 640.0,
-    "fetch_factor": 1.99221,
+    "fetch_factor": 1.99226,
     "write_factor": 1.0,
 }
 PMC_SOURCES = ("paged_kv_cache_192_amd/csrc/pa_decode.hip", "paged_kv_cache_192_amd/csrc/pa_api.cpp",
@@ -422,10 +422,16 @@ def run_single_layer(args) -> dict:
         valid = synth.valid_slots_per_block(case)
         uniq = 2 * Hkv * D * e * int(valid.sum())
         copy = 2 * 2 * len(case.extra["scratch"]) * Hkv * BS * D * e
+        # the HBM lower bound of the step: unique K/V, tables, q, out, and the
+        # copy's reads and writes; the logical rate is reported as effective
+        unique_alg = alg - kvb + uniq + copy
         res["unique_kv_bytes_per_layer"] = uniq
         res["copy_bytes_per_layer"] = copy
         res["unique_kv_gbs"] = round(uniq / (ms_layer * 1e-3) / 1e9, 1)
-        res["effective_kv_gbs_note"] = "kv_gbs counts each sequence's prefix (logical bytes)"
+        res["effective_pct_hbm_peak"] = res["pct_hbm_peak"]
+        res["pct_hbm_peak"] = round(100.0 * unique_alg / (ms_layer * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)
+        res["effective_kv_gbs_note"] = ("kv_gbs and effective_pct_hbm_peak count each sequence's prefix (logical "
+                                        "bytes); pct_hbm_peak counts each physical block once plus the copy")
     res["waste"] = waste_report(cls, BS, 2048 if w != "int8" else 32768)
     return res
 
