@@ -149,8 +149,10 @@ int32_t pa_abi_version(void);
  * the cache and counted in context_lens[s] = n.  Row i of them sits at
  * position n - L_s + i and attends causally to positions 0 .. n - L_s + i
  * (a row that would see no token gets zeros).  max_query_len (host) bounds
- * L_s.  Matrix-core kernel only (bf16 queries, head_dim 128); no fused
- * cache write.
+ * L_s; rows whose index falls outside [0, num_queries) (offsets that do not
+ * match num_queries, a caller error) are neither read nor written.
+ * Matrix-core kernel only (bf16 queries, head_dim 128); no fused cache
+ * write.
  *
  * `kernel` selects the implementation: 0 = automatic, 1 = vector-ALU
  * kernel (any supported case), 2 = matrix-core kernel (bf16, int8 or E4M3

@@ -363,7 +363,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     const float* __restrict__ k_scales, const float* __restrict__ v_scales, const int32_t* __restrict__ tables,
     int max_blocks, const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int NB, float qk_log2,
     int P, int nP, const char* __restrict__ new_k, const char* __restrict__ new_v,
-    const int32_t* __restrict__ qsl, int CG) {
+    const int32_t* __restrict__ qsl, int CG, int num_rows) {
   constexpr int D = 128;
   constexpr bool I8 = KV != kKvBf16;  // 1-byte codes with fp32 scales
   constexpr int E = I8 ? 1 : 2;
@@ -389,7 +389,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     if constexpr (MQ) {
       const int q0 = qsl[s], L = qsl[s + 1] - q0;
       const int col = 16 * (cgw * NCG + u) + c, i = col / G;
-      head_ok[u] = i < L;
+      // rows outside [0, num_rows) (offsets not matching num_queries, a
+      // caller error) are neither read nor written
+      head_ok[u] = i < L && q0 + i >= 0 && q0 + i < num_rows;
       h = g * G + col % G;
       qrow = q0 + i;
       lim[u] = head_ok[u] ? max(0, min(t_end, n - L + i + 1)) : 0;
@@ -1003,7 +1005,7 @@ pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipSt
                      a->k_scales, a->v_scales, a->block_tables, a->max_blocks_per_seq, a->context_lens,        \
                      a->num_q_heads, a->num_kv_heads, p.G, a->num_blocks, qk, p.partition_tokens,              \
                      p.num_partitions, (const char*)a->new_key, (const char*)a->new_value,                     \
-                     a->query_start_loc, cgw)
+                     a->query_start_loc, cgw, a->query_start_loc ? a->num_queries : a->num_seqs)
 #define PA_MFMA_LAUNCH(KV, BS, TOKSC)                                          \
   do {                                                                         \
     if (!a->query_start_loc) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, false);         \

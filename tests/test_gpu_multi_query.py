@@ -72,3 +72,25 @@ def test_single_row_queries_match_decode():
                       partition_tokens=P, query_start_loc=to_dev(qsl), max_query_len=1)
         torch.cuda.synchronize()
         assert torch.equal(a, b)
+
+
+def test_offsets_past_num_queries_touch_nothing_outside():
+    """query_start_loc ending past num_queries (a caller error): rows beyond
+    num_queries are skipped, so memory after q and out is never touched
+    (both are views into larger buffers holding sentinels), and the rows
+    inside still equal the oracle's."""
+    case, q, qsl, maxq = _mq_case(MQ_SHAPES[0], 520)
+    R = int(qsl[-1])
+    keep = R - 5                                  # the call is told only keep rows exist
+    d = case_on_device(case)
+    q_big = to_dev(q)
+    out_big = torch.full((R, case.num_q_heads, 128), 7.0, dtype=torch.float32, device="cuda:0")
+    say("multi-query offsets past num_queries")
+    pa.decode(q_big[:keep], d["k"], d["v"], d["bt"], d["cl"], float(case.scale), case.max_context_len,
+              out=out_big[:keep], partition_tokens=256, query_start_loc=to_dev(qsl), max_query_len=maxq)
+    torch.cuda.synchronize()
+    got = out_big.cpu().numpy().astype(np.float64)
+    assert np.all(got[keep:] == 7.0)
+    expect = oracle.paged_attention(q, case.k_cache, case.v_cache, case.block_tables, case.context_lens, qsl,
+                                    float(case.scale))
+    assert max_err(got[:keep], expect[:keep]) <= TOL_BF16
