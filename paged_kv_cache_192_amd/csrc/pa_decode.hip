@@ -374,6 +374,15 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   const int c = lane & 15;
   int s, g, p, cgw;
   mfma_item(blockIdx.x, gridDim.x, Hkv, nP, CG, s, g, p, cgw);
+  // The partition's table entries, two per lane (a partition spans at most
+  // 128 blocks, which the host guarantees): entry i of the partition is
+  // lane i of tbl0 or lane i - 64 of tbl1.  They are read before the
+  // context length is known, so the two loads overlap; entries past the
+  // sequence's blocks (inside the table row) are read and never used.
+  const int32_t* trow = tables + (size_t)s * max_blocks;
+  const int tbl_base = (p * P) / BS;
+  const int tbl0 = (tbl_base + lane < max_blocks) ? trow[tbl_base + lane] : -1;
+  const int tbl1 = (tbl_base + 64 + lane < max_blocks) ? trow[tbl_base + 64 + lane] : -1;
   // a length past the table row is a caller error; never read beyond the row
   const int n = min(context_lens[s], max_blocks * BS);
   const int t_begin = p * P;
@@ -434,16 +443,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       qf[u][kk] = as_bf16x8(w);
     }
 
-  const int32_t* trow = tables + (size_t)s * max_blocks;
   const int tile_begin = t_begin >> 4;
   const int tile_end = (t_end + 15) >> 4;
-  const int seq_blocks = (n + BS - 1) / BS;
-  // The partition's table entries, two per lane (a partition spans at most
-  // 128 blocks, which the host guarantees): entry i of the partition is
-  // lane i of tbl0 or lane i - 64 of tbl1.
-  const int tbl_base = t_begin / BS;
-  const int tbl0 = (tbl_base + lane < seq_blocks) ? trow[tbl_base + lane] : -1;
-  const int tbl1 = (tbl_base + 64 + lane < seq_blocks) ? trow[tbl_base + 64 + lane] : -1;
 
   constexpr int ROW = D * E;                       // bytes per token row
   const size_t head_stride = (size_t)BS * ROW;     // bytes per (block, kv head)
