@@ -322,7 +322,9 @@ def run_single_layer(args) -> dict:
     walks all replicas; per-layer time = step time / R.  The new token's
     cache write is fused into pa_decode (not for int8: no quantising
     write); the prefix workload also copies the shared partial block to 50
-    scratch blocks per layer (pa_copy_blocks) before decoding."""
+    scratch blocks per layer (pa_copy_blocks) before decoding, and passes
+    the 62 shared full blocks as the decode's shared prefix (unless
+    --no-shared-prefix)."""
     import numpy as np
     import torch
 
@@ -362,9 +364,14 @@ def run_single_layer(args) -> dict:
     newk = torch.randn(S, Hkv, D, generator=gen, device=dev).to(tdt) if w != "int8" else None
     newv = torch.randn(S, Hkv, D, generator=gen, device=dev).to(tdt) if w != "int8" else None
     pairs = None
+    shared, shared_len = None, 0
     if w == "prefix":
         pr = np.stack([np.full(S, case.extra["partial"]), case.extra["scratch"]], axis=1).astype(np.int64)
         pairs = put(pr)
+        if args.shared_prefix:
+            # the 62 full blocks every table starts with, read once per layer
+            shared = put(case.extra["shared"].astype(np.int32))
+            shared_len = len(case.extra["shared"]) * BS
     outs = [torch.empty(S, Hq, D, dtype=torch.float32, device=dev) for _ in range(R)]
     ws = torch.zeros(1 << 26, dtype=torch.uint8, device=dev)
     mcl = case.max_context_len
@@ -377,7 +384,8 @@ def run_single_layer(args) -> dict:
             calls.append(pa.PreparedDecode(q, K[r], V[r], bt, cl, float(case.scale), mcl, outs[r], k_scales=ks,
                                            v_scales=vs, workspace=ws, stream=stream, new_key=newk, new_value=newv,
                                            partition_tokens=args.partition_tokens, kernel=args.kernel,
-                                           total_context_len=int(np.sum(case.context_lens, dtype=np.int64))))
+                                           total_context_len=int(np.sum(case.context_lens, dtype=np.int64)),
+                                           shared_prefix_table=shared, shared_prefix_len=shared_len))
         return calls
 
     main = torch.cuda.current_stream()
@@ -416,7 +424,8 @@ def run_single_layer(args) -> dict:
            "pct_hbm_peak": round(100.0 * alg / (ms_layer * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
            "algorithmic_bytes_per_layer": alg, "kv_bytes_per_layer": kvb, "sum_ctx": int(sum(int(x) for x in cls)),
            "step": ("copy_blocks + " if pairs is not None else "") + "pa_decode" +
-                   (" with fused cache write" if newk is not None else "")}
+                   (" with fused cache write" if newk is not None else "") +
+                   (" and the shared prefix's %d blocks passed" % (shared_len // BS) if shared_len else "")}
     if w == "prefix":
         # unique bytes: every physical block's valid tokens once
         valid = synth.valid_slots_per_block(case)
@@ -695,6 +704,8 @@ def main():
                     help="override the library's automatic split-K partition length (tuning only)")
     ap.add_argument("--kernel", type=int, default=0, choices=[0, 1, 2],
                     help="decode kernel of the one-layer workloads: 0 library's choice, 1 vector-ALU, 2 matrix-core")
+    ap.add_argument("--no-shared-prefix", dest="shared_prefix", action="store_false",
+                    help="prefix workload: do not pass the shared prefix's blocks to pa_decode")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="llama3-70b",
                     help="the 70B-shaped 80-layer step (default; the JSON metric line) or one of the single-layer "
                          "workloads, reported as a per-layer record")

@@ -73,7 +73,7 @@ const char* pa_status_string(pa_status s);
 /* Message of the last failure on the calling thread ("" if none). */
 const char* pa_last_error(void);
 /* ABI version of this header (incremented on any incompatible change). */
-#define PA_ABI_VERSION 5
+#define PA_ABI_VERSION 6
 int32_t pa_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -154,6 +154,21 @@ int32_t pa_abi_version(void);
  * Matrix-core kernel only (bf16 queries, head_dim 128); no fused cache
  * write.
  *
+ * Shared prefix (optional): when every sequence's first shared_prefix_len
+ * tokens are the blocks shared_prefix_table[0 .. shared_prefix_len/BS - 1]
+ * (a common prompt stored once: glossary, section 3, scenario 01; ia-vox,
+ * prefix sharing), passing them lets the call read those blocks once for
+ * the whole batch instead of once per sequence.  The result is the same
+ * attention; a sequence shorter than the prefix sees only its own length
+ * of it.  The caller guarantees that every table row starts with these
+ * blocks.  With new_key/new_value, a sequence whose newest token lies
+ * inside the prefix (context_lens[s] <= shared_prefix_len) has its row
+ * neither stored nor attended (a shared block is never written; its
+ * cached token is used).  Used by the matrix-core kernel with one query
+ * row per sequence, otherwise ignored; a given partition_tokens then sets
+ * the partition length of both the prefix and the per-sequence part.
+ * shared_prefix_table is a device int32 array (4-byte aligned).
+ *
  * `kernel` selects the implementation: 0 = automatic, 1 = vector-ALU
  * kernel (any supported case), 2 = matrix-core kernel (bf16, int8 or E4M3
  * caches with bf16 queries, head_dim 128, 1..16 query heads per kv head;
@@ -194,6 +209,8 @@ typedef struct {
   const int32_t* query_start_loc; /* NULL = one query row per sequence; else [num_seqs + 1] row offsets */
   int32_t num_queries;           /* with query_start_loc: total query rows (= query_start_loc[num_seqs]) */
   int32_t max_query_len;         /* with query_start_loc: host bound on the rows of one sequence, >= 1 */
+  const int32_t* shared_prefix_table; /* optional: blocks of a prefix every sequence starts with */
+  int32_t shared_prefix_len;     /* tokens of that prefix (multiple of block_size, <= max_context_len), 0 = none */
 } pa_decode_args;
 
 /* Host only: bytes of workspace pa_decode needs for these arguments

@@ -21,7 +21,7 @@ PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_OOM, PA_ERR_STATE, PA_ERR_HIP 
 PA_F32, PA_BF16, PA_I8, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_SCALE_BLOCK, PA_SCALE_TOKEN = 0, 1
 KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA = 0, 1, 2
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_INVALID", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_OOM",
                 4: "PA_ERR_STATE", 5: "PA_ERR_HIP"}
@@ -71,6 +71,8 @@ class DecodeArgs(ctypes.Structure):
         ("query_start_loc", ctypes.c_void_p),
         ("num_queries", ctypes.c_int32),
         ("max_query_len", ctypes.c_int32),
+        ("shared_prefix_table", ctypes.c_void_p),
+        ("shared_prefix_len", ctypes.c_int32),
     ]
 
 
@@ -195,14 +197,16 @@ def make_decode_args(q, k_cache, v_cache, block_tables, context_lens, scale: flo
                      out=None, k_scales=None, v_scales=None, workspace=None, partition_tokens: int = 0,
                      kernel: int = KERNEL_AUTO, stream=None, device_pointers: bool = True, new_key=None,
                      new_value=None, total_context_len: int = 0, query_start_loc=None,
-                     max_query_len: int = 0) -> DecodeArgs:
+                     max_query_len: int = 0, shared_prefix_table=None, shared_prefix_len: int = 0) -> DecodeArgs:
     """Fill a DecodeArgs from tensors.  q ``[S][Hq][D]``; caches
     ``[NB][Hkv][BS][D]``; block_tables int32 ``[S][max_blocks]``;
     context_lens int32 ``[S]``; out float32 ``[S][Hq][D]``; optional
     new_key/new_value ``[S][Hkv][D]`` for the fused cache write;
     total_context_len: optional sum of the context lengths (partition
     hint, 0 = unknown); query_start_loc int32 ``[S+1]`` with max_query_len:
-    several causal query rows per sequence (q and out ``[R][Hq][D]``)."""
+    several causal query rows per sequence (q and out ``[R][Hq][D]``);
+    shared_prefix_table int32 ``[shared_prefix_len / BS]``: blocks every
+    table row starts with (read once for the whole batch)."""
     R, Hq, D = q.shape
     S = int(context_lens.shape[0])
     if query_start_loc is None and R != S:
@@ -252,6 +256,11 @@ def make_decode_args(q, k_cache, v_cache, block_tables, context_lens, scale: flo
         a.query_start_loc = get(query_start_loc)
         a.num_queries = R
         a.max_query_len = int(max_query_len)
+    if shared_prefix_table is not None:
+        if shared_prefix_table.dim() != 1 or int(shared_prefix_table.shape[0]) * BS != int(shared_prefix_len):
+            raise ValueError("shared_prefix_table must be int32 [shared_prefix_len / block_size]")
+        a.shared_prefix_table = get(shared_prefix_table)
+    a.shared_prefix_len = int(shared_prefix_len)
     return a
 
 
@@ -264,7 +273,7 @@ def decode_workspace_size(args: DecodeArgs) -> int:
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int, out=None,
            k_scales=None, v_scales=None, workspace=None, partition_tokens: int = 0, kernel: int = KERNEL_AUTO,
            stream=None, new_key=None, new_value=None, total_context_len: int = 0, query_start_loc=None,
-           max_query_len: int = 0):
+           max_query_len: int = 0, shared_prefix_table=None, shared_prefix_len: int = 0):
     """Paged decode attention (``pa_decode``).  Returns ``out`` (float32
     ``[S][Hq][D]``), allocated on q's device when not given.  A workspace
     is allocated when the plan needs one and none is passed (its contents
@@ -276,7 +285,8 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_co
                             k_scales=k_scales, v_scales=v_scales, workspace=workspace,
                             partition_tokens=partition_tokens, kernel=kernel, stream=stream, new_key=new_key,
                             new_value=new_value, total_context_len=total_context_len,
-                            query_start_loc=query_start_loc, max_query_len=max_query_len)
+                            query_start_loc=query_start_loc, max_query_len=max_query_len,
+                            shared_prefix_table=shared_prefix_table, shared_prefix_len=shared_prefix_len)
     need = decode_workspace_size(args)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -416,13 +426,14 @@ class PreparedDecode:
     def __init__(self, q, k_cache, v_cache, block_tables, context_lens, scale: float, max_context_len: int, out,
                  k_scales=None, v_scales=None, workspace=None, partition_tokens: int = 0, kernel: int = KERNEL_AUTO,
                  stream=None, new_key=None, new_value=None, total_context_len: int = 0, query_start_loc=None,
-                 max_query_len: int = 0):
+                 max_query_len: int = 0, shared_prefix_table=None, shared_prefix_len: int = 0):
         torch = _torch()
         self.args = make_decode_args(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
                                      out=out, k_scales=k_scales, v_scales=v_scales, workspace=workspace,
                                      partition_tokens=partition_tokens, kernel=kernel, stream=stream,
                                      new_key=new_key, new_value=new_value, total_context_len=total_context_len,
-                                     query_start_loc=query_start_loc, max_query_len=max_query_len)
+                                     query_start_loc=query_start_loc, max_query_len=max_query_len,
+                                     shared_prefix_table=shared_prefix_table, shared_prefix_len=shared_prefix_len)
         need = decode_workspace_size(self.args)
         if need and (workspace is None or self.args.workspace_bytes < need):
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -430,7 +441,7 @@ class PreparedDecode:
             self.args.workspace_bytes = need
         self.workspace_bytes = need
         self._keep = (q, k_cache, v_cache, block_tables, context_lens, out, k_scales, v_scales, workspace, new_key,
-                      new_value, query_start_loc)
+                      new_value, query_start_loc, shared_prefix_table)
         self._fn = library().pa_decode
         self._ref = ctypes.byref(self.args)
 

@@ -50,6 +50,11 @@ static int target_waves(KernelKind kind, pa_dtype kv) {
 // lengths (int8 and bf16 caches): ~5,000 waves of <= 16 tiles beat both
 // fewer longer waves and more shorter ones.
 constexpr int64_t kRaggedWaves = 5120;
+// Waves for the items over a shared prefix.  Measured on the prefix-sharing
+// layer (50 sequences, 1,984 shared tokens, 32/8 heads): 2 partitions of
+// 62 tiles (~1,000 waves) beat 4 to 16 shorter ones, whose extra partials
+// cost the merge more than the shorter chains save.
+constexpr int64_t kPrefixWaves = 1024;
 static bool is_ragged(const pa_decode_args* a, int64_t total) {
   return total * 4 < (int64_t)a->num_seqs * a->max_context_len * 3;
 }
@@ -95,6 +100,14 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
                 a->partition_tokens, kMaxPartitionBlocks);
   if (a->kernel < 0 || a->kernel > 2) return fail(PA_ERR_INVALID, "pa_decode: kernel %d not in {0, 1, 2}", a->kernel);
   const bool mq = a->query_start_loc != nullptr;
+  if (a->shared_prefix_len < 0 || (a->shared_prefix_len > 0 && !a->shared_prefix_table))
+    return fail(PA_ERR_INVALID, "pa_decode: shared_prefix_len %d needs shared_prefix_table", a->shared_prefix_len);
+  if (a->shared_prefix_len % a->block_size)
+    return fail(PA_ERR_INVALID, "pa_decode: shared_prefix_len %d is not a multiple of block_size %d",
+                a->shared_prefix_len, a->block_size);
+  if (a->shared_prefix_len > a->max_context_len)
+    return fail(PA_ERR_INVALID, "pa_decode: shared_prefix_len %d exceeds max_context_len %d", a->shared_prefix_len,
+                a->max_context_len);
   if (mq && (a->num_queries < 0 || a->max_query_len < 1))
     return fail(PA_ERR_INVALID, "pa_decode: with query_start_loc, num_queries >= 0 and max_query_len >= 1");
   if (mq && a->new_key)
@@ -134,44 +147,85 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   p->cg_waves = (int)((cg + p->ncg - 1) / p->ncg);
   p->rows = (int64_t)(mq ? a->num_queries : (a->num_seqs > 0 ? a->num_seqs : 0)) * a->num_q_heads;
 
-  const int64_t tiles = a->max_context_len > 0 ? (a->max_context_len + 15) / 16 : 1;
   const int64_t max_tiles = (int64_t)kMaxPartitionBlocks * a->block_size / 16;
-  int P = a->partition_tokens;
   const int64_t total = a->total_context_len > 0 ? a->total_context_len : seq_tokens;
-  if (P == 0 && a->num_seqs > 0 && !mq && is_ragged(a, total)) {
-    // Waves of one (sequence, kv head, head group): about total/P + S/2
-    // partitions each; choose P for ~kRaggedWaves waves, at least 4 tiles,
-    // at most kMaxPartitionBlocks blocks, and at most kMaxRaggedPartitions
-    // partitions per sequence.
-    const int64_t per_seq = (int64_t)a->num_kv_heads * p->head_groups;
-    int64_t room = kRaggedWaves - per_seq * a->num_seqs / 2;
-    if (room < kRaggedWaves / 4) room = kRaggedWaves / 4;
-    int64_t per = (per_seq * total + 16 * room - 1) / (16 * room);  // tiles per partition
-    const int64_t min_per = (tiles + kMaxRaggedPartitions - 1) / kMaxRaggedPartitions;
-    if (per < min_per) per = min_per;
-    if (per < 4) per = 4;
-    if (per > max_tiles) per = max_tiles;
-    if (per > tiles) per = tiles;
-    P = (int)(16 * per);
-  } else if (P == 0) {
-    // Split each sequence into nP equal partitions so the grid holds about
-    // target_waves() waves, within [4 tiles, kMaxPartitionBlocks blocks] per
-    // partition and at most kMaxAutoPartitions partitions.
-    const int64_t groups =
-        (int64_t)(a->num_seqs > 0 ? a->num_seqs : 1) * a->num_kv_heads * p->head_groups * p->cg_waves;
-    // a wave carrying two column groups does twice the arithmetic per tile:
-    // twice the waves keep the same bytes in flight per unit of compute
-    const int64_t target = target_waves(kind, a->kv_dtype) * p->ncg;
-    int64_t nP = (target + groups / 2) / groups;
+  const int64_t target = target_waves(kind, a->kv_dtype);
+
+  // Partition length for `seqs` sequences of at most max_len tokens (sum
+  // total_len), each split over `per_seq` items per partition of `wpi`
+  // waves each (the waves of an item share its tiles); `wave_mult` scales
+  // the wave target (waves carrying two column groups), `tgt` replaces it.
+  auto choose_split = [&](int64_t max_len, int64_t total_len, int64_t seqs, int64_t per_seq, int64_t wave_mult,
+                          bool ragged_ok, int64_t wpi = 1, int64_t tgt = 0) -> int {
+    const int64_t tiles = max_len > 0 ? (max_len + 15) / 16 : 1;
+    if (ragged_ok && seqs > 0 && total_len * 4 < seqs * max_len * 3) {
+      // Ragged lengths: about total/P + S/2 partitions per wave column;
+      // choose P for ~kRaggedWaves waves, at least 4 tiles per wave, at
+      // most kMaxPartitionBlocks blocks and kMaxRaggedPartitions partitions.
+      int64_t room = kRaggedWaves - per_seq * wpi * seqs / 2;
+      if (room < kRaggedWaves / 4) room = kRaggedWaves / 4;
+      int64_t per = (per_seq * wpi * total_len + 16 * room - 1) / (16 * room);  // tiles per partition
+      const int64_t min_per = (tiles + kMaxRaggedPartitions - 1) / kMaxRaggedPartitions;
+      if (per < min_per) per = min_per;
+      if (per < 4 * wpi) per = 4 * wpi;
+      if (per > max_tiles) per = max_tiles;
+      if (per > tiles) per = tiles;
+      return (int)(16 * per);
+    }
+    // Near-equal lengths: nP equal partitions so the grid holds about
+    // target waves, within [4 tiles per wave, kMaxPartitionBlocks blocks]
+    // per partition and at most kMaxAutoPartitions partitions.
+    const int64_t groups = (seqs > 0 ? seqs : 1) * per_seq * wpi;
+    const int64_t tw = (tgt ? tgt : target) * wave_mult;
+    int64_t nP = (tw + groups / 2) / groups;
     if (nP < 1) nP = 1;
     if (nP > kMaxAutoPartitions) nP = kMaxAutoPartitions;
-    if (nP > (tiles + 3) / 4) nP = (tiles + 3) / 4;
+    if (nP > (tiles + 4 * wpi - 1) / (4 * wpi)) nP = (tiles + 4 * wpi - 1) / (4 * wpi);
     int64_t per = (tiles + nP - 1) / nP;
     if (per > max_tiles) per = max_tiles;
-    P = (int)(16 * per);
+    return (int)(16 * per);
+  };
+
+  // Shared prefix (cascade): every sequence's first shared_prefix_len tokens
+  // are the blocks of shared_prefix_table.  Prefix items attend all
+  // sequences' queries to those blocks (K/V read once per 16 columns of
+  // sequences x query heads), the other items each sequence to the rest of
+  // its tokens, in one launch of kCascadeWaves-wave items; the merge
+  // combines both.  Matrix-core kernel, one query row per sequence;
+  // otherwise the hint is ignored.  The prefix's tiles are re-read by every
+  // column group (mostly from cache), so its items are latency-bound, not
+  // bandwidth-bound: they get kPrefixWaves waves.  The rest of each
+  // sequence is split by the near-equal rule; with S x Hkv items of 4
+  // waves above the wave target it stays one partition per sequence.
+  p->cascade = false;
+  p->prefix_partitions = 0;
+  if (a->shared_prefix_len > 0 && kind == KERNEL_MFMA && !mq && a->num_seqs > 0) {
+    // A given partition_tokens sets both passes' partition length.
+    p->cascade = true;
+    const int64_t pcg = ((int64_t)G * a->num_seqs + 15) / 16;
+    p->prefix_cgroups = (int)pcg;
+    const int Pp = a->partition_tokens ? a->partition_tokens
+                                       : choose_split(a->shared_prefix_len, a->shared_prefix_len, 1,
+                                                      (int64_t)a->num_kv_heads * pcg, 1, false, kCascadeWaves,
+                                                      kPrefixWaves);
+    p->prefix_tokens = Pp;
+    p->prefix_partitions = (a->shared_prefix_len + Pp - 1) / Pp;
+    const int64_t rest_max = a->max_context_len - a->shared_prefix_len;
+    const int64_t rest_total = total - (int64_t)a->num_seqs * a->shared_prefix_len;
+    const int P = a->partition_tokens ? a->partition_tokens
+                                      : choose_split(rest_max, rest_total > 0 ? rest_total : 0, a->num_seqs,
+                                                     a->num_kv_heads, 1, false, kCascadeWaves);
+    p->partition_tokens = P;
+    p->num_partitions = rest_max > 0 ? (int)((rest_max + P - 1) / P) : 0;
+  } else {
+    int P = a->partition_tokens;
+    if (P == 0)
+      P = choose_split(a->max_context_len, total, a->num_seqs, (int64_t)a->num_kv_heads * p->head_groups *
+                       p->cg_waves, p->ncg, !mq);
+    p->partition_tokens = P;
+    p->num_partitions = a->max_context_len > 0 ? (a->max_context_len + P - 1) / P : 1;
   }
-  p->partition_tokens = P;
-  p->num_partitions = a->max_context_len > 0 ? (a->max_context_len + P - 1) / P : 1;
+  p->ws_partitions = p->prefix_partitions + p->num_partitions;
   p->workspace_bytes = workspace_layout(a, *p).bytes;
   return PA_OK;
 }
@@ -216,6 +270,8 @@ pa_status pa_decode(const pa_decode_args* a) {
     return fail(PA_ERR_INVALID, "pa_decode: a required device pointer is NULL");
   if (a->query_start_loc && !aligned(a->query_start_loc, 4))
     return fail(PA_ERR_INVALID, "pa_decode: query_start_loc must be 4-byte aligned");
+  if (a->shared_prefix_len > 0 && !aligned(a->shared_prefix_table, 4))
+    return fail(PA_ERR_INVALID, "pa_decode: shared_prefix_table must be 4-byte aligned");
   if (!aligned(a->out, 16) || !aligned(a->q, 16) || !aligned(a->k_cache, 16) || !aligned(a->v_cache, 16) ||
       !aligned(a->new_key, 16) || !aligned(a->new_value, 16))
     return fail(PA_ERR_INVALID, "pa_decode: out, q, the caches and new_key/new_value must be 16-byte aligned");
@@ -232,7 +288,7 @@ pa_status pa_decode(const pa_decode_args* a) {
   }
   hipStream_t st = (hipStream_t)a->stream;
   s = p.kind == KERNEL_MFMA ? launch_decode_mfma(a, p, st) : launch_decode_valu(a, p, st);
-  if (s != PA_OK || p.num_partitions == 1) return s;
+  if (s != PA_OK || p.ws_partitions == 1) return s;
   return launch_decode_merge(a, p, st);
 }
 

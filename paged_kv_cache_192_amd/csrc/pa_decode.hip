@@ -344,6 +344,30 @@ __device__ __forceinline__ void mfma_item(int bid, int nblk, int Hkv, int nP, in
   }
 }
 
+// A shared prefix (cascade): the first items of the grid attend every
+// sequence's query row to the blocks of one shared table -- a "virtual
+// sequence" whose columns are (sequence, head) pairs, 16 per column group,
+// each lane masking to its own sequence's length -- so each prefix K/V tile
+// is read once per column group instead of once per sequence; the other
+// items attend each sequence to its tokens from t0 = prefix length on.
+// Both write partials: prefix partition p at slot p, the sequence's
+// partition p at slot nPp + p, of nPw slots per row.  An item of a cascade
+// launch is a workgroup of kCascadeWaves waves: wave w takes tiles
+// tile_begin + w, + 2w, ... of the partition (chains a quarter as long,
+// the neighbouring tiles in flight together) and the waves' (m, l, acc)
+// are combined through LDS before the one partial is written.
+struct Cascade {
+  const int32_t* table;  // shared prefix blocks (NULL: no prefix items)
+  int blocks;            // prefix length / BS
+  int items;             // prefix items = Hkv * nP * CG, first in the grid
+  int nP, P, CG;         // prefix partitions, their length, column groups
+  int t0;                // first token of the per-sequence items
+  int nPw;               // partial slots per output row (1: write out directly)
+};
+
+constexpr int kModeDecode = 0, kModeMultiQuery = 1, kModeCascade = 2;
+static_assert(kCascadeWaves == 1 || kCascadeWaves == 2 || kCascadeWaves == 4, "1, 2 or 4 waves per item");
+
 // KV: kKvBf16, kKvI8 or kKvFp8 cache; TOKSC: quantised cache with one scale
 // per token ([NB][Hkv][BS]) instead of one per (block, kv head).
 //
@@ -356,37 +380,54 @@ __device__ __forceinline__ void mfma_item(int bid, int nblk, int Hkv, int nP, in
 // wave carries NCG consecutive column groups over the same K/V tiles (one
 // score MFMA chain, softmax state and accumulator set per group, V^T
 // operands built once), so K/V are read once per NCG groups.
-template <int KV, int BS, bool TOKSC, int NCG, bool MQ>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(
+template <int KV, int BS, bool TOKSC, int NCG, int MODE>
+__global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) void decode_mfma_kernel(
     float* __restrict__ out, SplitK ws,
     const unsigned short* __restrict__ q, char* __restrict__ k_cache, char* __restrict__ v_cache,
     const float* __restrict__ k_scales, const float* __restrict__ v_scales, const int32_t* __restrict__ tables,
     int max_blocks, const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int NB, float qk_log2,
     int P, int nP, const char* __restrict__ new_k, const char* __restrict__ new_v,
-    const int32_t* __restrict__ qsl, int CG, int num_rows) {
+    const int32_t* __restrict__ qsl, int CG, int num_rows, Cascade cz) {
+  constexpr bool MQ = MODE == kModeMultiQuery;
+  constexpr int WPI = MODE == kModeCascade ? kCascadeWaves : 1;  // waves per item
   constexpr int D = 128;
   constexpr bool I8 = KV != kKvBf16;  // 1-byte codes with fp32 scales
   constexpr int E = I8 ? 1 : 2;
   // scales of a tile: the (block, head) scale, or the lane's four tokens'
   using Sc = typename std::conditional<TOKSC, f32x4_t, float>::type;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wv = WPI > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   const int j = lane >> 4;
   const int c = lane & 15;
+  // wave-uniform: prefix item of a cascade launch
+  const bool pre = MODE == kModeCascade && (int)blockIdx.x < cz.items;
   int s, g, p, cgw;
-  mfma_item(blockIdx.x, gridDim.x, Hkv, nP, CG, s, g, p, cgw);
+  if (pre) {
+    mfma_item(blockIdx.x, cz.items, Hkv, cz.nP, cz.CG, s, g, p, cgw);
+  } else if (MODE == kModeCascade) {
+    mfma_item(blockIdx.x - cz.items, gridDim.x - cz.items, Hkv, nP, CG, s, g, p, cgw);
+  } else {
+    mfma_item(blockIdx.x, gridDim.x, Hkv, nP, CG, s, g, p, cgw);
+  }
+  // this wave's tokens: [t_begin, t_end) of a table row of row_blocks entries
+  const int32_t* trow = pre ? cz.table : tables + (size_t)s * max_blocks;
+  const int row_blocks = pre ? cz.blocks : max_blocks;
+  const int Pw = pre ? cz.P : P;
+  const int t_begin = (MODE == kModeCascade && !pre ? cz.t0 : 0) + p * Pw;
+  // partial slot of this wave's partition, of nPw per row
+  const int slot = MODE == kModeCascade ? (pre ? p : cz.nP + p) : p;
+  const int nPw = MODE == kModeCascade ? cz.nPw : nP;
   // The partition's table entries, two per lane (a partition spans at most
   // 128 blocks, which the host guarantees): entry i of the partition is
   // lane i of tbl0 or lane i - 64 of tbl1.  They are read before the
   // context length is known, so the two loads overlap; entries past the
   // sequence's blocks (inside the table row) are read and never used.
-  const int32_t* trow = tables + (size_t)s * max_blocks;
-  const int tbl_base = (p * P) / BS;
-  const int tbl0 = (tbl_base + lane < max_blocks) ? trow[tbl_base + lane] : -1;
-  const int tbl1 = (tbl_base + 64 + lane < max_blocks) ? trow[tbl_base + 64 + lane] : -1;
+  const int tbl_base = t_begin / BS;
+  const int tbl0 = (tbl_base + lane < row_blocks) ? trow[tbl_base + lane] : -1;
+  const int tbl1 = (tbl_base + 64 + lane < row_blocks) ? trow[tbl_base + 64 + lane] : -1;
   // a length past the table row is a caller error; never read beyond the row
-  const int n = min(context_lens[s], max_blocks * BS);
-  const int t_begin = p * P;
-  const int t_end = min(n, t_begin + P);
+  const int n = pre ? cz.blocks * BS : min(context_lens[s], max_blocks * BS);
+  const int t_end = min(n, t_begin + Pw);
   // this lane's column in each group u: output / partial row orow[u],
   // visible tokens < lim[u] (MQ: several rows per sequence, qsl given)
   bool head_ok[NCG];
@@ -405,6 +446,14 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       qrow = q0 + i;
       lim[u] = head_ok[u] ? max(0, min(t_end, n - L + i + 1)) : 0;
       if (u == 0 && 16 * cgw * NCG >= G * L) return;  // no column of these groups exists
+    } else if (pre) {
+      // prefix column col -> (sequence col / G, head col % G), seeing the
+      // prefix up to its own length
+      const int col = 16 * (cgw * NCG + u) + c, i = col / G;
+      head_ok[u] = i < num_rows;
+      h = g * G + col % G;
+      qrow = head_ok[u] ? i : 0;
+      lim[u] = head_ok[u] ? max(0, min(t_end, min(context_lens[i], max_blocks * BS))) : 0;
     } else {
       head_ok[u] = c < G;
       h = g * G + c;
@@ -417,14 +466,15 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   if (t_begin >= t_end) {
     // Nothing to attend to.  With one partition the output row is zero;
     // otherwise the partial is marked empty (no weight) for the merge.
+    if (wv != 0) return;
 #pragma unroll
     for (int u = 0; u < NCG; ++u) {
-      if (nP == 1 && head_ok[u]) {
+      if (nPw == 1 && head_ok[u]) {
         float4* o = (float4*)(out + orow[u] * D + 32 * j);
 #pragma unroll
         for (int k = 0; k < 8; ++k) o[k] = float4{0.f, 0.f, 0.f, 0.f};
-      } else if (nP > 1 && head_ok[u] && j == 0) {
-        ws.ml[orow[u] * nP + p] = float2{kNegInf, 0.f};
+      } else if (nPw > 1 && head_ok[u] && j == 0) {
+        ws.ml[orow[u] * nPw + slot] = float2{kNegInf, 0.f};
       }
     }
     return;
@@ -454,7 +504,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   // into the cache slot at the end and attends with it in the tile that
   // holds the position (bf16 caches only; the host rejects int8).
   const int tnew = n - 1;
-  const bool owns_new = !I8 && new_k != nullptr && tnew >= t_begin && tnew < t_end;  // wave-uniform
+  const bool owns_new = !I8 && !pre && new_k != nullptr && tnew >= t_begin && tnew < t_end &&
+                        ((tnew >> 4) - (t_begin >> 4)) % WPI == wv;  // wave-uniform
   u32x4_t nk = {0u, 0u, 0u, 0u}, nv = {0u, 0u, 0u, 0u};
   if (owns_new) {
     const size_t src = ((size_t)s * Hkv + g) * ROW + (size_t)c * 16;
@@ -466,7 +517,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   // ch ^ (r mod chunks-per-row), so the row-wise writes and the MFMA-layout
   // reads (16 rows, one chunk each) spread over the banks.
   constexpr int CPR = ROW / 16;  // 16 B chunks per row
-  __shared__ u32x4_t ktile[16 * CPR];
+  // With several waves per item the same LDS later holds the waves'
+  // (m, l, acc) for their combination.
+  constexpr int KT_BYTES = WPI * 16 * CPR * 16;
+  constexpr int ACC_BYTES = (WPI - 1) * NCG * 8 * 64 * 16;
+  constexpr int CMB_BYTES = WPI > 1 ? ACC_BYTES + WPI * NCG * 2 * 64 * 4 : 0;
+  __shared__ __attribute__((aligned(16))) char smem[KT_BYTES > CMB_BYTES ? KT_BYTES : CMB_BYTES];
+  u32x4_t* ktile = (u32x4_t*)smem + wv * 16 * CPR;
   unsigned koff[4], voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -558,7 +615,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
         float xs = qk_log2;
         if constexpr (TOKSC) xs *= ks[r];
         else if (I8) xs *= ks;
-        x[r] = (ok && tok0 + r < (MQ ? lim[u] : t_end)) ? sc[r] * xs : kNegInf;
+        x[r] = (ok && tok0 + r < (MODE != kModeDecode ? lim[u] : t_end)) ? sc[r] * xs : kNegInf;
       }
       float mloc = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       mloc = xor_max_rows(mloc);
@@ -643,18 +700,21 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   const char *kA, *vA, *kB, *vB;
   bool okA, okB;
   Sc ksA{}, vsA{}, ksB{}, vsB{};
-  int ti = tile_begin;
-  tile_ptrs(ti, kA, vA, okA, ksA, vsA);
-  mfma_load_tile<I8>(A, kA, vA, koff, voff);
-  while (true) {
-    tile_ptrs(min(ti + 1, tile_end - 1), kB, vB, okB, ksB, vsB);
-    mfma_load_tile<I8>(B, kB, vB, koff, voff);
-    compute(A, ti, okA, ksA, vsA);
-    if (++ti >= tile_end) break;
-    tile_ptrs(min(ti + 1, tile_end - 1), kA, vA, okA, ksA, vsA);
+  // wave wv: tiles tile_begin + wv, + WPI, ...
+  int ti = tile_begin + wv;
+  if (ti < tile_end) {
+    tile_ptrs(ti, kA, vA, okA, ksA, vsA);
     mfma_load_tile<I8>(A, kA, vA, koff, voff);
-    compute(B, ti, okB, ksB, vsB);
-    if (++ti >= tile_end) break;
+    while (true) {
+      tile_ptrs(ti + WPI < tile_end ? ti + WPI : ti, kB, vB, okB, ksB, vsB);
+      mfma_load_tile<I8>(B, kB, vB, koff, voff);
+      compute(A, ti, okA, ksA, vsA);
+      if ((ti += WPI) >= tile_end) break;
+      tile_ptrs(ti + WPI < tile_end ? ti + WPI : ti, kA, vA, okA, ksA, vsA);
+      mfma_load_tile<I8>(A, kA, vA, koff, voff);
+      compute(B, ti, okB, ksB, vsB);
+      if ((ti += WPI) >= tile_end) break;
+    }
   }
 
   if (owns_new && j == 0) {
@@ -667,13 +727,54 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     }
   }
 
+  if constexpr (WPI > 1) {
+    // Combine the item's waves lane by lane in wave order: each holds its
+    // own reference m (-inf: no weight), weight sum l and acc for the same
+    // (column, d) slots; wave 0 continues with the combination.
+    f32x4_t(*s_acc)[NCG][8][64] = (f32x4_t(*)[NCG][8][64])smem;
+    float(*s_ml)[NCG][2][64] = (float(*)[NCG][2][64])(smem + ACC_BYTES);
+    __syncthreads();  // every wave is done with its K tile
+#pragma unroll
+    for (int u = 0; u < NCG; ++u) {
+      s_ml[wv][u][0][lane] = m_run[u];
+      s_ml[wv][u][1][lane] = l_run[u];
+      if (wv > 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_acc[wv - 1][u][e][lane] = acc[u][e];
+      }
+    }
+    __syncthreads();
+    if (wv != 0) return;
+#pragma unroll
+    for (int u = 0; u < NCG; ++u) {
+      float M = m_run[u];
+#pragma unroll
+      for (int w = 1; w < WPI; ++w) M = fmaxf(M, s_ml[w][u][0][lane]);
+      if (M != kNegInf) {
+        float f = m_run[u] == kNegInf ? 0.f : fast_exp2(m_run[u] - M);
+        l_run[u] *= f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[u][e] *= f;
+#pragma unroll
+        for (int w = 1; w < WPI; ++w) {
+          const float mw = s_ml[w][u][0][lane];
+          f = mw == kNegInf ? 0.f : fast_exp2(mw - M);
+          l_run[u] = fmaf(f, s_ml[w][u][1][lane], l_run[u]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[u][e] += f * s_acc[w - 1][u][e][lane];
+        }
+      }
+      m_run[u] = M;
+    }
+  }
+
   // lane holds d = 32j + 8r + e in acc[u][e][r]
 #pragma unroll
   for (int u = 0; u < NCG; ++u) {
     const float l_tot = xor_sum_rows(l_run[u]);
     const f32x4_t* a = acc[u];
     if (!head_ok[u]) continue;
-    if (nP == 1) {
+    if (nPw == 1) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       float* o = out + orow[u] * D + 32 * j;
 #pragma unroll
@@ -682,7 +783,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
         *(float4*)(o + 8 * r + 4) = float4{a[4][r] * inv, a[5][r] * inv, a[6][r] * inv, a[7][r] * inv};
       }
     } else {
-      const size_t row_id = orow[u] * nP + p;
+      const size_t row_id = orow[u] * nPw + slot;
       float* o = ws.acc + row_id * D + 32 * j;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -985,7 +1086,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
 
 static inline SplitK split_k(const pa_decode_args* a, const DecodePlan& p) {
   SplitK w{nullptr, nullptr};
-  if (p.num_partitions > 1) {
+  if (p.ws_partitions > 1) {
     const WorkspaceLayout L = workspace_layout(a, p);
     char* base = (char*)a->workspace;
     w.ml = (float2*)(base + L.ml_offset);
@@ -996,22 +1097,36 @@ static inline SplitK split_k(const pa_decode_args* a, const DecodePlan& p) {
 
 pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipStream_t st) {
   const int ncg = p.ncg, cgw = p.cg_waves;
-  const size_t items = (size_t)a->num_seqs * a->num_kv_heads * p.num_partitions * cgw;
+  Cascade cz{nullptr, 0, 0, 0, 0, 1, 0, p.ws_partitions};
+  size_t pre_items = 0;
+  if (p.cascade) {
+    pre_items = (size_t)a->num_kv_heads * p.prefix_partitions * p.prefix_cgroups;
+    cz.table = a->shared_prefix_table;
+    cz.blocks = a->shared_prefix_len / a->block_size;
+    cz.nP = p.prefix_partitions;
+    cz.P = p.prefix_tokens;
+    cz.CG = p.prefix_cgroups;
+    cz.t0 = a->shared_prefix_len;
+  }
+  const size_t items = pre_items + (size_t)a->num_seqs * a->num_kv_heads * p.num_partitions * cgw;
   if (items > 0x7fffffffu) return fail(PA_ERR_UNSUPPORTED, "pa_decode: grid too large");
+  cz.items = (int)pre_items;
   const float qk = a->scale * kLog2e;
   const SplitK ws = split_k(a, p);
-#define PA_MFMA_LAUNCH1(KV, BS, TOKSC, NCG, MQ)                                                                 \
-  hipLaunchKernelGGL((decode_mfma_kernel<KV, BS, TOKSC, NCG, MQ>), dim3((unsigned)items), dim3(64), 0, st,      \
+#define PA_MFMA_LAUNCH1(KV, BS, TOKSC, NCG, MODE)                                                               \
+  hipLaunchKernelGGL((decode_mfma_kernel<KV, BS, TOKSC, NCG, MODE>), dim3((unsigned)items),                     \
+                     dim3(MODE == kModeCascade ? 64 * kCascadeWaves : 64), 0, st,                               \
                      (float*)a->out, ws, (const unsigned short*)a->q, (char*)a->k_cache, (char*)a->v_cache,      \
                      a->k_scales, a->v_scales, a->block_tables, a->max_blocks_per_seq, a->context_lens,        \
                      a->num_q_heads, a->num_kv_heads, p.G, a->num_blocks, qk, p.partition_tokens,              \
                      p.num_partitions, (const char*)a->new_key, (const char*)a->new_value,                     \
-                     a->query_start_loc, cgw, a->query_start_loc ? a->num_queries : a->num_seqs)
-#define PA_MFMA_LAUNCH(KV, BS, TOKSC)                                          \
-  do {                                                                         \
-    if (!a->query_start_loc) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, false);         \
-    else if (ncg == 2) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 2, true);                \
-    else PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, true);                              \
+                     a->query_start_loc, cgw, a->query_start_loc ? a->num_queries : a->num_seqs, cz)
+#define PA_MFMA_LAUNCH(KV, BS, TOKSC)                                                \
+  do {                                                                               \
+    if (p.cascade) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeCascade);                  \
+    else if (!a->query_start_loc) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeDecode);    \
+    else if (ncg == 2) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 2, kModeMultiQuery);           \
+    else PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeMultiQuery);                         \
   } while (0)
 #define PA_MFMA_BS(KV, TOKSC)                              \
   if (a->block_size == 16) PA_MFMA_LAUNCH(KV, 16, TOKSC); \
@@ -1093,11 +1208,11 @@ static void merge_dispatch(const pa_decode_args* a, const DecodePlan& p, hipStre
                            const SplitK& ws, int max_tokens) {
 #define PA_MERGE_LAUNCH(W)                                                                                  \
   hipLaunchKernelGGL((decode_merge_kernel<D, W>), dim3(rows), dim3(64 * W), 0, st, (float*)a->out, ws,       \
-                     a->query_start_loc ? nullptr : a->context_lens, a->num_q_heads, p.partition_tokens,        \
-                     p.num_partitions, max_tokens)
-  if (p.num_partitions <= 16) PA_MERGE_LAUNCH(1);
-  else if (p.num_partitions <= 32) PA_MERGE_LAUNCH(2);
-  else if (p.num_partitions <= 64) PA_MERGE_LAUNCH(4);
+                     a->query_start_loc || p.cascade ? nullptr : a->context_lens, a->num_q_heads,             \
+                     p.partition_tokens, p.ws_partitions, max_tokens)
+  if (p.ws_partitions <= 16) PA_MERGE_LAUNCH(1);
+  else if (p.ws_partitions <= 32) PA_MERGE_LAUNCH(2);
+  else if (p.ws_partitions <= 64) PA_MERGE_LAUNCH(4);
   else PA_MERGE_LAUNCH(8);
 #undef PA_MERGE_LAUNCH
 }

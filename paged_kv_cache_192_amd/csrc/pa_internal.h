@@ -45,6 +45,8 @@ constexpr int kMaxPartitionBlocks = 128;
 // workspace, which holds max_context_len / partition_tokens partials per
 // row).
 constexpr int kMaxAutoPartitions = 32;
+// waves per work item of the shared-prefix (cascade) decode
+constexpr int kCascadeWaves = 4;
 constexpr int kMaxRaggedPartitions = 512;
 
 // Everything the launchers need, derived on the host from pa_decode_args.
@@ -59,14 +61,22 @@ struct DecodePlan {
   int ncg;               // MFMA: column groups carried by one wave (1 or 2)
   int cg_waves;          // MFMA: waves per (sequence, kv head, partition) = ceil(cgroups / ncg)
   int64_t rows;          // output rows: query rows (num_seqs, or num_queries) x num_q_heads
+  // shared prefix (cascade): items over the shared blocks for all
+  // sequences, split into prefix_partitions partitions of prefix_tokens,
+  // with prefix_cgroups column groups (sequences x heads, 16 at a time,
+  // one wave each); the per-sequence items then start at the prefix's end
+  bool cascade;
+  int prefix_tokens, prefix_partitions, prefix_cgroups;
+  int ws_partitions;     // partials per output row: prefix_partitions + num_partitions
   size_t workspace_bytes;
 };
 
 pa_status plan_decode(const pa_decode_args* a, DecodePlan* plan);
 
-// Workspace layout for num_partitions > 1 (offsets 256-byte aligned):
-//   float2 ml [S][Hq][nP]      reference max (log2 units), sum of weights
-//   float  acc[S][Hq][nP][D]   unnormalised weighted sum of values
+// Workspace layout for ws_partitions > 1 (offsets 256-byte aligned), with
+// nP = ws_partitions (shared-prefix partials first, then the sequences'):
+//   float2 ml [rows][nP]      reference max (log2 units), sum of weights
+//   float  acc[rows][nP][D]   unnormalised weighted sum of values
 // Every entry a merge reads is written by the same call, so the workspace
 // needs no initialisation.
 struct WorkspaceLayout {
@@ -77,8 +87,8 @@ inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 inline WorkspaceLayout workspace_layout(const pa_decode_args* a, const DecodePlan& p) {
   WorkspaceLayout L{0, 0, 0};
-  if (p.num_partitions <= 1) return L;
-  const size_t rows = (size_t)p.rows * p.num_partitions;
+  if (p.ws_partitions <= 1) return L;
+  const size_t rows = (size_t)p.rows * p.ws_partitions;
   L.ml_offset = 0;
   L.acc_offset = align256(rows * 2 * sizeof(float));
   L.bytes = L.acc_offset + align256(rows * a->head_dim * sizeof(float));

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
     assert len(names) >= 16, names
     for n in names:
         assert hasattr(lib, n), "libpa.so does not export %s" % n
-    assert lib.pa_abi_version() == pa.ABI_VERSION == 5
+    assert lib.pa_abi_version() == pa.ABI_VERSION == 6
 
 
 def test_status_strings():
@@ -162,6 +162,39 @@ def test_multi_query_argument_checks():
     st, n = _ws(_cpu_args(query_start_loc=qsl, num_queries=5, max_query_len=3, partition_tokens=64))
     al = lambda b: (b + 255) // 256 * 256  # noqa: E731
     assert st == pa.PA_OK and n == al(5 * 8 * 2 * 8) + al(5 * 8 * 2 * 128 * 4)
+
+
+def test_shared_prefix_argument_checks_and_plan():
+    lib = pa.library()
+    tbl = 0x40000
+    al = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    for over in (dict(shared_prefix_len=32),                               # no table
+                 dict(shared_prefix_table=tbl, shared_prefix_len=40),      # not whole blocks
+                 dict(shared_prefix_table=tbl, shared_prefix_len=112),     # > max_context_len 100
+                 dict(shared_prefix_table=tbl, shared_prefix_len=-16)):
+        a = _cpu_args(**over)
+        assert lib.pa_decode(ctypes.byref(a)) == pa.PA_ERR_INVALID
+        assert "shared_prefix" in lib.pa_last_error().decode()
+    a = _cpu_args(shared_prefix_table=0x40002, shared_prefix_len=64)
+    assert lib.pa_decode(ctypes.byref(a)) == pa.PA_ERR_INVALID
+    # partials per row: prefix partitions, then the sequences' own -- given
+    # 32-token partitions: 64 prefix tokens -> 2, the other <= 36 -> 2
+    st, n = _ws(_cpu_args(shared_prefix_table=tbl, shared_prefix_len=64, partition_tokens=32))
+    assert st == pa.PA_OK and n == al(24 * 4 * 8) + al(24 * 4 * 128 * 4)
+    # automatic: one partition for each part -> 2 partials per row
+    st, n = _ws(_cpu_args(shared_prefix_table=tbl, shared_prefix_len=64))
+    assert st == pa.PA_OK and n == al(24 * 2 * 8) + al(24 * 2 * 128 * 4)
+    # the whole context shared: only prefix partials (given 32-token
+    # partitions: 3); automatic: one partition of 96 (at least 4 tiles per
+    # wave of an item) -> written directly, no workspace
+    st, n = _ws(_cpu_args(shared_prefix_table=tbl, shared_prefix_len=96, max_context_len=96, partition_tokens=32))
+    assert st == pa.PA_OK and n == al(24 * 3 * 8) + al(24 * 3 * 128 * 4)
+    st, n = _ws(_cpu_args(shared_prefix_table=tbl, shared_prefix_len=96, max_context_len=96))
+    assert st == pa.PA_OK and n == 0
+    # ignored by the vector-ALU kernel: the plan without a prefix
+    st0, n0 = _ws(_cpu_args(kernel=pa.KERNEL_VALU))
+    st, n = _ws(_cpu_args(shared_prefix_table=tbl, shared_prefix_len=64, kernel=pa.KERNEL_VALU))
+    assert st == st0 == pa.PA_OK and n == n0
 
 
 def test_fused_write_argument_checks():
