@@ -136,6 +136,10 @@ __global__ __launch_bounds__(64 * W) void decode_merge_kernel(float* __restrict_
     const int n = min(context_lens[row / Hq], max_tokens);
     np = n > 0 ? min(nP, (n + P - 1) / P) : 0;
   }
+  // A row with at most GRP partials needs one wave: the others leave before
+  // any barrier (the condition is the same for the whole workgroup).
+  const bool solo = W > 1 && np <= GRP;
+  if (solo && wave > 0) return;
   const size_t r = row * (size_t)nP;
   float m_run = kNegInf, L = 0.f, a[PER];
 #pragma unroll
@@ -169,7 +173,7 @@ __global__ __launch_bounds__(64 * W) void decode_merge_kernel(float* __restrict_
       for (int q = 0; q < PER; ++q) a[q] = wk > 0.f ? fmaf(wk, part[k][q], a[q]) : a[q];
     }
   }
-  if constexpr (W > 1) {
+  if (W > 1 && !solo) {
     __shared__ float s_ml[W][2];
     __shared__ float s_a[W][D];
     if (lane == 0) {
