@@ -95,10 +95,10 @@ def cpu_model() -> str:
 # (profiles/decode_mfma_llama3-70b_pmc_traffic.md).  Valid only for the
 # sources the counters were taken on: a changed kernel or plan reports null.
 PMC_TRAFFIC = {
-    "sources_sha256": "adf1320b868a469157b40e39712171e54757f85fd121622c1d938213ef6b9683",
-    "fetch_kib": 320978.8 + 1384.5,
+    "sources_sha256": "a4eaef347ff05f4da62ecd1bbd20da67c9fed3ef809edc30ad72f6a92608799d",
+    "fetch_kib": 320996.6 + 1382.5,
     "write_kib": 2680.0 + 640.0,
-    "fetch_factor": 1.99226,
+    "fetch_factor": 1.99227,
     "write_factor": 1.0,
 }
 PMC_SOURCES = ("paged_kv_cache_192_amd/csrc/pa_decode.hip", "paged_kv_cache_192_amd/csrc/pa_api.cpp",
