@@ -50,6 +50,9 @@ static int target_waves(KernelKind kind, pa_dtype kv) {
 // lengths (int8 and bf16 caches): ~5,000 waves of <= 16 tiles beat both
 // fewer longer waves and more shorter ones.
 constexpr int64_t kRaggedWaves = 5120;
+// Waves of a balanced split (one launch, all kv heads).
+static int64_t balanced_waves(int32_t kv_dtype) { return kv_dtype == PA_BF16 ? 640 : 2560; }
+
 // Waves for the items over a shared prefix.  Measured on the prefix-sharing
 // layer (50 sequences, 1,984 shared tokens, 32/8 heads): 2 partitions of
 // 62 tiles (~1,000 waves) beat 4 to 16 shorter ones, whose extra partials
@@ -226,6 +229,38 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
     p->num_partitions = a->max_context_len > 0 ? (a->max_context_len + P - 1) / P : 1;
   }
   p->ws_partitions = p->prefix_partitions + p->num_partitions;
+  // Balanced split for a skewed batch (length hint given, mean under 1/4 of
+  // the maximum, matrix-core decode with the library's own split): every
+  // wave gets an equal range of its head's tiles, whatever the lengths, so
+  // long and short sequences cost no per-partition start-up or partial
+  // beyond one per (range, sequence) piece.  Measured on log-normal
+  // lengths (mean / max 0.12): bf16 59 -> 70 %, int8 44 -> 50 % of HBM
+  // peak; on U[200, 2048] (mean / max 0.55) the short partitions of the
+  // ragged rule stay ahead by ~1 point.
+  p->balanced = false;
+  if (kind == KERNEL_MFMA && !mq && !p->cascade && a->partition_tokens == 0 && a->total_context_len > 0 &&
+      a->num_seqs > 0 && a->num_seqs <= kBalancedMaxSeqs && a->max_context_len > 0 &&
+      a->total_context_len * 4 < (int64_t)a->num_seqs * a->max_context_len) {
+    const int64_t max_tiles = (a->max_context_len + 15) / 16;
+    // tiles per head from the hint (an upper bound on the true count), and
+    // enough waves that no wave needs a second range of at most
+    // kBalancedMaxTiles (a second range doubles that wave's time)
+    const int64_t t_hint = (a->total_context_len + 15) / 16 + a->num_seqs;
+    int64_t wh = (balanced_waves(a->kv_dtype) + a->num_kv_heads - 1) / a->num_kv_heads;
+    if (wh < (t_hint + kBalancedMaxTiles - 1) / kBalancedMaxTiles) wh = (t_hint + kBalancedMaxTiles - 1) / kBalancedMaxTiles;
+    int64_t pw = (t_hint + wh - 1) / wh;
+    if (pw < 1) pw = 1;
+    if (pw > kBalancedMaxTiles) pw = kBalancedMaxTiles;
+    // a sequence of n tiles meets at most floor((n - 1) / pw) + 2 ranges;
+    // the kernel keeps ranges >= max_tiles / (slots - 1) tiles so that
+    // every sequence's pieces fit its slots, whatever the true lengths
+    const int64_t slots = (max_tiles + pw - 1) / pw + 1;
+    p->balanced = true;
+    p->balanced_waves = (int)wh;
+    p->balanced_min_tiles = (int)((max_tiles + slots - 2) / (slots - 1));
+    p->num_partitions = (int)slots;
+    p->ws_partitions = (int)slots;
+  }
   p->workspace_bytes = workspace_layout(a, *p).bytes;
   return PA_OK;
 }

@@ -107,13 +107,15 @@ __device__ __forceinline__ float wave_sum(float x) { return xor_sum_rows(row_sum
 struct SplitK {
   float2* ml;     // [S][Hq][nP]: reference max (log2 units), sum of weights
   float* acc;     // [S][Hq][nP][D]: unnormalised weighted sum of values
+  int32_t* counts;  // balanced split: partials of each sequence [S], else NULL
 };
 
 // One workgroup of W waves per output row (query row, head): out = sum_p
 // 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p over the partitions that hold
 // tokens, in partition order.  Every partition of the grid leaves its
 // (m, l), empty ones (-inf, 0), so a row's nP partials can be read without
-// first reading its length.  With lengths given (decode rows) and W > 1
+// first reading its length (a balanced split instead records how many
+// partials each sequence has, and only those are read).  With lengths given (decode rows) and W > 1
 // (long ragged rows, most partitions empty) only the ceil(n / P) that hold
 // tokens are read.  Partitions are read sixteen at a time, all loads of a
 // group issued together (one memory round trip per group); wave w takes
@@ -132,7 +134,9 @@ __global__ __launch_bounds__(64 * W) void decode_merge_kernel(float* __restrict_
   const int wave = threadIdx.x >> 6;
   const size_t row = blockIdx.x;
   int np = nP;
-  if (W > 1 && context_lens) {
+  if (ws.counts) {
+    np = min(nP, max(0, ws.counts[row / Hq]));
+  } else if (W > 1 && context_lens) {
     const int n = min(context_lens[row / Hq], max_tokens);
     np = n > 0 ? min(nP, (n + P - 1) / P) : 0;
   }
@@ -369,7 +373,81 @@ struct Cascade {
   int nPw;               // partial slots per output row (1: write out directly)
 };
 
-constexpr int kModeDecode = 0, kModeMultiQuery = 1, kModeCascade = 2;
+constexpr int kModeDecode = 0, kModeMultiQuery = 1, kModeCascade = 2, kModeBalanced = 3;
+
+// Balanced split of a ragged decode batch.  A kv head's work is the
+// sequence of 16-token tiles of all sequences in order; it is cut into V
+// ranges of pw tiles, range v handled by wave v mod Wh of the head (waves
+// loop over their ranges).  A range that crosses sequence boundaries is
+// processed as pieces, one per sequence, each leaving a partial in slot
+// v - (first range of that sequence).  Every wave reads all lengths once
+// (sequence 64*ch + lane in chunk ch) and scans the tile counts; tile
+// index a -> its sequence by a ballot over the inclusive sums.
+constexpr int kBalancedChunks = kBalancedMaxSeqs / 64;
+struct TileMap {
+  int incl[kBalancedChunks];  // inclusive prefix sums of the tile counts
+  int len[kBalancedChunks];   // the sequences' lengths (capped at the table row)
+  int last[kBalancedChunks];  // incl of each chunk's last lane (wave-uniform)
+  int total;                  // tiles of all sequences
+};
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// tiles attended of a sequence of n tokens: those of its first min(n, cap)
+__device__ __forceinline__ int tile_count(int n, int cap) { return n > 0 ? (min(n, cap) + 15) >> 4 : 0; }
+
+__device__ __forceinline__ void tile_map_init(TileMap& m, const int32_t* __restrict__ context_lens, int S,
+                                              int row_cap, int cap, int lane) {
+  int n[kBalancedChunks];
+#pragma unroll
+  for (int ch = 0; ch < kBalancedChunks; ++ch) {
+    const int si = 64 * ch + lane;
+    n[ch] = si < S ? max(0, min(context_lens[si], row_cap)) : 0;
+  }
+  int run = 0;
+#pragma unroll
+  for (int ch = 0; ch < kBalancedChunks; ++ch) {
+    const int x = wave_incl_scan(tile_count(n[ch], cap), lane) + run;
+    m.incl[ch] = x;
+    m.len[ch] = n[ch];
+    run = __builtin_amdgcn_readlane(x, 63);
+    m.last[ch] = run;
+  }
+  m.total = run;
+}
+
+// tile index a < m.total -> sequence s, its length n, tile count c and the
+// tiles before it (the chunk found by counting, its values by selects: no
+// indexing of the register arrays)
+__device__ __forceinline__ void tile_find(const TileMap& m, int a, int cap, int& s, int& n, int& c, int& excl) {
+  int ch = 0;
+#pragma unroll
+  for (int k = 0; k + 1 < kBalancedChunks; ++k) ch += m.last[k] <= a ? 1 : 0;
+  int incl = m.incl[0], len = m.len[0];
+#pragma unroll
+  for (int k = 1; k < kBalancedChunks; ++k) {
+    incl = ch == k ? m.incl[k] : incl;
+    len = ch == k ? m.len[k] : len;
+  }
+  const unsigned long long b = __ballot(incl > a);
+  const int l = b ? __builtin_ctzll(b) : 0;
+  n = __builtin_amdgcn_readlane(len, l);
+  c = tile_count(n, cap);
+  excl = __builtin_amdgcn_readlane(incl, l) - c;
+  s = 64 * ch + l;
+}
+
+struct Balanced {
+  int min_tiles;  // least tiles per range (keeps every sequence's pieces within nP slots)
+  int cap;        // tokens attended per sequence at most (max_context_len)
+};
 static_assert(kCascadeWaves == 1 || kCascadeWaves == 2 || kCascadeWaves == 4, "1, 2 or 4 waves per item");
 
 // KV: kKvBf16, kKvI8 or kKvFp8 cache; TOKSC: quantised cache with one scale
@@ -391,7 +469,7 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
     const float* __restrict__ k_scales, const float* __restrict__ v_scales, const int32_t* __restrict__ tables,
     int max_blocks, const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int NB, float qk_log2,
     int P, int nP, const char* __restrict__ new_k, const char* __restrict__ new_v,
-    const int32_t* __restrict__ qsl, int CG, int num_rows, Cascade cz) {
+    const int32_t* __restrict__ qsl, int CG, int num_rows, Cascade cz, Balanced bz) {
   constexpr bool MQ = MODE == kModeMultiQuery;
   constexpr int WPI = MODE == kModeCascade ? kCascadeWaves : 1;  // waves per item
   constexpr int D = 128;
@@ -405,8 +483,46 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
   const int c = lane & 15;
   // wave-uniform: prefix item of a cascade launch
   const bool pre = MODE == kModeCascade && (int)blockIdx.x < cz.items;
-  int s, g, p, cgw;
-  if (pre) {
+  // balanced split: this wave's ranges v = blockIdx.x / Hkv + k * Wh of pw tiles
+  TileMap tm;
+  int pw = 1, V = 0, Wh = 1, v = 0, ra = 0, rb = 0;
+  if constexpr (MODE == kModeBalanced) {
+    tile_map_init(tm, context_lens, num_rows, max_blocks * BS, bz.cap, lane);
+    Wh = gridDim.x / Hkv;
+    pw = min(max((tm.total + Wh - 1) / Wh, bz.min_tiles), kBalancedMaxTiles);
+    V = (tm.total + pw - 1) / pw;
+    v = (int)blockIdx.x / Hkv - Wh;
+    if (blockIdx.x == 0) {
+      // partials of each sequence: the ranges its tiles meet
+#pragma unroll
+      for (int ch = 0; ch < kBalancedChunks; ++ch) {
+        const int si = 64 * ch + lane;
+        const int c = tile_count(tm.len[ch], bz.cap), in = tm.incl[ch];
+        if (si < num_rows) ws.counts[si] = c > 0 ? (in - 1) / pw - (in - c) / pw + 1 : 0;
+      }
+    }
+  }
+  // one item per wave, except in a balanced split (a loop over pieces)
+  for (;;) {
+  int s, g, p, cgw, n_piece = 0, piece_t0 = 0, piece_t1 = 0, piece_slot = 0;
+  if constexpr (MODE == kModeBalanced) {
+    if (ra >= rb) {
+      v += Wh;
+      if (v >= V) return;
+      ra = v * pw;
+      rb = min(tm.total, ra + pw);
+    }
+    int c, excl;
+    tile_find(tm, ra, bz.cap, s, n_piece, c, excl);
+    const int lt0 = ra - excl, lt1 = min(c, lt0 + (rb - ra));
+    piece_t0 = 16 * lt0;
+    piece_t1 = 16 * lt1;
+    piece_slot = v - excl / pw;
+    ra += lt1 - lt0;
+    g = (int)blockIdx.x % Hkv;
+    p = 0;
+    cgw = 0;
+  } else if (pre) {
     mfma_item(blockIdx.x, cz.items, Hkv, cz.nP, cz.CG, s, g, p, cgw);
   } else if (MODE == kModeCascade) {
     mfma_item(blockIdx.x - cz.items, gridDim.x - cz.items, Hkv, nP, CG, s, g, p, cgw);
@@ -417,9 +533,9 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
   const int32_t* trow = pre ? cz.table : tables + (size_t)s * max_blocks;
   const int row_blocks = pre ? cz.blocks : max_blocks;
   const int Pw = pre ? cz.P : P;
-  const int t_begin = (MODE == kModeCascade && !pre ? cz.t0 : 0) + p * Pw;
+  const int t_begin = MODE == kModeBalanced ? piece_t0 : (MODE == kModeCascade && !pre ? cz.t0 : 0) + p * Pw;
   // partial slot of this wave's partition, of nPw per row
-  const int slot = MODE == kModeCascade ? (pre ? p : cz.nP + p) : p;
+  const int slot = MODE == kModeBalanced ? piece_slot : MODE == kModeCascade ? (pre ? p : cz.nP + p) : p;
   const int nPw = MODE == kModeCascade ? cz.nPw : nP;
   // The partition's table entries, two per lane (a partition spans at most
   // 128 blocks, which the host guarantees): entry i of the partition is
@@ -430,8 +546,8 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
   const int tbl0 = (tbl_base + lane < row_blocks) ? trow[tbl_base + lane] : -1;
   const int tbl1 = (tbl_base + 64 + lane < row_blocks) ? trow[tbl_base + 64 + lane] : -1;
   // a length past the table row is a caller error; never read beyond the row
-  const int n = pre ? cz.blocks * BS : min(context_lens[s], max_blocks * BS);
-  const int t_end = min(n, t_begin + Pw);
+  const int n = pre ? cz.blocks * BS : MODE == kModeBalanced ? n_piece : min(context_lens[s], max_blocks * BS);
+  const int t_end = min(n, MODE == kModeBalanced ? piece_t1 : t_begin + Pw);
   // this lane's column in each group u: output / partial row orow[u],
   // visible tokens < lim[u] (MQ: several rows per sequence, qsl given)
   bool head_ok[NCG];
@@ -481,7 +597,8 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
         ws.ml[orow[u] * nPw + slot] = float2{kNegInf, 0.f};
       }
     }
-    return;
+    if constexpr (MODE == kModeBalanced) continue;
+    else return;
   }
 
   // Queries as the B operand: column c of group u, the 8 values of d-chunk
@@ -797,6 +914,8 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
       if (j == 0) ws.ml[row_id] = float2{m_run[u], l_tot};
     }
   }
+  if constexpr (MODE != kModeBalanced) return;
+  }  // piece loop
 }
 
 // ===========================================================================
@@ -1089,12 +1208,13 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
 // ===========================================================================
 
 static inline SplitK split_k(const pa_decode_args* a, const DecodePlan& p) {
-  SplitK w{nullptr, nullptr};
+  SplitK w{nullptr, nullptr, nullptr};
   if (p.ws_partitions > 1) {
     const WorkspaceLayout L = workspace_layout(a, p);
     char* base = (char*)a->workspace;
     w.ml = (float2*)(base + L.ml_offset);
     w.acc = (float*)(base + L.acc_offset);
+    if (p.balanced) w.counts = (int32_t*)(base + L.counts_offset);
   }
   return w;
 }
@@ -1112,7 +1232,9 @@ pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipSt
     cz.CG = p.prefix_cgroups;
     cz.t0 = a->shared_prefix_len;
   }
-  const size_t items = pre_items + (size_t)a->num_seqs * a->num_kv_heads * p.num_partitions * cgw;
+  const size_t items = p.balanced ? (size_t)a->num_kv_heads * p.balanced_waves
+                                  : pre_items + (size_t)a->num_seqs * a->num_kv_heads * p.num_partitions * cgw;
+  const Balanced bz{p.balanced_min_tiles, a->max_context_len};
   if (items > 0x7fffffffu) return fail(PA_ERR_UNSUPPORTED, "pa_decode: grid too large");
   cz.items = (int)pre_items;
   const float qk = a->scale * kLog2e;
@@ -1124,10 +1246,11 @@ pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipSt
                      a->k_scales, a->v_scales, a->block_tables, a->max_blocks_per_seq, a->context_lens,        \
                      a->num_q_heads, a->num_kv_heads, p.G, a->num_blocks, qk, p.partition_tokens,              \
                      p.num_partitions, (const char*)a->new_key, (const char*)a->new_value,                     \
-                     a->query_start_loc, cgw, a->query_start_loc ? a->num_queries : a->num_seqs, cz)
+                     a->query_start_loc, cgw, a->query_start_loc ? a->num_queries : a->num_seqs, cz, bz)
 #define PA_MFMA_LAUNCH(KV, BS, TOKSC)                                                \
   do {                                                                               \
     if (p.cascade) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeCascade);                  \
+    else if (p.balanced) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeBalanced);           \
     else if (!a->query_start_loc) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeDecode);    \
     else if (ncg == 2) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 2, kModeMultiQuery);           \
     else PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeMultiQuery);                         \
@@ -1212,7 +1335,7 @@ static void merge_dispatch(const pa_decode_args* a, const DecodePlan& p, hipStre
                            const SplitK& ws, int max_tokens) {
 #define PA_MERGE_LAUNCH(W)                                                                                  \
   hipLaunchKernelGGL((decode_merge_kernel<D, W>), dim3(rows), dim3(64 * W), 0, st, (float*)a->out, ws,       \
-                     a->query_start_loc || p.cascade ? nullptr : a->context_lens, a->num_q_heads,             \
+                     a->query_start_loc || p.cascade || p.balanced ? nullptr : a->context_lens, a->num_q_heads, \
                      p.partition_tokens, p.ws_partitions, max_tokens)
   if (p.ws_partitions <= 16) PA_MERGE_LAUNCH(1);
   else if (p.ws_partitions <= 32) PA_MERGE_LAUNCH(2);

@@ -47,6 +47,10 @@ constexpr int kMaxPartitionBlocks = 128;
 constexpr int kMaxAutoPartitions = 32;
 // waves per work item of the shared-prefix (cascade) decode
 constexpr int kCascadeWaves = 4;
+// balanced split of a ragged batch: at most this many sequences (the
+// lengths sit in four 64-lane chunks of registers) and tiles per wave range
+constexpr int kBalancedMaxSeqs = 256;
+constexpr int kBalancedMaxTiles = 64;
 constexpr int kMaxRaggedPartitions = 512;
 
 // Everything the launchers need, derived on the host from pa_decode_args.
@@ -68,6 +72,11 @@ struct DecodePlan {
   bool cascade;
   int prefix_tokens, prefix_partitions, prefix_cgroups;
   int ws_partitions;     // partials per output row: prefix_partitions + num_partitions
+  // balanced split (ragged batch): each kv head's tiles, in sequence order,
+  // cut into equal ranges of at least balanced_min_tiles, one per wave of
+  // balanced_waves per head; ws_partitions partial slots per row
+  bool balanced;
+  int balanced_waves, balanced_min_tiles;
   size_t workspace_bytes;
 };
 
@@ -80,18 +89,20 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* plan);
 // Every entry a merge reads is written by the same call, so the workspace
 // needs no initialisation.
 struct WorkspaceLayout {
-  size_t ml_offset, acc_offset, bytes;
+  size_t ml_offset, acc_offset, counts_offset, bytes;
 };
 
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 inline WorkspaceLayout workspace_layout(const pa_decode_args* a, const DecodePlan& p) {
-  WorkspaceLayout L{0, 0, 0};
+  WorkspaceLayout L{0, 0, 0, 0};
   if (p.ws_partitions <= 1) return L;
   const size_t rows = (size_t)p.rows * p.ws_partitions;
   L.ml_offset = 0;
   L.acc_offset = align256(rows * 2 * sizeof(float));
-  L.bytes = L.acc_offset + align256(rows * a->head_dim * sizeof(float));
+  L.counts_offset = L.acc_offset + align256(rows * a->head_dim * sizeof(float));
+  // balanced split: partials per sequence, int32 [num_seqs]
+  L.bytes = L.counts_offset + (p.balanced ? align256((size_t)a->num_seqs * sizeof(int32_t)) : 0);
   return L;
 }
 

@@ -79,8 +79,10 @@ def test_struct_layout_and_workspace_size():
 
 def test_partition_plan_follows_the_length_hint():
     """Near-equal lengths (hint absent or close to num_seqs * max): a few
-    long partitions per sequence; a ragged batch: short ones, here the
-    4-tile minimum, up to 512 per sequence."""
+    long partitions per sequence.  A ragged batch: short partitions, here
+    the 4-tile minimum, up to 512 per sequence; a strongly skewed one (mean
+    under a quarter of the maximum) on the matrix-core kernel: the balanced
+    split, 640 waves over the heads' tiles."""
     al = lambda b: (b + 255) // 256 * 256  # noqa: E731
 
     def ws_for(nP):
@@ -94,6 +96,13 @@ def test_partition_plan_follows_the_length_hint():
         assert n == ws_for(32)                          # 1024-token partitions
     st, n = _ws(_cpu_args(total_context_len=40000, **big))
     assert st == pa.PA_OK and n == ws_for(512)          # 64-token partitions
+    st, n = _ws(_cpu_args(total_context_len=20000, kernel=pa.KERNEL_VALU, **big))
+    assert st == pa.PA_OK and n == ws_for(512)
+    # balanced: 320 waves per kv head, ranges of ceil((1250 + 3) / 320) = 4
+    # tiles, so a 2,048-tile sequence meets at most 513 ranges; then the
+    # per-sequence partial counts
+    st, n = _ws(_cpu_args(total_context_len=20000, **big))
+    assert st == pa.PA_OK and n == ws_for(513) + al(3 * 4)
     # an explicit partition size ignores the hint
     st, n = _ws(_cpu_args(total_context_len=40000, partition_tokens=2048, **big))
     assert st == pa.PA_OK and n == ws_for(16)

@@ -1,6 +1,8 @@
 """Ragged decode batches (log-normal lengths, a few empty sequences, one
-long one) under the partition plans the length hint selects: the result
-must not depend on the hint's value, which only shapes the split.  Checked
+long one) under the plans the length hint selects -- the balanced split
+(each kv head's tiles cut into equal ranges over the sequences, up to 256
+sequences), short partitions, long ones: the result must not depend on the
+hint's value, which only shapes the split.  Checked
 against the CPU oracle, max |gpu - oracle| <= 2e-3 (bf16, int8 or E4M3
 inputs); the fused cache write bit-exact."""
 import math
@@ -33,11 +35,11 @@ def _decode(case, dev, total, P=0, new=None):
     return out.cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("S", [7, 64, 257])
+@pytest.mark.parametrize("S", [7, 64, 200, 256, 257])
 def test_ragged_grid_any_hint(S):
-    """The exact total (short partitions for the ragged batch), a quarter of
-    it (a hint below the truth) and the near-uniform bound (long
-    partitions)."""
+    """The exact total (the balanced split; short partitions past 256
+    sequences), a quarter of it (a hint below the truth: longer ranges than
+    the hint suggests) and the near-uniform bound (long partitions)."""
     lens = _lognormal(S, S, 300)
     lens[0] = max(int(lens.max()), 1500)             # one long sequence: most of its partitions' peers empty
     case = synth.make_case("ragged_%d" % S, 100 + S, lens, 32, 8, 128, 16, free_frac=0.05)
@@ -84,3 +86,16 @@ def test_ragged_grid_quantised(kv, mode):
         say("ragged grid quantised", kv, mode, "hint", hint)
         err = max_err(_decode(case, dev, hint), expect)
         assert err <= TOL_BF16, (kv, mode, hint, err)
+
+
+def test_ragged_hint_with_every_sequence_empty():
+    """A hint that claims tokens for a batch of empty sequences (max length
+    64 passed): nothing to attend to, every output row zero."""
+    case = synth.make_case("ragged_empty", 81, [64] + [0] * 11, 16, 4, 128, 16)
+    case.context_lens[:] = 0
+    dev = case_on_device(case)
+    say("ragged hint, all sequences empty")
+    out = pa.decode(dev["q"], dev["k"], dev["v"], dev["bt"], dev["cl"], float(case.scale), 64,
+                    total_context_len=100)
+    torch.cuda.synchronize()
+    assert np.all(out.cpu().numpy() == 0.0)
