@@ -664,6 +664,9 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
       kr[i] = c * 16 + ((i * 4 + j) ^ c);            // read slot of d-chunk (i*4 + j), row c
     }
   }
+  // per-(block, head) scales: NB * Hkv floats (< 2^30 entries: the pool fits one GPU)
+  const __amdgpu_buffer_rsrc_t rks = tile_rsrc((const char*)k_scales, NB * Hkv * 4);
+  const __amdgpu_buffer_rsrc_t rvs = tile_rsrc((const char*)v_scales, NB * Hkv * 4);
   auto tile_ptrs = [&](int ti, const char*& kb, const char*& vb, bool& ok, Sc& ks, Sc& vs) {
     const int e = (ti * 16) / BS - tbl_base;
     int b = e < 64 ? __builtin_amdgcn_readlane(tbl0, e) : __builtin_amdgcn_readlane(tbl1, e - 64);
@@ -678,8 +681,12 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
       ks = *(const f32x4_t*)(k_scales + si);
       vs = *(const f32x4_t*)(v_scales + si);
     } else if (I8) {
-      ks = k_scales[(size_t)b * Hkv + g];
-      vs = v_scales[(size_t)b * Hkv + g];
+      // Vector-memory loads, not scalar ones: a scalar load shares the
+      // LDS wait counter, so the current tile's wait for its K rows in LDS
+      // would also wait for the next tile's scales to arrive from memory.
+      const unsigned so = (unsigned)(b * Hkv + g) * 4u;
+      ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, so, 0, 0));
+      vs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, so, 0, 0));
     }
   };
 
