@@ -95,8 +95,8 @@ def cpu_model() -> str:
 # (profiles/decode_mfma_llama3-70b_pmc_traffic.md).  Valid only for the
 # sources the counters were taken on: a changed kernel or plan reports null.
 PMC_TRAFFIC = {
-    "sources_sha256": "a4eaef347ff05f4da62ecd1bbd20da67c9fed3ef809edc30ad72f6a92608799d",
-    "fetch_kib": 320996.6 + 1382.5,
+    "sources_sha256": "e4d6d7e4701a0a5eff28c8547ef92b9273c0df3d7a0f3560dc3a69a0e6d04342",
+    "fetch_kib": 321009.1 + 1391.0,
     "write_kib": 2680.0 + 640.0,
     "fetch_factor": 1.99227,
     "write_factor": 1.0,
