@@ -320,36 +320,19 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
          ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)hi) << 16);
 }
 
-// Work item of a wave: (sequence s, kv head g, partition p).  With the kv
-// head fastest, the waves that start together read neighbouring 4 KB
-// chunks of the same physical blocks (measured ~1 % faster than partition
-// fastest on the 70B-shaped layer).
-constexpr int kItemOrder = 1;     // 0: p fastest; 1: g fastest
-constexpr bool kXcdRemap = false;  // give each XCD a contiguous range of items
-__device__ __forceinline__ void mfma_item(int bid, int nblk, int Hkv, int nP, int CG, int& s, int& g, int& p,
-                                          int& cg) {
-  int item = bid;
-  if (kXcdRemap) {
-    // workgroups are dispatched round-robin over the 8 XCDs: XCD x runs
-    // bid = x, x+8, ...; map those to one contiguous range of items
-    const int q = nblk / 8, r = nblk % 8, x = bid % 8, l = bid / 8;
-    item = x * q + min(x, r) + l;
-  }
-  if (kItemOrder == 0) {
-    p = item % nP;
-    const int sg = item / nP;
-    g = sg % Hkv;
-    const int sc = sg / Hkv;
-    cg = sc % CG;
-    s = sc / CG;
-  } else {
-    g = item % Hkv;
-    const int rest = item / Hkv;
-    cg = rest % CG;
-    const int sp = rest / CG;
-    p = sp % nP;
-    s = sp / nP;
-  }
+// Work item of a wave: (sequence s, kv head g, partition p[, column group
+// cg]), kv head fastest: the waves that start together read neighbouring
+// 4 KB chunks of the same physical blocks (measured ~1 % faster than
+// partition fastest on the 70B-shaped layer; giving each XCD a contiguous
+// range of items instead of the round-robin dispatch order measured no
+// better).
+__device__ __forceinline__ void mfma_item(int item, int Hkv, int nP, int CG, int& s, int& g, int& p, int& cg) {
+  g = item % Hkv;
+  const int rest = item / Hkv;
+  cg = rest % CG;
+  const int sp = rest / CG;
+  p = sp % nP;
+  s = sp / nP;
 }
 
 // A shared prefix (cascade): the first items of the grid attend every
@@ -523,11 +506,11 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
     p = 0;
     cgw = 0;
   } else if (pre) {
-    mfma_item(blockIdx.x, cz.items, Hkv, cz.nP, cz.CG, s, g, p, cgw);
+    mfma_item(blockIdx.x, Hkv, cz.nP, cz.CG, s, g, p, cgw);
   } else if (MODE == kModeCascade) {
-    mfma_item(blockIdx.x - cz.items, gridDim.x - cz.items, Hkv, nP, CG, s, g, p, cgw);
+    mfma_item(blockIdx.x - cz.items, Hkv, nP, CG, s, g, p, cgw);
   } else {
-    mfma_item(blockIdx.x, gridDim.x, Hkv, nP, CG, s, g, p, cgw);
+    mfma_item(blockIdx.x, Hkv, nP, CG, s, g, p, cgw);
   }
   // this wave's tokens: [t_begin, t_end) of a table row of row_blocks entries
   const int32_t* trow = pre ? cz.table : tables + (size_t)s * max_blocks;
