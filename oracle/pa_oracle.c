@@ -404,24 +404,33 @@ void oracle_quantize_int8(int8_t* codes, float* scales, const float* x,
  * Nearest E4M3 code to the fp32 value v: the finite code whose value is
  * closest to v; between two equally close codes the one with an even
  * mantissa field; |v| beyond the largest finite value (448) gives +-448
- * (saturation); NaN gives the NaN code 0x7F.  Written as a search over all
- * codes of v's sign, so that it follows the definition above literally.
+ * (saturation); NaN gives the NaN code 0x7F.  The non-negative finite
+ * codes 0..0x7E have strictly increasing values, so the search bisects for
+ * the last code whose value does not exceed |v| and compares it with the
+ * next code up.
  */
 uint8_t oracle_fp8_e4m3_encode(float v) {
   const int sign = signbit(v) ? 1 : 0;
   const double a = fabs((double)v);
-  int best = 0;
-  double best_err;
+  int best;
   if (isnan(v)) return 0x7F;
-  best_err = fabs(oracle_fp8_e4m3_value(0) - a);
-  for (int c = 1; c < 0x7F; ++c) { /* 0x7F is NaN */
-    double err = fabs(oracle_fp8_e4m3_value((uint8_t)c) - a);
-    if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
-      best = c;
-      best_err = err;
+  if (a >= 448.0) {
+    best = 0x7E;
+  } else {
+    /* value(lo) <= a < value(hi) throughout */
+    int lo = 0, hi = 0x7E;
+    double below, above;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) / 2;
+      if (oracle_fp8_e4m3_value((uint8_t)mid) <= a)
+        lo = mid;
+      else
+        hi = mid;
     }
+    below = a - oracle_fp8_e4m3_value((uint8_t)lo);
+    above = oracle_fp8_e4m3_value((uint8_t)hi) - a;
+    best = (above < below || (above == below && (hi & 1) == 0)) ? hi : lo;
   }
-  if (a > 448.0) best = 0x7E;
   return (uint8_t)(best | (sign << 7));
 }
 

@@ -45,7 +45,8 @@ MUTANTS = [
      "else v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
     ("E4M3 subnormals read as normals", "if (e == 0) v = ldexp((double)m / 8.0, 1 - 7);",
      "if (e == 0) v = ldexp(1.0 + (double)m / 8.0, -7);"),
-    ("E4M3 ties to odd", "(c & 1) == 0 && (best & 1) == 1", "(c & 1) == 1 && (best & 1) == 0"),
+    ("E4M3 ties to odd", "(above == below && (hi & 1) == 0)", "(above == below && (hi & 1) == 1)"),
+    ("E4M3 rounds down always", "best = (above < below ||", "best = (0 && above < below ||"),
     ("per-token scale read per block",
      "return scale_mode == OR_SCALE_TOKEN ? (b * Hkv + g) * BS + slot : b * Hkv + g;",
      "return scale_mode == OR_SCALE_TOKEN ? (b * Hkv + g) * BS : b * Hkv + g;"),
