@@ -95,10 +95,10 @@ def cpu_model() -> str:
 # (profiles/decode_mfma_llama3-70b_pmc_traffic.md).  Valid only for the
 # sources the counters were taken on: a changed kernel or plan reports null.
 PMC_TRAFFIC = {
-    "sources_sha256": "e4d6d7e4701a0a5eff28c8547ef92b9273c0df3d7a0f3560dc3a69a0e6d04342",
-    "fetch_kib": 321009.1 + 1391.0,
+    "sources_sha256": "bb24f875d5b82f3672f16403830e16d232e455d395455e57f7adf204869e24de",
+    "fetch_kib": 320973.7 + 1391.0,
     "write_kib": 2680.0 + 640.0,
-    "fetch_factor": 1.99227,
+    "fetch_factor": 1.99226,
     "write_factor": 1.0,
 }
 PMC_SOURCES = ("paged_kv_cache_192_amd/csrc/pa_decode.hip", "paged_kv_cache_192_amd/csrc/pa_api.cpp",
