@@ -90,15 +90,15 @@ def cpu_model() -> str:
 
 # HBM bytes of one pa_decode call on the 70B-shaped layer (decode + merge
 # kernels, fused cache write), from rocprofv3 --pmc FETCH_SIZE and
-# WRITE_SIZE runs: FETCH_SIZE scaled by 1.99226 and WRITE_SIZE by 1.0, the
+# WRITE_SIZE runs: FETCH_SIZE scaled by 1.99227 and WRITE_SIZE by 1.0, the
 # ratios of a plain copy's known bytes to what the same counters read for it
 # (profiles/decode_mfma_llama3-70b_pmc_traffic.md).  Valid only for the
 # sources the counters were taken on: a changed kernel or plan reports null.
 PMC_TRAFFIC = {
-    "sources_sha256": "bb24f875d5b82f3672f16403830e16d232e455d395455e57f7adf204869e24de",
-    "fetch_kib": 320973.7 + 1391.0,
+    "sources_sha256": "09182017e6db66dfb8982d361628100ce686847148bd92964a4ba22cd63b9cdc",
+    "fetch_kib": 320967.625 + 1391.0,
     "write_kib": 2680.0 + 640.0,
-    "fetch_factor": 1.99226,
+    "fetch_factor": 1.99227,
     "write_factor": 1.0,
 }
 PMC_SOURCES = ("paged_kv_cache_192_amd/csrc/pa_decode.hip", "paged_kv_cache_192_amd/csrc/pa_api.cpp",

@@ -33,6 +33,19 @@
  *  - Contents of device arrays (table entries, slot ids, pair ids) are the
  *    caller's responsibility; the kernels skip or clamp nothing beyond what
  *    each call documents.
+ *  - With the environment variable PA_DEBUG set (to anything but "" or
+ *    "0"; read on every call), the calls check those contents before any
+ *    launch and return PA_ERR_INVALID naming the first violation: decode
+ *    table entries in use inside [0, num_blocks), context lengths within
+ *    [0, min(max_context_len, max_blocks_per_seq * block_size)], query row
+ *    offsets (from 0 to num_queries, at most max_query_len and the
+ *    sequence's length each), table rows starting with the shared prefix,
+ *    distinct slots for the fused write; cache-write slots inside the pool
+ *    and distinct; copy pairs inside the pool with distinct destinations
+ *    disjoint from the sources; distinct swap destinations.  The arrays are
+ *    copied to the host on the call's stream, which is synchronised, so a
+ *    checked call waits for the stream's earlier work; while the stream is
+ *    being captured into a graph the checks are skipped.
  *  - Kernels are stateless and re-entrant; a pa_pool is not thread-safe.
  */
 #ifndef PA_H_

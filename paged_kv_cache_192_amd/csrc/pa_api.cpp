@@ -322,6 +322,7 @@ pa_status pa_decode(const pa_decode_args* a) {
     if (!aligned(a->workspace, 16)) return fail(PA_ERR_INVALID, "pa_decode: workspace must be 16-byte aligned");
   }
   hipStream_t st = (hipStream_t)a->stream;
+  if (debug_enabled() && (s = debug_check_decode(a, st)) != PA_OK) return s;
   s = p.kind == KERNEL_MFMA ? launch_decode_mfma(a, p, st) : launch_decode_valu(a, p, st);
   if (s != PA_OK || p.ws_partitions == 1) return s;
   return launch_decode_merge(a, p, st);
@@ -366,6 +367,9 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
   if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(slot_mapping, 8))
     return fail(PA_ERR_INVALID, "pa_reshape_and_cache: key, value and caches must be 16-byte aligned");
+  if (debug_enabled() && (s = debug_check_slots(slot_mapping, num_tokens, num_blocks, block_size, (hipStream_t)stream,
+                                                "pa_reshape_and_cache")) != PA_OK)
+    return s;
   return launch_reshape_and_cache(key, value, k_cache, v_cache, dtype_bytes(kv_dtype), slot_mapping, num_tokens,
                                   num_kv_heads, head_dim, block_size, num_blocks, (hipStream_t)stream);
 }
@@ -385,6 +389,9 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, pa_dtype kv_dtype, float*
   if (!k_cache || !v_cache || !block_pairs) return fail(PA_ERR_INVALID, "pa_copy_blocks: NULL device pointer");
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_pairs, 8))
     return fail(PA_ERR_INVALID, "pa_copy_blocks: caches must be 16-byte aligned");
+  if (debug_enabled() && (s = debug_check_pairs(block_pairs, num_pairs, num_blocks, num_blocks, true,
+                                                (hipStream_t)stream, "pa_copy_blocks")) != PA_OK)
+    return s;
   const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * dtype_bytes(kv_dtype);
   return launch_block_copy(k_cache, v_cache, k_scales, v_scales, k_cache, v_cache, k_scales, v_scales, block_bytes,
                            q8 ? scales_per_block(scale_mode, num_kv_heads, block_size) : 0, block_pairs, num_pairs,
@@ -436,6 +443,9 @@ pa_status pa_swap_blocks(const void* src_k, const void* src_v, const float* src_
     if (!v) return fail(PA_ERR_INVALID, "pa_swap_blocks: argument %d is neither device nor pinned host memory", i);
     dv[i] = v;
   }
+  if (debug_enabled() && (s = debug_check_pairs(block_pairs, num_pairs, src_num_blocks, dst_num_blocks,
+                                                src_k == dst_k, (hipStream_t)stream, "pa_swap_blocks")) != PA_OK)
+    return s;
   const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * dtype_bytes(kv_dtype);
   return launch_block_copy(dv[0], dv[1], (const float*)dv[5], (const float*)dv[6], (void*)dv[2], (void*)dv[3],
                            (float*)dv[7], (float*)dv[8], block_bytes,
@@ -467,6 +477,9 @@ pa_status pa_quantize_and_cache(const void* key, const void* value, pa_dtype src
   if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(k_scales, 4) || !aligned(v_scales, 4) || !aligned(slot_mapping, 8))
     return fail(PA_ERR_INVALID, "pa_quantize_and_cache: key, value and caches must be 16-byte aligned");
+  if (debug_enabled() && (s = debug_check_slots(slot_mapping, num_tokens, num_blocks, block_size, (hipStream_t)stream,
+                                                "pa_quantize_and_cache")) != PA_OK)
+    return s;
   return launch_quantize_and_cache(key, value, src_dtype, k_cache, v_cache, kv_dtype, k_scales, v_scales, scale_mode,
                                    k_static_scale, v_static_scale, slot_mapping, num_tokens, num_kv_heads, head_dim,
                                    block_size, num_blocks, (hipStream_t)stream);

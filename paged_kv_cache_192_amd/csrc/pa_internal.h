@@ -15,6 +15,15 @@ namespace pa {
 pa_status fail(pa_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 pa_status hip_fail(hipError_t e, const char* what);
 
+// Checks of the device-side preconditions pa.h leaves to the caller, when
+// the environment variable PA_DEBUG is set (pa_debug.cpp).
+bool debug_enabled();
+pa_status debug_check_decode(const pa_decode_args* a, hipStream_t st);
+pa_status debug_check_slots(const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks, int32_t block_size,
+                            hipStream_t st, const char* fn);
+pa_status debug_check_pairs(const int64_t* block_pairs, int32_t num_pairs, int32_t src_num_blocks,
+                            int32_t dst_num_blocks, bool same_pool, hipStream_t st, const char* fn);
+
 inline int dtype_bytes(pa_dtype t) {
   switch (t) {
     case PA_F32: return 4;
