@@ -272,7 +272,12 @@ using namespace pa;
 extern "C" {
 
 const char* pa_status_string(pa_status s) {
-  switch (s) {
+  // A C caller may pass any int; read it as one (an enum value outside the
+  // enumerators' range is undefined in C++).
+  static_assert(sizeof(pa_status) == sizeof(int), "pa_status is an int");
+  int code;
+  std::memcpy(&code, &s, sizeof code);
+  switch (code) {
     case PA_OK: return "PA_OK";
     case PA_ERR_INVALID: return "PA_ERR_INVALID";
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
