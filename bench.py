@@ -95,8 +95,8 @@ def cpu_model() -> str:
 # (profiles/decode_mfma_llama3-70b_pmc_traffic.md).  Valid only for the
 # sources the counters were taken on: a changed kernel or plan reports null.
 PMC_TRAFFIC = {
-    "sources_sha256": "09182017e6db66dfb8982d361628100ce686847148bd92964a4ba22cd63b9cdc",
-    "fetch_kib": 320967.625 + 1391.0,
+    "sources_sha256": "6a2c31abaa750e88492ff83466544da9316734a961b8e9c674c6ef3741fdcf20",
+    "fetch_kib": 320953.59375 + 1391.0,
     "write_kib": 2680.0 + 640.0,
     "fetch_factor": 1.99227,
     "write_factor": 1.0,
