@@ -566,6 +566,19 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
     orow[u] = (size_t)qrow * Hq + h;
   }
 
+  // The lowest visible-token limit over this wave's existing columns: a
+  // tile entirely below it (and in the pool) needs no mask, and its scores
+  // are all finite.
+  int lim_lo = t_end;
+  if (MQ || pre) {  // wave-uniform; every other item's columns all see up to t_end
+    int lo = 0x7fffffff;
+#pragma unroll
+    for (int u = 0; u < NCG; ++u) lo = min(lo, head_ok[u] ? lim[u] : 0x7fffffff);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) lo = min(lo, __shfl_xor(lo, d, 64));
+    lim_lo = __builtin_amdgcn_readfirstlane(lo);
+  }
+
   if (t_begin >= t_end) {
     // Nothing to attend to.  With one partition the output row is zero;
     // otherwise the partial is marked empty (no weight) for the merge.
@@ -683,7 +696,10 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
     l_run[u] = 0.f;
   }
 
-  auto compute = [&](MfmaTile<I8>& T, int ti, bool ok, const Sc& ks, const Sc& vs) {
+  // FULL: every token of the tile is in the pool and visible to every
+  // existing column (no mask; the scores, and so the reference, are finite).
+  auto compute = [&](auto full_tag, MfmaTile<I8>& T, int ti, bool ok, const Sc& ks, const Sc& vs) {
+    constexpr bool FULL = decltype(full_tag)::value;
     const bool new_tile = owns_new && ti == (tnew >> 4);  // wave-uniform
     const int rnew = tnew & 15;
     if (I8) {
@@ -726,7 +742,7 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
         float xs = qk_log2;
         if constexpr (TOKSC) xs *= ks[r];
         else if (I8) xs *= ks;
-        x[r] = (ok && tok0 + r < (MODE != kModeDecode ? lim[u] : t_end)) ? sc[r] * xs : kNegInf;
+        x[r] = (FULL || (ok && tok0 + r < (MODE != kModeDecode ? lim[u] : t_end))) ? sc[r] * xs : kNegInf;
       }
       float mloc = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       mloc = xor_max_rows(mloc);
@@ -742,7 +758,7 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
       }
       float pw[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pw[r] = x[r] == kNegInf ? 0.f : fast_exp2(x[r] - m_run[u]);
+      for (int r = 0; r < 4; ++r) pw[r] = (FULL || x[r] != kNegInf) ? fast_exp2(x[r] - m_run[u]) : 0.f;
       l_run[u] += (pw[0] + pw[1]) + (pw[2] + pw[3]);
       if constexpr (TOKSC) {
 #pragma unroll
@@ -763,7 +779,7 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
     }
     // ---- V^T operands: rows 4j+i of this lane; rows past the context are
     // zeroed (they may hold NaN and would poison 0 * NaN in the MFMA)
-    const bool partial = !ok || ti * 16 + 15 >= t_end;  // wave-uniform
+    const bool partial = !FULL && (!ok || ti * 16 + 15 >= t_end);  // wave-uniform
     if (partial) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -806,27 +822,42 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
 
   // Software pipeline: the next tile's loads are in flight while the
   // current one is computed.  The last prefetch re-reads the final tile
-  // (always in bounds) so every iteration issues the same loads.
+  // (always in bounds) so every iteration issues the same loads.  The
+  // tiles below lim_lo (visible to every existing column) run first with
+  // the mask-free tile body, the rest with the masked one, as two loops so
+  // that the two bodies are never live together; a fully visible tile
+  // whose block id is outside the pool is skipped (it contributes nothing,
+  // as the masked body would make it).
   MfmaTile<I8> A, B;
   const char *kA, *vA, *kB, *vB;
   bool okA, okB;
   Sc ksA{}, vsA{}, ksB{}, vsB{};
-  // wave wv: tiles tile_begin + wv, + WPI, ...
-  int ti = tile_begin + wv;
-  if (ti < tile_end) {
+  auto run_tiles = [&](auto full_tag, int ti, int tend) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    if (ti >= tend) return;
     tile_ptrs(ti, kA, vA, okA, ksA, vsA);
     mfma_load_tile<I8>(A, kA, vA, koff, voff);
     while (true) {
-      tile_ptrs(ti + WPI < tile_end ? ti + WPI : ti, kB, vB, okB, ksB, vsB);
+      tile_ptrs(ti + WPI < tend ? ti + WPI : ti, kB, vB, okB, ksB, vsB);
       mfma_load_tile<I8>(B, kB, vB, koff, voff);
-      compute(A, ti, okA, ksA, vsA);
-      if ((ti += WPI) >= tile_end) break;
-      tile_ptrs(ti + WPI < tile_end ? ti + WPI : ti, kA, vA, okA, ksA, vsA);
+      if (!FULL || okA) compute(full_tag, A, ti, okA, ksA, vsA);
+      if ((ti += WPI) >= tend) break;
+      tile_ptrs(ti + WPI < tend ? ti + WPI : ti, kA, vA, okA, ksA, vsA);
       mfma_load_tile<I8>(A, kA, vA, koff, voff);
-      compute(B, ti, okB, ksB, vsB);
-      if ((ti += WPI) >= tile_end) break;
+      if (!FULL || okB) compute(full_tag, B, ti, okB, ksB, vsB);
+      if ((ti += WPI) >= tend) break;
     }
+  };
+  // wave wv: tiles tile_begin + wv, + WPI, ...; tiles below full_end are
+  // fully visible.  The split costs the second loop an unoverlapped first
+  // load, so a wave takes it only with at least 16 fully visible tiles.
+  const int full_end = min(tile_end, max(lim_lo, 0) >> 4);
+  int ti = tile_begin + wv;
+  if (full_end - ti >= 16 * WPI) {
+    run_tiles(std::true_type{}, ti, full_end);
+    ti += (full_end - ti + WPI - 1) / WPI * WPI;
   }
+  run_tiles(std::false_type{}, ti, tile_end);
 
   if (owns_new && j == 0) {
     const int e = tnew / BS - tbl_base;
