@@ -744,11 +744,14 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
         else if (I8) xs *= ks;
         x[r] = (FULL || (ok && tok0 + r < (MODE != kModeDecode ? lim[u] : t_end))) ? sc[r] * xs : kNegInf;
       }
-      float mloc = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      mloc = xor_max_rows(mloc);
-      // ---- lazy rescale of the running reference
-      const bool need = mloc > m_run[u] + kRescaleThreshold;
-      if (__any(need)) {
+      // ---- lazy rescale of the running reference.  A column's maximum
+      // exceeds its reference (the same on the column's four rows) exactly
+      // when one of its lanes' own maxima does, so the cross-row maximum is
+      // formed only in the rare branch that moves the reference.
+      const float xloc = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      if (__any(xloc > m_run[u] + kRescaleThreshold)) {
+        const float mloc = xor_max_rows(xloc);
+        const bool need = mloc > m_run[u] + kRescaleThreshold;
         const float m_new = need ? mloc : m_run[u];
         const float alpha = need ? fast_exp2(m_run[u] - m_new) : 1.f;
 #pragma unroll
