@@ -95,8 +95,8 @@ def cpu_model() -> str:
 # (profiles/decode_mfma_llama3-70b_pmc_traffic.md).  Valid only for the
 # sources the counters were taken on: a changed kernel or plan reports null.
 PMC_TRAFFIC = {
-    "sources_sha256": "3ced6f8d08e8e8d488a90eec27c0379c62c2173d74955e5f6883bea31ae68cdb",
-    "fetch_kib": 320927.78125 + 1390.5,
+    "sources_sha256": "d1d29593642f31caa0766fdb1dbed72f499c486fe2fd3d3dcdbb911f9958765b",
+    "fetch_kib": 320921.59375 + 1391.0,
     "write_kib": 2680.0 + 640.0,
     "fetch_factor": 1.99227,
     "write_factor": 1.0,
