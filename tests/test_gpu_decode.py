@@ -400,3 +400,35 @@ def test_fused_cache_write(shape):
             assert np.array_equal(oa, ob), (kern, P)
             err = max_err(ob, expect)
             assert err <= tolerance(case), (kern, P, err)
+
+
+@pytest.mark.parametrize("kvd", [synth.BF16, synth.I8])
+def test_block_outside_the_pool_contributes_nothing(kvd):
+    """An in-use table entry outside [0, num_blocks) -- a caller error that
+    PA_DEBUG reports -- is never read: its tokens drop out of the sequence,
+    so the result equals the oracle's attention over the sequence with that
+    block removed (attention does not depend on token order).  Library
+    partitions (short: the masked tile body) and 1,024-token partitions (the
+    bad block deep inside a run of fully visible tiles: the mask-free
+    body)."""
+    case = synth.make_case("bad-block", 91, [1000, 700, 33], 32, 8, 128, 16, kv_dtype=kvd)
+    if kvd == synth.I8:
+        quantize_case(case)
+    NB = case.k_cache.shape[0]
+    ref_tables = case.block_tables.copy()
+    ref_lens = case.context_lens.copy()
+    for s, k in ((0, 20), (1, 3)):                 # full blocks, inside the sequence
+        row = list(case.block_tables[s])
+        ref_tables[s] = row[:k] + row[k + 1:] + [-1]
+        ref_lens[s] -= 16
+    case.block_tables[0, 20] = NB + 7
+    case.block_tables[1, 3] = -5
+    expect = oracle.paged_decode(case.q, case.k_cache, case.v_cache, ref_tables, ref_lens, float(case.scale),
+                                 case.k_scales, case.v_scales)
+    dev = case_on_device(case)
+    kernels = (0, VALU, MFMA) if kvd == synth.BF16 else (MFMA,)
+    for kern in kernels:
+        for P in (0, 1024):
+            say("block outside the pool", kvd, "kernel", kern, "partition", P)
+            err = max_err(run_decode(case, dev, partition_tokens=P, kernel=kern), expect)
+            assert err <= TOL_BF16, (kvd, kern, P, err)
