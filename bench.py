@@ -711,7 +711,7 @@ def main():
                          "workloads, reported as a per-layer record")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path (asked for --gpus %d)"
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path (asked for --gpus %d)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.layers != 80:
