@@ -77,6 +77,17 @@ def waste_report(context_lens, block_size: int, reserved: int):
 # benchmark
 # --------------------------------------------------------------------------
 
+def pctl(sorted_vals, p: float) -> float:
+    """p-th percentile of an ascending list, linear between closest ranks."""
+    n = len(sorted_vals)
+    if n == 1:
+        return float(sorted_vals[0])
+    x = (n - 1) * p / 100.0
+    i = int(math.floor(x))
+    j = min(i + 1, n - 1)
+    return float(sorted_vals[i] + (sorted_vals[j] - sorted_vals[i]) * (x - i))
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -122,6 +133,29 @@ def measured_traffic(fused: bool):
     return int(round((t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"]) * 1024))
 
 
+def llama70b_prepare(stream, Q, K, V, KN, VN, bt, cl, outs, ws, slots, total_context_len: int, scale: float,
+                     context_len: int, block_size: int, fused: bool = True, partition_tokens: int = 0):
+    """One step of the 70B-shaped workload, arguments packed once, on
+    `stream`: per layer the write of the new token's K/V into its slot and
+    the decode over all tokens -- one fused pa_decode call per layer (the
+    timed form), or with fused=False a slot-mapping launch per step and a
+    cache-write launch per layer before each decode.  Returns (calls before
+    the layers, [(write calls, decode call)] per layer)."""
+    import paged_kv_cache_192_amd as pa
+
+    pre = [pa.prepare_slot_mapping(bt, block_size, slots, context_lens=cl, stream=stream)] if not fused else []
+    layers = []
+    for layer in range(len(Q)):
+        writes = [] if fused else [pa.prepare_reshape_and_cache(KN[layer], VN[layer], K[layer], V[layer], slots,
+                                                                 stream=stream)]
+        d = pa.PreparedDecode(Q[layer], K[layer], V[layer], bt, cl, scale, context_len, outs[layer], workspace=ws,
+                              stream=stream, new_key=KN[layer] if fused else None,
+                              new_value=VN[layer] if fused else None, partition_tokens=partition_tokens,
+                              total_context_len=total_context_len)
+        layers.append((writes, d))
+    return pre, layers
+
+
 def run(args) -> dict:
     import numpy as np
     import torch
@@ -161,21 +195,8 @@ def run(args) -> dict:
     fused = not args.unfused
 
     def prepare(stream):
-        """One step's calls, arguments packed once, on `stream`: per layer the
-        new token's cache write and the decode (one fused launch by default;
-        with --unfused a slot-mapping launch per step and a cache-write
-        launch per layer before each decode)."""
-        pre = [pa.prepare_slot_mapping(bt, BS, slots, context_lens=cl, stream=stream)] if not fused else []
-        layers = []
-        for layer in range(L):
-            writes = [] if fused else [pa.prepare_reshape_and_cache(KN[layer], VN[layer], K[layer], V[layer], slots,
-                                                                     stream=stream)]
-            d = pa.PreparedDecode(Q[layer], K[layer], V[layer], bt, cl, scale, ctx, outs[layer], workspace=ws,
-                                  stream=stream, new_key=KN[layer] if fused else None,
-                                  new_value=VN[layer] if fused else None, partition_tokens=args.partition_tokens,
-                                  total_context_len=int(st["context_lens"].sum()))
-            layers.append((writes, d))
-        return pre, layers
+        return llama70b_prepare(stream, Q, K, V, KN, VN, bt, cl, outs, ws, slots, int(st["context_lens"].sum()),
+                                scale, ctx, BS, fused, args.partition_tokens)
 
     main_stream = torch.cuda.current_stream()
     eager_pre, eager_layers = prepare(main_stream)
@@ -221,17 +242,23 @@ def run(args) -> dict:
     if not torch.equal(torch.stack(outs), ref):
         raise RuntimeError("graph replay differs from the eager step")
 
-    # timed region: exactly `steps` steps between two synchronisations
+    # timed region: exactly `steps` steps between two synchronisations; an
+    # event pair around each step gives the per-step distribution (events
+    # are recorded on the stream the step runs on, no synchronisation)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        step_ev[i].record()
         step()
+    step_ev[args.steps].record()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = e0.elapsed_time(e1) / args.steps
+    step_ms = sorted(step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps))
 
     # per-launch duration of the decode call: events around each eager call
     launch_ms = []
@@ -278,6 +305,9 @@ def run(args) -> dict:
                    "kv_dtype": "bf16", "global_batch": S, "seq_len": ctx},
         "tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "step_ms": {"p10": round(pctl(step_ms, 10), 4), "p50": round(pctl(step_ms, 50), 4),
+                    "p90": round(pctl(step_ms, 90), 4), "min": round(step_ms[0], 4), "max": round(step_ms[-1], 4),
+                    "source": "event pair around each step of the timed region"},
         "kv_bytes_per_step": kv_step,
         "wall_s_timed_region": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

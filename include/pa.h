@@ -114,7 +114,9 @@ int32_t pa_abi_version(void);
  *                 (PA_SCALE_BLOCK) or [num_blocks][num_kv_heads][block_size]
  *                 (PA_SCALE_TOKEN)
  *   block_tables  [num_seqs][max_blocks_per_seq] int32; entries past
- *                 ceil(n / BS) are never read
+ *                 ceil(n / BS) are never used, but the matrix-core kernel
+ *                 may load any entry of the row (in bounds of the row), so
+ *                 every row must be allocated in full
  *   context_lens  [num_seqs] int32, 0 <= n <= max_blocks_per_seq * BS and
  *                 n <= max_context_len
  *   out           [num_seqs][num_q_heads][head_dim] fp32
@@ -177,9 +179,11 @@ int32_t pa_abi_version(void);
  * blocks.  With new_key/new_value, a sequence whose newest token lies
  * inside the prefix (context_lens[s] <= shared_prefix_len) has its row
  * neither stored nor attended (a shared block is never written; its
- * cached token is used).  Used by the matrix-core kernel with one query
- * row per sequence, otherwise ignored; a given partition_tokens then sets
- * the partition length of both the prefix and the per-sequence part.
+ * cached token is used), whichever kernel runs.  The matrix-core kernel
+ * with one query row per sequence reads the prefix once for the batch; the
+ * vector-ALU kernel and several query rows per sequence read it through
+ * each table row as usual.  A given partition_tokens then sets the
+ * partition length of both the prefix and the per-sequence part.
  * shared_prefix_table is a device int32 array (4-byte aligned).
  *
  * `kernel` selects the implementation: 0 = automatic, 1 = vector-ALU
@@ -230,6 +234,11 @@ typedef struct {
  * (device pointers are not read and may be NULL).  PA_ERR_INVALID /
  * PA_ERR_UNSUPPORTED as pa_decode would return. */
 pa_status pa_decode_workspace_size(const pa_decode_args* a, size_t* bytes);
+
+/* The same size as a plain return value: the bytes pa_decode_workspace_size
+ * would store, or SIZE_MAX when it would return an error (pa_last_error()
+ * then says which).  0 means no workspace is needed. */
+size_t pa_decode_workspace_bytes(const pa_decode_args* a);
 
 /* Launch decode attention as defined above. */
 pa_status pa_decode(const pa_decode_args* a);

@@ -96,6 +96,8 @@ def library() -> ctypes.CDLL:
     lib.pa_abi_version.restype = i32
     lib.pa_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_size_t)]
     lib.pa_decode_workspace_size.restype = ctypes.c_int
+    lib.pa_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeArgs)]
+    lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.pa_decode.argtypes = [ctypes.POINTER(DecodeArgs)]
     lib.pa_decode.restype = ctypes.c_int
     lib.pa_slot_mapping.argtypes = [P, i32, i32, P, P, P, i32, i32, P, P]

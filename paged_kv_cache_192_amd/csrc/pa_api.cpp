@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdint>
 #include <cstring>
 
 #include "pa_internal.h"
@@ -299,6 +300,11 @@ pa_status pa_decode_workspace_size(const pa_decode_args* a, size_t* bytes) {
   if (s != PA_OK) return s;
   *bytes = p.workspace_bytes;
   return PA_OK;
+}
+
+size_t pa_decode_workspace_bytes(const pa_decode_args* a) {
+  DecodePlan p;
+  return plan_decode(a, &p) == PA_OK ? p.workspace_bytes : SIZE_MAX;
 }
 
 pa_status pa_decode(const pa_decode_args* a) {

@@ -1055,7 +1055,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
     char* __restrict__ k_cache, char* __restrict__ v_cache, const float* __restrict__ k_scales,
     const float* __restrict__ v_scales, const int32_t* __restrict__ tables, int max_blocks,
     const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int head_groups, int NB, float qk_log2,
-    int P, int nP, const char* __restrict__ new_k, const char* __restrict__ new_v, int tok_scales) {
+    int P, int nP, const char* __restrict__ new_k, const char* __restrict__ new_v, int tok_scales,
+    int prefix_len) {
   constexpr int DC = D / 16;
   constexpr bool I8 = sizeof(KV) == 1;
   constexpr int E = sizeof(KV);
@@ -1114,9 +1115,12 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
   const size_t head_stride = (size_t)BS * D * E;
   // Fused cache write of the newest token (position n - 1): lanes holding
   // that position read its K/V chunk from new_k/new_v instead of the cache;
-  // the first head group's wave stores it into the slot at the end.
+  // the first head group's wave stores it into the slot at the end.  A
+  // position inside a shared prefix (tnew < prefix_len) lies in a block
+  // other sequences read: it is neither stored nor taken from new_k/new_v.
   const int tnew = n - 1;
-  const bool owns_new = !I8 && new_k != nullptr && tnew >= t_begin && tnew < t_end;  // wave-uniform
+  const bool owns_new = !I8 && new_k != nullptr && tnew >= prefix_len && tnew >= t_begin &&
+                        tnew < t_end;  // wave-uniform
   const size_t new_off = ((size_t)s * Hkv + g) * D * E + (size_t)c * DC * E;
   for (int t4 = t_begin; t4 < t_end; t4 += 16) {
     // one 16-token tile: four passes of four tokens
@@ -1310,7 +1314,7 @@ static void valu_dispatch_g(const pa_decode_args* a, const DecodePlan& p, hipStr
                      a->v_scales, a->block_tables, a->max_blocks_per_seq, a->context_lens, a->num_q_heads,   \
                      a->num_kv_heads, p.G, p.head_groups, a->num_blocks, qk, p.partition_tokens,             \
                      p.num_partitions, (const char*)a->new_key, (const char*)a->new_value,                \
-                     a->kv_scale_mode == PA_SCALE_TOKEN ? 1 : 0)
+                     a->kv_scale_mode == PA_SCALE_TOKEN ? 1 : 0, a->shared_prefix_len)
   switch (p.heads_per_wave) {
     case 1: PA_VALU_LAUNCH(1); break;
     case 2: PA_VALU_LAUNCH(2); break;

@@ -77,6 +77,28 @@ def test_struct_layout_and_workspace_size():
     assert st == pa.PA_ERR_INVALID and "block_size 24" in pa.library().pa_last_error().decode()
 
 
+def test_workspace_bytes_is_the_size_call_as_a_value():
+    """pa_decode_workspace_bytes returns what pa_decode_workspace_size
+    stores, SIZE_MAX where the latter fails, with the same message."""
+    lib = pa.library()
+    size_max = 2 ** (8 * ctypes.sizeof(ctypes.c_size_t)) - 1
+    for over in ({}, {"partition_tokens": 128}, {"partition_tokens": 16}, {"total_context_len": 40},
+                 {"max_context_len": 0}, {"num_seqs": 0}):
+        a = _cpu_args(**over)
+        st, n = _ws(a)
+        assert st == pa.PA_OK, (over, lib.pa_last_error())
+        assert lib.pa_decode_workspace_bytes(ctypes.byref(a)) == n, over
+    for over, text in (({"head_dim": 96}, "head_dim 96"), ({"num_q_heads": 7}, "not a multiple"),
+                       ({"struct_size": 8}, "struct_size"), ({"kernel": 3}, "kernel 3")):
+        a = _cpu_args(**over)
+        st, _ = _ws(a)
+        assert st != pa.PA_OK
+        lib.pa_last_error()
+        assert lib.pa_decode_workspace_bytes(ctypes.byref(a)) == size_max, over
+        assert text in lib.pa_last_error().decode(), (over, lib.pa_last_error())
+    assert lib.pa_decode_workspace_bytes(None) == size_max
+
+
 def test_partition_plan_follows_the_length_hint():
     """Near-equal lengths (hint absent or close to num_seqs * max): a few
     long partitions per sequence.  A ragged batch: short partitions, here
@@ -343,3 +365,29 @@ def test_pool_leak_free_after_cancel_and_fragmentation(golden):
     with pytest.raises(pa.PaError) as e:
         pool.alloc(81)
     assert e.value.status == pa.PA_ERR_OOM and pool.num_free() == 80
+
+
+def test_workload_tables_are_what_the_pool_hands_out():
+    """The workloads' seeded placement (perm = a seeded permutation, each
+    sequence's logical blocks laid out on perm[0], perm[1], ...) is exactly
+    what a pool created with initial_order = perm returns when each
+    sequence's blocks are allocated in sequence order -- through the
+    library's pool and the oracle's pool model alike."""
+    import synth
+
+    st = synth.config3_structure()
+    cases = [(st["block_tables"], st["context_lens"], st["perm"], 16)]
+    for c in (synth.config1(), synth.config2()):
+        cases.append((c.block_tables, c.context_lens, c.perm, c.block_size))
+    for tables, lens, perm, BS in cases:
+        NB = len(perm)
+        pool = pa.BlockPool(NB, initial_order=perm)
+        model = PoolModel(NB, initial_order=perm)
+        for s, n in enumerate(lens):
+            nb = -(-int(n) // BS)
+            got = pool.alloc(nb)
+            rc, exp = model.alloc(nb)
+            assert rc == 0 and got == exp == tables[s, :nb].tolist(), s
+            assert np.all(tables[s, nb:] == -1)
+        assert pool.num_free() == NB - int(np.sum(-(-lens // BS)))
+        pool.close()

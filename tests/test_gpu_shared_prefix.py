@@ -26,7 +26,7 @@ def _shared_case(name, seed, lens, Hq, Hkv, BS, prefix_blocks, kv_dtype=synth.BF
     return case
 
 
-def _run(case, dev, prefix_blocks, partition_tokens=0, hint=False, new=None):
+def _run(case, dev, prefix_blocks, partition_tokens=0, hint=False, new=None, kernel=0):
     BS = case.block_size
     table = to_dev(np.ascontiguousarray(case.block_tables[0, :prefix_blocks]))
     total = int(np.sum(case.context_lens, dtype=np.int64)) if hint else 0
@@ -34,7 +34,7 @@ def _run(case, dev, prefix_blocks, partition_tokens=0, hint=False, new=None):
     out = pa.decode(dev["q"], dev["k"], dev["v"], dev["bt"], dev["cl"], float(case.scale), case.max_context_len,
                     k_scales=dev["ks"], v_scales=dev["vs"], partition_tokens=partition_tokens,
                     total_context_len=total, shared_prefix_table=table, shared_prefix_len=prefix_blocks * BS,
-                    new_key=nk, new_value=nv)
+                    new_key=nk, new_value=nv, kernel=kernel)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64)
 
@@ -125,10 +125,13 @@ def test_config4_with_shared_prefix_and_fused_write():
     assert err <= TOL_BF16, err
 
 
-def test_fused_write_inside_the_prefix_is_skipped():
+@pytest.mark.parametrize("kernel", [0, pa.KERNEL_VALU, pa.KERNEL_MFMA])
+def test_fused_write_inside_the_prefix_is_skipped(kernel):
     """A sequence whose newest token lies inside the shared prefix: its row
     is neither stored (a shared block is never written) nor attended; the
-    others are written and attended as usual."""
+    others are written and attended as usual -- on either kernel (the
+    vector-ALU kernel reads the prefix through each table row, but must
+    skip the same writes)."""
     pb, BS = 4, 16
     L = pb * BS
     lens = [L + 50, L, L - 3, L + 1]
@@ -137,8 +140,8 @@ def test_fused_write_inside_the_prefix_is_skipped():
     k_new = synth.bf16_bits(rng.standard_normal((4, 4, 128), dtype=np.float32))
     v_new = synth.bf16_bits(rng.standard_normal((4, 4, 128), dtype=np.float32))
     dev = case_on_device(case)
-    say("fused write inside the prefix")
-    got = _run(case, dev, pb, new=(to_dev(k_new), to_dev(v_new)))
+    say("fused write inside the prefix, kernel", kernel)
+    got = _run(case, dev, pb, new=(to_dev(k_new), to_dev(v_new)), kernel=kernel)
     written = [0, 3]                                  # sequences past the prefix
     slots = oracle.slot_mapping(case.block_tables[written], case.context_lens[written] - 1, BS)
     oracle.reshape_and_cache(k_new[written], v_new[written], case.k_cache, case.v_cache, slots)
