@@ -243,6 +243,22 @@ size_t pa_decode_workspace_bytes(const pa_decode_args* a);
 /* Launch decode attention as defined above. */
 pa_status pa_decode(const pa_decode_args* a);
 
+/* pa_decode for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the split-K workspace is a fixed array of
+ * pa_decode_noalloc_scratch_bytes() bytes (64 MiB) that the library owns on
+ * each GPU it runs on, held from the library's load until the process
+ * ends.  a->workspace and a->workspace_bytes are ignored; everything else,
+ * the result included, is as for pa_decode.  Arguments whose plan needs
+ * more workspace than the array holds return PA_ERR_INVALID before any
+ * launch.  The array's device address is looked up on the first call made
+ * with each device current (the stream's device must be current, as for
+ * any launch).  Every call on one GPU shares that GPU's array: calls that
+ * may overlap on one GPU (two streams, two threads) race.  Calls no
+ * hipMalloc or hipFree. */
+pa_status pa_decode_noalloc(const pa_decode_args* a);
+size_t pa_decode_noalloc_scratch_bytes(void);
+
 /* ------------------------------------------------------------------------
  * Slot mapping: where each new token goes
  * ------------------------------------------------------------------------

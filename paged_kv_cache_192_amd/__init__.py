@@ -100,6 +100,10 @@ def library() -> ctypes.CDLL:
     lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.pa_decode.argtypes = [ctypes.POINTER(DecodeArgs)]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_noalloc.argtypes = [ctypes.POINTER(DecodeArgs)]
+    lib.pa_decode_noalloc.restype = ctypes.c_int
+    lib.pa_decode_noalloc_scratch_bytes.argtypes = []
+    lib.pa_decode_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.pa_slot_mapping.argtypes = [P, i32, i32, P, P, P, i32, i32, P, P]
     lib.pa_slot_mapping.restype = ctypes.c_int
     lib.pa_reshape_and_cache.argtypes = [P, P, P, P, ctypes.c_int, P, i32, i32, i32, i32, i32, P]

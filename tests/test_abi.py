@@ -391,3 +391,27 @@ def test_workload_tables_are_what_the_pool_hands_out():
             assert np.all(tables[s, nb:] == -1)
         assert pool.num_free() == NB - int(np.sum(-(-lens // BS)))
         pool.close()
+
+
+def test_noalloc_refuses_on_the_host_what_its_scratch_cannot_hold():
+    """pa_decode_noalloc checks the plan's workspace against its fixed array
+    before touching the device: 256 sequences of up to 32,768 tokens with
+    64 query heads need more than it holds; no GPU is used."""
+    lib = pa.library()
+    cap = lib.pa_decode_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    S, Hq, Hkv, D, BS, MB = 256, 64, 8, 128, 16, 2048
+    q = torch.zeros(S, Hq, D, dtype=torch.bfloat16)
+    kc = torch.zeros(4, Hkv, BS, D, dtype=torch.bfloat16)
+    bt = torch.zeros(S, MB, dtype=torch.int32)
+    cl = torch.zeros(S, dtype=torch.int32)
+    a = pa.make_decode_args(q, kc, kc, bt, cl, 0.1, MB * BS, device_pointers=False)
+    a.out = 0x10000
+    st, need = _ws(a)
+    assert st == pa.PA_OK and need > cap
+    assert lib.pa_decode_noalloc(ctypes.byref(a)) == pa.PA_ERR_INVALID
+    assert "fixed scratch" in lib.pa_last_error().decode()
+    # invalid arguments are refused as pa_decode refuses them
+    b = _cpu_args(head_dim=96)
+    assert lib.pa_decode_noalloc(ctypes.byref(b)) == pa.PA_ERR_INVALID
+    assert "head_dim 96" in lib.pa_last_error().decode()
