@@ -689,6 +689,79 @@ def cpu_baseline(args, K, V, Q, st, L) -> dict:
             "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
+def read_ceiling(args) -> dict:
+    """The memory system's read ceiling for decode's access pattern, on the
+    70B-shaped layer's bytes (K and V caches of 10,000 blocks, 655 MB, one
+    allocation): pa_read_probe reading every 4 KiB (block, kv head) chunk
+    once, in address order (plain streaming) and in the decode's table
+    order (the shuffled blocks of 20 sequences x 500 blocks x 8 kv heads,
+    K then V), over a sweep of wave counts; then pa_decode on the same
+    layer (no fused write, the library's plan), timed the same way, as a
+    fraction of both ceilings.  Each figure is the mean over `steps`
+    launches between two events."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_192_amd as pa
+    import synth
+
+    pa.library()
+    dev = torch.device("cuda:0")
+    c = synth.CFG3
+    st = synth.config3_structure()
+    NB, Hkv, BS, D = st["num_blocks"], c["num_kv_heads"], c["block_size"], c["head_dim"]
+    q, k, v, _, _ = synth.config3_layer_values(0, dev)
+    kv = torch.empty((2, NB, Hkv, BS, D), dtype=torch.bfloat16, device=dev)
+    kv[0].copy_(k)
+    kv[1].copy_(v)
+    del k, v
+    chunk = BS * D * 2
+    assert chunk == 4096
+    n = 2 * NB * Hkv
+    tab = st["block_tables"]
+    order = (tab[:, :, None].astype(np.int64) * Hkv + np.arange(Hkv)[None, None, :]).reshape(-1)
+    ids = torch.from_numpy(np.concatenate([order, order + NB * Hkv]).astype(np.int32)).to(dev)
+    assert ids.numel() == n
+    total = n * chunk
+    sink = torch.empty(16384 * 64, dtype=torch.int32, device=dev)
+
+    def timed(f):
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    res = {"mode": "read-ceiling", "bytes_per_launch": total, "chunk_bytes": chunk, "chunks": n,
+           "steps": args.steps, "sequential_gbs": {}, "table_order_gbs": {}}
+    for waves in (256, 512, 1024, 2048, 4096, 8192, 16384):
+        for name, cid in (("sequential_gbs", None), ("table_order_gbs", ids)):
+            ms = timed(pa.prepare_read_probe(kv, n, sink, chunk_ids=cid, num_waves=waves))
+            res[name][str(waves)] = round(total / (ms * 1e-3) / 1e9, 1)
+    res["best_sequential_gbs"] = max(res["sequential_gbs"].values())
+    res["best_table_order_gbs"] = max(res["table_order_gbs"].values())
+    bt = torch.from_numpy(tab).to(dev)
+    cl = torch.from_numpy(st["context_lens"]).to(dev)
+    out = torch.empty(c["num_seqs"], c["num_q_heads"], D, dtype=torch.float32, device=dev)
+    d = pa.PreparedDecode(q, kv[0], kv[1], bt, cl, float(st["scale"]), c["context_len"], out,
+                          total_context_len=int(st["context_lens"].sum()))
+    ms = timed(d)
+    kvb = kv_bytes(st["context_lens"], Hkv, D, 2)
+    assert kvb == total
+    gbs = kvb / (ms * 1e-3) / 1e9
+    res["decode_call_ms"] = round(ms, 5)
+    res["decode_kv_gbs"] = round(gbs, 1)
+    res["decode_frac_of_sequential"] = round(gbs / res["best_sequential_gbs"], 4)
+    res["decode_frac_of_table_order"] = round(gbs / res["best_table_order_gbs"], 4)
+    res["note"] = ("decode_* = one pa_decode call (decode + merge kernels, launched eagerly) on the same bytes; "
+                   "KV bytes only, the same bytes the probe reads")
+    return res
+
+
 def copy_calibration(args) -> dict:
     """A plain copy of known size through pa_copy_blocks, for scaling HBM
     byte counters: `pairs` whole blocks of K and of V (8 kv heads x 32 slots
@@ -725,9 +798,10 @@ def main():
                     help="separate slot-mapping and reshape_and_cache launches instead of the fused cache write")
     ap.add_argument("--eager", dest="graph", action="store_false",
                     help="launch each call from Python instead of replaying the captured step")
-    ap.add_argument("--mode", choices=["decode", "copy-calibration", "swap"], default="decode",
+    ap.add_argument("--mode", choices=["decode", "copy-calibration", "swap", "read-ceiling"], default="decode",
                     help="copy-calibration: a known-size block copy for scaling HBM byte counters; swap: "
-                         "pa_swap_blocks bandwidth between the device and a pinned host pool")
+                         "pa_swap_blocks bandwidth between the device and a pinned host pool; read-ceiling: "
+                         "plain and table-order reads of the 70B-shaped layer's bytes, and pa_decode beside them")
     ap.add_argument("--swap-blocks", type=int, default=4096, help="blocks per swap call (--mode swap)")
     ap.add_argument("--copy-pairs", type=int, default=4096)
     ap.add_argument("--partition-tokens", type=int, default=0,
@@ -751,6 +825,8 @@ def main():
         res = copy_calibration(args)
     elif args.mode == "swap":
         res = run_swap(args)
+    elif args.mode == "read-ceiling":
+        res = read_ceiling(args)
     elif args.workload in ("int8-token", "fp8", "spec-decode", "chunked-prefill"):
         res = run_next_workload(args)
     elif args.workload != "llama3-70b":

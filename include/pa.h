@@ -370,6 +370,25 @@ pa_status pa_quantize_and_cache(const void* key, const void* value, pa_dtype src
                                 int32_t head_dim, int32_t block_size, int32_t num_blocks, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Diagnostic: read-bandwidth probe (not part of attention)
+ * ------------------------------------------------------------------------
+ * Reads num_chunks chunks of 4096 bytes -- the size of one (block, kv
+ * head) of a bf16 cache with 16-token blocks and head_dim 128 -- with the
+ * 16-byte non-temporal loads the decode kernels use, and nothing else:
+ * chunk c is base + 4096 * c, or base + 4096 * chunk_ids[c] when chunk_ids
+ * (device int32 [num_chunks]) is given (for instance the chunks of a decode
+ * batch in table order, which the block tables scatter over the pool).
+ * num_waves waves of 64 lanes share the chunks; each stores one word per
+ * lane into sink (device, num_waves * 64 uint32, written) so no load is
+ * optimised away.  The caller guarantees every chunk lies inside one
+ * allocation.  Used to measure the memory system's read ceiling for
+ * decode's access pattern; the kernel's time over the bytes read is that
+ * ceiling.
+ */
+pa_status pa_read_probe(const void* base, int64_t num_chunks, const int32_t* chunk_ids, int32_t num_waves,
+                        uint32_t* sink, void* stream);
+
+/* ------------------------------------------------------------------------
  * Block pool (host only)
  * ------------------------------------------------------------------------
  * A stack of free physical block ids with a reference count per block.

@@ -1,10 +1,11 @@
-"""The long-context regression guard (GUARD_BF16 = 2e-5, beside the 2e-3
-parity gate of the GPU tests) catches lost work that the gate alone lets
-through.  Pinned on the CPU with the oracle only: the same attention with
-one 16-token tile, or one whole split-K partition, left out of a
-sequence's table moves the outputs by more than the guard -- at the
-70B-shaped layer's 8,000 tokens and at 131,072 tokens, where the gate alone
-would not notice a dropped tile.
+"""The long-context regression guard (GUARD_BF16 = 2e-5 on the rows of
+sequences of at least GUARD_MIN_LEN = 2,048 tokens, beside the 2e-3 parity
+gate of the GPU tests) catches lost work that the gate alone lets through.
+Pinned on the CPU with the oracle only: the same attention with one
+16-token tile, or one whole split-K partition, left out of a sequence's
+table moves the outputs by more than the guard -- at the 70B-shaped
+layer's 8,000 tokens and at 131,072 tokens, where the gate alone would not
+notice a dropped tile -- and below 2,048 tokens by more than the gate.
 
 Dropping a tile is done through the table: with blocks of 16 tokens a tile
 is one block, so removing one entry from the row (and 16 tokens from the
@@ -15,7 +16,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_helpers import GUARD_BF16, TOL_BF16
+from gpu_helpers import GUARD_BF16, GUARD_MIN_LEN, TOL_BF16
 
 
 def _drop_blocks(case, s, first, count):
@@ -81,3 +82,17 @@ def test_double_counted_tile_breaks_the_guard():
                               float(case.scale))
     d = float(np.max(np.abs(got - full)))
     assert d > 5 * GUARD_BF16, d
+
+
+@pytest.mark.parametrize("n,hq,hkv", [(17, 8, 1), (300, 32, 8), (1000, 8, 1), (2047, 8, 1), (2047, 32, 8)])
+def test_dropped_tile_below_the_guard_length_breaks_the_gate(n, hq, hkv):
+    """Rows the guard leaves out (sequences under GUARD_MIN_LEN tokens, in
+    the GPU tests' head shapes): leaving out any one of their full tiles
+    moves some output of the sequence by more than the 2e-3 gate."""
+    assert n < GUARD_MIN_LEN
+    case = synth.make_case("gate-%d" % n, 11 + n, [n], hq, hkv, 128, 16, free_frac=0.0)
+    full = _full(case, 0)
+    nb = -(-n // 16)
+    for first in range(0, nb - 1, max(1, (nb - 1) // 12)):
+        d = float(np.max(np.abs(_drop_blocks(case, 0, first, 1) - full)))
+        assert d > TOL_BF16, (n, first, d)
