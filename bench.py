@@ -738,12 +738,28 @@ def read_ceiling(args) -> dict:
 
     res = {"mode": "read-ceiling", "bytes_per_launch": total, "chunk_bytes": chunk, "chunks": n,
            "steps": args.steps, "sequential_gbs": {}, "table_order_gbs": {}}
-    for waves in (256, 512, 1024, 2048, 4096, 8192, 16384):
+    waves_sweep = (256, 512, 1024, 2048, 4096, 8192, 16384)
+    for waves in waves_sweep:
         for name, cid in (("sequential_gbs", None), ("table_order_gbs", ids)):
             ms = timed(pa.prepare_read_probe(kv, n, sink, chunk_ids=cid, num_waves=waves))
             res[name][str(waves)] = round(total / (ms * 1e-3) / 1e9, 1)
     res["best_sequential_gbs"] = max(res["sequential_gbs"].values())
     res["best_table_order_gbs"] = max(res["table_order_gbs"].values())
+    # smaller chunks over the same 655 MB (a 1-byte cache's (block, kv head)
+    # is 2 KiB): address order, and a seeded random order of all chunks
+    res["by_chunk_gbs"] = {}
+    rng = np.random.default_rng(17)
+    for cb in (1024, 2048, 4096):
+        nc = total // cb
+        perm = torch.from_numpy(rng.permutation(nc).astype(np.int32)).to(dev)
+        for order, cid in (("sequential", None), ("random", perm)):
+            best = 0.0
+            for waves in waves_sweep:
+                ms = timed(pa.prepare_read_probe(kv, nc, sink, chunk_ids=cid, num_waves=waves, chunk_bytes=cb))
+                gbs = total / (ms * 1e-3) / 1e9
+                res["by_chunk_gbs"]["%d_%s_%d" % (cb, order, waves)] = round(gbs, 1)
+                best = max(best, gbs)
+            res["by_chunk_gbs"]["%d_%s_best" % (cb, order)] = round(best, 1)
     bt = torch.from_numpy(tab).to(dev)
     cl = torch.from_numpy(st["context_lens"]).to(dev)
     out = torch.empty(c["num_seqs"], c["num_q_heads"], D, dtype=torch.float32, device=dev)

@@ -372,11 +372,12 @@ pa_status pa_quantize_and_cache(const void* key, const void* value, pa_dtype src
 /* ------------------------------------------------------------------------
  * Diagnostic: read-bandwidth probe (not part of attention)
  * ------------------------------------------------------------------------
- * Reads num_chunks chunks of 4096 bytes -- the size of one (block, kv
- * head) of a bf16 cache with 16-token blocks and head_dim 128 -- with the
- * 16-byte non-temporal loads the decode kernels use, and nothing else:
- * chunk c is base + 4096 * c, or base + 4096 * chunk_ids[c] when chunk_ids
- * (device int32 [num_chunks]) is given (for instance the chunks of a decode
+ * Reads num_chunks chunks of chunk_bytes (1024, 2048 or 4096) bytes --
+ * 4096 is one (block, kv head) of a bf16 cache with 16-token blocks and
+ * head_dim 128, 2048 the same with 1-byte codes -- with the 16-byte
+ * non-temporal loads the decode kernels use, and nothing else: chunk c is
+ * base + chunk_bytes * c, or base + chunk_bytes * chunk_ids[c] when
+ * chunk_ids (device int32 [num_chunks]) is given (for instance the chunks of a decode
  * batch in table order, which the block tables scatter over the pool).
  * num_waves waves of 64 lanes share the chunks; each stores one word per
  * lane into sink (device, num_waves * 64 uint32, written) so no load is
@@ -385,8 +386,8 @@ pa_status pa_quantize_and_cache(const void* key, const void* value, pa_dtype src
  * decode's access pattern; the kernel's time over the bytes read is that
  * ceiling.
  */
-pa_status pa_read_probe(const void* base, int64_t num_chunks, const int32_t* chunk_ids, int32_t num_waves,
-                        uint32_t* sink, void* stream);
+pa_status pa_read_probe(const void* base, int64_t num_chunks, const int32_t* chunk_ids, int32_t chunk_bytes,
+                        int32_t num_waves, uint32_t* sink, void* stream);
 
 /* ------------------------------------------------------------------------
  * Block pool (host only)

@@ -100,7 +100,7 @@ def library() -> ctypes.CDLL:
     lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.pa_decode.argtypes = [ctypes.POINTER(DecodeArgs)]
     lib.pa_decode.restype = ctypes.c_int
-    lib.pa_read_probe.argtypes = [P, i64, P, i32, P, P]
+    lib.pa_read_probe.argtypes = [P, i64, P, i32, i32, P, P]
     lib.pa_read_probe.restype = ctypes.c_int
     lib.pa_decode_noalloc.argtypes = [ctypes.POINTER(DecodeArgs)]
     lib.pa_decode_noalloc.restype = ctypes.c_int
@@ -358,16 +358,19 @@ def quantize_and_cache(key, value, k_cache, v_cache, k_scales, v_scales, slot_ma
                                v_static_scale, stream=stream)()
 
 
-def prepare_read_probe(base, num_chunks: int, sink, chunk_ids=None, num_waves: int = 4096,
+def prepare_read_probe(base, num_chunks: int, sink, chunk_ids=None, num_waves: int = 4096, chunk_bytes: int = 4096,
                        stream=None) -> "PreparedCall":
-    """``pa_read_probe``: read num_chunks 4 KiB chunks of ``base`` (a device
-    tensor), in address order or in the order of ``chunk_ids`` (device
-    int32); ``sink`` is a device int32 tensor of num_waves * 64 words."""
+    """``pa_read_probe``: read num_chunks chunks of chunk_bytes (1, 2 or 4
+    KiB) of ``base`` (a device tensor), in address order or in the order of
+    ``chunk_ids`` (device int32); ``sink`` is a device int32 tensor of
+    num_waves * 64 words."""
     if sink.numel() < num_waves * 64:
         raise ValueError("sink must hold num_waves * 64 words")
+    if num_chunks * chunk_bytes > base.numel() * base.element_size() and chunk_ids is None:
+        raise ValueError("chunks reach past the tensor")
     ids = None if chunk_ids is None else _ptr(chunk_ids)
-    return PreparedCall("pa_read_probe", (_ptr(base), int(num_chunks), ids, int(num_waves), _ptr(sink),
-                                          _stream(stream)), keep=(base, sink, chunk_ids))
+    return PreparedCall("pa_read_probe", (_ptr(base), int(num_chunks), ids, int(chunk_bytes), int(num_waves),
+                                          _ptr(sink), _stream(stream)), keep=(base, sink, chunk_ids))
 
 
 # --------------------------------------------------------------------------
