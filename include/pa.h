@@ -126,8 +126,9 @@ int32_t pa_abi_version(void);
  * Supported: head_dim in {64, 128}; block_size in {16, 32};
  * q_dtype in {PA_F32, PA_BF16}; kv_dtype in {PA_F32, PA_BF16, PA_I8,
  * PA_FP8_E4M3};
- * out_dtype PA_F32; num_q_heads a multiple of num_kv_heads, at most 16
- * query heads per kv head.  All of q, caches and out 16-byte aligned.
+ * out_dtype PA_F32; num_q_heads a multiple of num_kv_heads (any number of
+ * query heads per kv head: the matrix-core kernel takes them 16 at a time,
+ * two groups of 16 per wave).  All of q, caches and out 16-byte aligned.
  *
  * Long contexts are split into partitions of `partition_tokens` tokens
  * (0 = chosen by the library), each computed by its own wave and merged by
@@ -173,7 +174,9 @@ int32_t pa_abi_version(void);
  * tokens are the blocks shared_prefix_table[0 .. shared_prefix_len/BS - 1]
  * (a common prompt stored once: glossary, section 3, scenario 01; ia-vox,
  * prefix sharing), passing them lets the call read those blocks once for
- * the whole batch instead of once per sequence.  The result is the same
+ * the whole batch instead of once per sequence (with at most 16 query
+ * heads per kv head; more are read through each table row).  The result
+ * is the same
  * attention; a sequence shorter than the prefix sees only its own length
  * of it.  The caller guarantees that every table row starts with these
  * blocks.  With new_key/new_value, a sequence whose newest token lies
@@ -188,8 +191,7 @@ int32_t pa_abi_version(void);
  *
  * `kernel` selects the implementation: 0 = automatic, 1 = vector-ALU
  * kernel (any supported case), 2 = matrix-core kernel (bf16, int8 or E4M3
- * caches with bf16 queries, head_dim 128, 1..16 query heads per kv head;
- * else PA_ERR_UNSUPPORTED).  Both compute the definition above; they
+ * caches with bf16 queries, head_dim 128; else PA_ERR_UNSUPPORTED).  Both compute the definition above; they
  * differ in rounding only.
  */
 typedef struct {

@@ -77,7 +77,6 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
     return fail(PA_ERR_INVALID, "pa_decode: num_q_heads %d is not a multiple of num_kv_heads %d",
                 a->num_q_heads, a->num_kv_heads);
   const int G = a->num_q_heads / a->num_kv_heads;
-  if (G > 16) return fail(PA_ERR_UNSUPPORTED, "pa_decode: %d query heads per kv head (max 16)", G);
   if (a->head_dim != 64 && a->head_dim != 128)
     return fail(PA_ERR_INVALID, "pa_decode: head_dim %d not in {64, 128}", a->head_dim);
   if (a->block_size != 16 && a->block_size != 32)
@@ -143,12 +142,17 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   while (hpw < G && hpw < 8) hpw *= 2;
   p->heads_per_wave = kind == KERNEL_VALU ? hpw : G;
   p->head_groups = kind == KERNEL_VALU ? (G + hpw - 1) / hpw : 1;
-  // columns of the MFMA kernel: G heads x up to max_query_len rows, 16 at a time
-  const int64_t cg = mq ? ((int64_t)G * a->max_query_len + 15) / 16 : 1;
-  if (cg > 4096) return fail(PA_ERR_UNSUPPORTED, "pa_decode: max_query_len %d too large", a->max_query_len);
-  p->cgroups = (int)cg;
-  p->ncg = cg >= 2 ? 2 : 1;
-  p->cg_waves = (int)((cg + p->ncg - 1) / p->ncg);
+  // columns of the MFMA kernel: G heads x up to max_query_len rows (one
+  // row without query_start_loc), 16 at a time; more than 16 query heads
+  // per kv head take several column groups as several rows would
+  const int64_t cg = ((int64_t)G * (mq ? a->max_query_len : 1) + 15) / 16;
+  if (cg > 4096)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: %lld groups of 16 (query row, head) columns per kv head (max 4096)",
+                (long long)cg);
+  // (the vector-ALU kernel takes the heads in head groups instead)
+  p->cgroups = kind == KERNEL_MFMA ? (int)cg : 1;
+  p->ncg = p->cgroups >= 2 ? 2 : 1;
+  p->cg_waves = (p->cgroups + p->ncg - 1) / p->ncg;
   p->rows = (int64_t)(mq ? a->num_queries : (a->num_seqs > 0 ? a->num_seqs : 0)) * a->num_q_heads;
 
   const int64_t max_tiles = (int64_t)kMaxPartitionBlocks * a->block_size / 16;
@@ -203,7 +207,7 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   // waves above the wave target it stays one partition per sequence.
   p->cascade = false;
   p->prefix_partitions = 0;
-  if (a->shared_prefix_len > 0 && kind == KERNEL_MFMA && !mq && a->num_seqs > 0) {
+  if (a->shared_prefix_len > 0 && kind == KERNEL_MFMA && !mq && p->cgroups == 1 && a->num_seqs > 0) {
     // A given partition_tokens sets both passes' partition length.
     p->cascade = true;
     const int64_t pcg = ((int64_t)G * a->num_seqs + 15) / 16;
@@ -239,7 +243,7 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   // peak; on U[200, 2048] (mean / max 0.55) the short partitions of the
   // ragged rule stay ahead by ~1 point.
   p->balanced = false;
-  if (kind == KERNEL_MFMA && !mq && !p->cascade && a->partition_tokens == 0 && a->total_context_len > 0 &&
+  if (kind == KERNEL_MFMA && !mq && p->cgroups == 1 && !p->cascade && a->partition_tokens == 0 && a->total_context_len > 0 &&
       a->num_seqs > 0 && a->num_seqs <= kBalancedMaxSeqs && a->max_context_len > 0 &&
       a->total_context_len * 4 < (int64_t)a->num_seqs * a->max_context_len) {
     const int64_t max_tiles = (a->max_context_len + 15) / 16;

@@ -354,6 +354,7 @@ struct Cascade {
   int nP, P, CG;         // prefix partitions, their length, column groups
   int t0;                // first token of the per-sequence items
   int nPw;               // partial slots per output row (1: write out directly)
+  int write_from;        // fused write: positions below (a shared prefix) are neither stored nor taken from new_k
 };
 
 constexpr int kModeDecode = 0, kModeMultiQuery = 1, kModeCascade = 2, kModeBalanced = 3;
@@ -540,7 +541,9 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
   for (int u = 0; u < NCG; ++u) {
     int h, qrow;
     if constexpr (MQ) {
-      const int q0 = qsl[s], L = qsl[s + 1] - q0;
+      // without row offsets (more than 16 query heads per kv head): one
+      // query row per sequence, row s
+      const int q0 = qsl ? qsl[s] : s, L = qsl ? qsl[s + 1] - q0 : 1;
       const int col = 16 * (cgw * NCG + u) + c, i = col / G;
       // rows outside [0, num_rows) (offsets not matching num_queries, a
       // caller error) are neither read nor written
@@ -621,8 +624,8 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
   // into the cache slot at the end and attends with it in the tile that
   // holds the position (bf16 caches only; the host rejects int8).
   const int tnew = n - 1;
-  const bool owns_new = !I8 && !pre && new_k != nullptr && tnew >= t_begin && tnew < t_end &&
-                        ((tnew >> 4) - (t_begin >> 4)) % WPI == wv;  // wave-uniform
+  const bool owns_new = !I8 && !pre && new_k != nullptr && tnew >= cz.write_from && tnew >= t_begin &&
+                        tnew < t_end && ((tnew >> 4) - (t_begin >> 4)) % WPI == wv;  // wave-uniform
   u32x4_t nk = {0u, 0u, 0u, 0u}, nv = {0u, 0u, 0u, 0u};
   if (owns_new) {
     const size_t src = ((size_t)s * Hkv + g) * ROW + (size_t)c * 16;
@@ -1249,7 +1252,7 @@ static inline SplitK split_k(const pa_decode_args* a, const DecodePlan& p) {
 
 pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipStream_t st) {
   const int ncg = p.ncg, cgw = p.cg_waves;
-  Cascade cz{nullptr, 0, 0, 0, 0, 1, 0, p.ws_partitions};
+  Cascade cz{nullptr, 0, 0, 0, 0, 1, 0, p.ws_partitions, a->shared_prefix_len};
   size_t pre_items = 0;
   if (p.cascade) {
     pre_items = (size_t)a->num_kv_heads * p.prefix_partitions * p.prefix_cgroups;
@@ -1279,7 +1282,7 @@ pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipSt
   do {                                                                               \
     if (p.cascade) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeCascade);                  \
     else if (p.balanced) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeBalanced);           \
-    else if (!a->query_start_loc) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeDecode);    \
+    else if (!a->query_start_loc && p.cgroups == 1) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeDecode); \
     else if (ncg == 2) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 2, kModeMultiQuery);           \
     else PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeMultiQuery);                         \
   } while (0)

@@ -134,7 +134,6 @@ def test_partition_plan_follows_the_length_hint():
     ("struct_size", 8, pa.PA_ERR_INVALID),
     ("num_q_heads", 7, pa.PA_ERR_INVALID),            # not a multiple of 2 kv heads
     ("num_q_heads", 0, pa.PA_ERR_INVALID),
-    ("num_q_heads", 64, pa.PA_ERR_UNSUPPORTED),       # 32 per kv head
     ("head_dim", 256, pa.PA_ERR_INVALID),
     ("block_size", 8, pa.PA_ERR_INVALID),
     ("out_dtype", pa.PA_BF16, pa.PA_ERR_UNSUPPORTED),
@@ -415,3 +414,25 @@ def test_noalloc_refuses_on_the_host_what_its_scratch_cannot_hold():
     b = _cpu_args(head_dim=96)
     assert lib.pa_decode_noalloc(ctypes.byref(b)) == pa.PA_ERR_INVALID
     assert "head_dim 96" in lib.pa_last_error().decode()
+
+
+def test_wide_query_groups_are_planned_as_column_groups():
+    """More than 16 query heads per kv head: the matrix-core plan takes them
+    16 at a time (two groups per wave), as it does query rows; the
+    workspace holds one partial row per query head."""
+    lib = pa.library()
+    al = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    for hq in (34, 64, 256):                           # 17, 32 and 128 per kv head
+        a = _cpu_args(num_q_heads=hq, partition_tokens=64)
+        st, n = _ws(a)
+        assert st == pa.PA_OK, lib.pa_last_error()
+        rows = 3 * hq * 2                              # 3 sequences, 2 partitions of 64 tokens
+        assert n == al(rows * 8) + al(rows * 128 * 4)
+    a = _cpu_args(num_q_heads=64, kernel=pa.KERNEL_VALU, partition_tokens=64)
+    assert _ws(a)[0] == pa.PA_OK
+    # the shared prefix is read through each row; the balanced split is not used
+    big = dict(num_seqs=3, num_q_heads=64, max_blocks_per_seq=2048, max_context_len=32768, num_blocks=6000)
+    st, n = _ws(_cpu_args(total_context_len=20000, **big))
+    assert st == pa.PA_OK
+    st2, n2 = _ws(_cpu_args(total_context_len=20000, shared_prefix_table=0x40000, shared_prefix_len=160, **big))
+    assert st2 == pa.PA_OK and n2 == n
