@@ -154,6 +154,17 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   p->ncg = p->cgroups >= 2 ? 2 : 1;
   p->cg_waves = (p->cgroups + p->ncg - 1) / p->ncg;
   p->rows = (int64_t)(mq ? a->num_queries : (a->num_seqs > 0 ? a->num_seqs : 0)) * a->num_q_heads;
+  // Several query rows with more than one wave of column groups per item
+  // and a bf16 cache: the item's waves share each K/V tile through LDS in
+  // workgroups (else each wave reads every tile itself), one column group
+  // per wave in workgroups of kSharedWaves.  On the 70B-shaped layer with a
+  // 64-row chunk per sequence (32 column groups per item) the per-wave
+  // kernel is bound by those re-reads: 347-349 against 384-389 TFLOP/s.
+  p->shared_tiles = kind == KERNEL_MFMA && mq && a->kv_dtype == PA_BF16 && p->cg_waves >= 2;
+  if (p->shared_tiles) {
+    p->ncg = 1;
+    p->cg_waves = p->cgroups;
+  }
 
   const int64_t max_tiles = (int64_t)kMaxPartitionBlocks * a->block_size / 16;
   const int64_t total = a->total_context_len > 0 ? a->total_context_len : seq_tokens;

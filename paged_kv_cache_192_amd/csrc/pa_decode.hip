@@ -35,6 +35,11 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 8.0f;
 constexpr float kNegInf = -__builtin_huge_valf();
+// A finite starting reference (log2 units), the lowest finite float: any
+// larger finite score exceeds it by more than kRescaleThreshold (8 is below
+// its spacing), so the first one moves the reference, and
+// 2^(-inf - kFloorRef) = 0.
+constexpr float kFloorRef = -3.40282347e38f;
 
 // Streaming loads: every cached byte is read once per step, so they bypass
 // reuse in the caches (non-temporal hint).
@@ -946,6 +951,281 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
 }
 
 // ===========================================================================
+// Several query rows per sequence with many column groups (long prefill
+// chunks): the column-group waves of one (sequence, kv head, partition)
+// share its K/V tiles.  A workgroup of W waves loads each 16-token tile
+// once -- one 16-byte chunk per thread, K in the first 256 threads and V in
+// the next 256 -- into a two-stage LDS ring, and every wave computes its
+// NCG column groups from LDS; one barrier per tile.  Used with one column
+// group per wave and 16 waves (109 VGPRs, 4 waves per SIMD): two per wave
+// in 8-wave workgroups measured 320-370 against 370-373 TFLOP/s on a 64-row
+// chunk, the per-wave kernel 344-349.
+// Each thread keeps the next two tiles' chunks in flight in registers (the
+// loads past the partition re-read its last tile, so every iteration waits
+// for the same number of loads).  bf16 caches, head_dim 128.
+//
+// Without it every column-group wave reads every tile itself (from L2 after
+// the first): a 64-row chunk with 8 query heads per kv head has 32 column
+// groups, 16 waves, and is bound by those re-reads, not by its arithmetic
+// (the same speed with the softmax, half of the P.V products or the score
+// products taken out).
+// ===========================================================================
+template <int BS, int NCG, int W>
+__global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
+    float* __restrict__ out, SplitK ws, const unsigned short* __restrict__ q, const char* __restrict__ k_cache,
+    const char* __restrict__ v_cache, const int32_t* __restrict__ tables, int max_blocks,
+    const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int NB, float qk_log2, int P, int nP,
+    const int32_t* __restrict__ qsl, int CGW, int WGI, int num_rows) {
+  constexpr int D = 128;
+  constexpr int ROW = D * 2;  // bytes per token row
+  constexpr int CPR = ROW / 16;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane >> 4;
+  const int c = lane & 15;
+  // item (sequence s, kv head g, partition p, wave group wgi), kv head fastest
+  const int g = (int)blockIdx.x % Hkv;
+  int rest = (int)blockIdx.x / Hkv;
+  const int wgi = rest % WGI;
+  rest /= WGI;
+  const int p = rest % nP;
+  const int s = rest / nP;
+  const int cgw = wgi * W + wv;
+  // wave-uniform: a wave past the item's last column groups still loads and
+  // takes every barrier
+  const bool active = cgw < CGW;
+  const int32_t* trow = tables + (size_t)s * max_blocks;
+  const int t_begin = p * P;
+  // the partition's table entries (at most 128 blocks), two per lane
+  const int tbl_base = t_begin / BS;
+  const int tbl0 = (tbl_base + lane < max_blocks) ? trow[tbl_base + lane] : -1;
+  const int tbl1 = (tbl_base + 64 + lane < max_blocks) ? trow[tbl_base + 64 + lane] : -1;
+  const int n = min(context_lens[s], max_blocks * BS);
+  const int t_end = min(n, t_begin + P);
+  bool head_ok[NCG];
+  size_t orow[NCG];
+  int lim[NCG];
+  {
+    const int q0 = qsl[s], L = qsl[s + 1] - q0;
+#pragma unroll
+    for (int u = 0; u < NCG; ++u) {
+      const int col = 16 * (cgw * NCG + u) + c, i = col / G;
+      head_ok[u] = active && i < L && q0 + i >= 0 && q0 + i < num_rows;
+      lim[u] = head_ok[u] ? max(0, min(t_end, n - L + i + 1)) : 0;
+      orow[u] = (size_t)(q0 + i) * Hq + g * G + col % G;
+    }
+  }
+  // the lowest visible-token limit over this wave's existing columns: tiles
+  // below it need no token mask
+  int lim_lo = 0x7fffffff;
+#pragma unroll
+  for (int u = 0; u < NCG; ++u) lim_lo = min(lim_lo, head_ok[u] ? lim[u] : 0x7fffffff);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) lim_lo = min(lim_lo, __shfl_xor(lim_lo, d, 64));
+  lim_lo = __builtin_amdgcn_readfirstlane(lim_lo);
+  if (t_begin >= t_end) {
+    // nothing to attend to (the same for every wave of the workgroup)
+#pragma unroll
+    for (int u = 0; u < NCG; ++u) {
+      if (nP == 1 && head_ok[u]) {
+        float4* o = (float4*)(out + orow[u] * D + 32 * j);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = float4{0.f, 0.f, 0.f, 0.f};
+      } else if (nP > 1 && head_ok[u] && j == 0) {
+        ws.ml[orow[u] * nP + p] = float2{kNegInf, 0.f};
+      }
+    }
+    return;
+  }
+  bf16x8_t qf[NCG][4];
+#pragma unroll
+  for (int u = 0; u < NCG; ++u)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4_t w = {0u, 0u, 0u, 0u};
+      if (head_ok[u]) w = *(const u32x4_t*)(q + orow[u] * D + (kk * 4 + j) * 8);
+      qf[u][kk] = as_bf16x8(w);
+    }
+
+  // two stages of one tile: K rows (chunk ch of row r at r * 16 + (ch ^ r),
+  // so the MFMA-layout reads of 16 rows spread over the banks) and V rows
+  // (row-major; each row is read whole by 16 lanes)
+  __shared__ __attribute__((aligned(16))) u32x4_t kv_lds[2][2][16 * CPR];
+  // the first 2 * 16 * CPR threads (whole waves) load
+  static_assert(W * 64 >= 2 * 16 * CPR, "a workgroup loads a tile in one pass");
+  const bool loader = tid < 2 * 16 * CPR;
+  const bool ld_v = tid >= 16 * CPR;
+  const int ld_r = (tid & (16 * CPR - 1)) >> 4, ld_ch = tid & 15;
+  const int ld_slot = ld_r * 16 + (ld_v ? ld_ch : ld_ch ^ ld_r);
+  const char* ld_cache = ld_v ? v_cache : k_cache;
+  const unsigned ld_off = (unsigned)(ld_r * ROW + ld_ch * 16);
+  const size_t head_stride = (size_t)BS * ROW;
+  auto block_of = [&](int ti, bool& ok) {
+    const int e = (ti * 16) / BS - tbl_base;
+    int b = e < 64 ? __builtin_amdgcn_readlane(tbl0, e) : __builtin_amdgcn_readlane(tbl1, e - 64);
+    ok = b >= 0 && b < NB;
+    return ok ? b : 0;
+  };
+  auto load_chunk = [&](int ti) {
+    bool ok;
+    const int b = block_of(ti, ok);
+    const char* tile = ld_cache + ((size_t)b * Hkv + g) * head_stride + (size_t)((ti * 16) % BS) * ROW;
+    return ld16(tile + ld_off);
+  };
+  int kr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kr[i] = c * 16 + ((i * 4 + j) ^ c);
+
+  f32x4_t acc[NCG][8];
+  float m_run[NCG], l_run[NCG];
+#pragma unroll
+  for (int u = 0; u < NCG; ++u) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[u][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // a finite reference below every score: the first finite score moves
+    // it (rescaling zeros), and 2^(-inf - reference) = 0 needs no guard
+    m_run[u] = kFloorRef;
+    l_run[u] = 0.f;
+  }
+
+  // one tile from LDS stage st; tiles every existing column sees whole skip
+  // the token mask
+  auto compute = [&](int st, int ti) {
+    if (!active) return;
+    bool ok;
+    (void)block_of(ti, ok);
+    const bool full = ok && ti * 16 + 15 < lim_lo;  // wave-uniform
+    const u32x4_t* KT = kv_lds[st][0];
+    const u32x4_t* VT = kv_lds[st][1];
+    bf16x8_t ka[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) ka[kk] = as_bf16x8(KT[kr[kk]]);
+    const int tok0 = ti * 16 + 4 * j;
+    i16x4_t Phi[NCG], Plo[NCG];
+#pragma unroll
+    for (int u = 0; u < NCG; ++u) {
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qf[u][kk], sc, 0, 0, 0);
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = sc[r] * qk_log2;
+      if (!full) {  // wave-uniform
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = (ok && tok0 + r < lim[u]) ? x[r] : kNegInf;
+      }
+      const float xloc = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      if (__any(xloc > m_run[u] + kRescaleThreshold)) {
+        const float mloc = xor_max_rows(xloc);
+        const bool need = mloc > m_run[u] + kRescaleThreshold;
+        const float m_new = need ? mloc : m_run[u];
+        const float alpha = need ? fast_exp2(m_run[u] - m_new) : 1.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[u][e] *= alpha;
+        l_run[u] *= alpha;
+        m_run[u] = m_new;
+      }
+      float pw[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pw[r] = fast_exp2(x[r] - m_run[u]);
+      l_run[u] += (pw[0] + pw[1]) + (pw[2] + pw[3]);
+      float lo[4];
+      const unsigned hi01 = pack_bf16x2(pw[0], pw[1]), hi23 = pack_bf16x2(pw[2], pw[3]);
+      lo[0] = pw[0] - bf16_lo(hi01);
+      lo[1] = pw[1] - bf16_hi(hi01);
+      lo[2] = pw[2] - bf16_lo(hi23);
+      lo[3] = pw[3] - bf16_hi(hi23);
+      Phi[u] = as_i16x4(hi01, hi23);
+      Plo[u] = as_i16x4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
+    }
+    // V^T operands from rows 4j .. 4j+3; rows past the partition or of a
+    // block outside the pool are zeroed (they may hold NaN)
+    u32x4_t vr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vr[i] = VT[(4 * j + i) * 16 + c];
+    if (!ok || ti * 16 + 15 >= t_end) {  // wave-uniform
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool keep = ok && tok0 + i < t_end;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) vr[i][w] = keep ? vr[i][w] : 0u;
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const i16x4_t a_even = as_i16x4(__builtin_amdgcn_perm(vr[1][w], vr[0][w], 0x05040100u),
+                                      __builtin_amdgcn_perm(vr[3][w], vr[2][w], 0x05040100u));
+      const i16x4_t a_odd = as_i16x4(__builtin_amdgcn_perm(vr[1][w], vr[0][w], 0x07060302u),
+                                     __builtin_amdgcn_perm(vr[3][w], vr[2][w], 0x07060302u));
+#pragma unroll
+      for (int u = 0; u < NCG; ++u) {
+        f32x4_t* au = acc[u];
+        au[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_even, Phi[u], au[2 * w], 0, 0, 0);
+        au[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_even, Plo[u], au[2 * w], 0, 0, 0);
+        au[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_odd, Phi[u], au[2 * w + 1], 0, 0, 0);
+        au[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_odd, Plo[u], au[2 * w + 1], 0, 0, 0);
+      }
+    }
+  };
+
+  const int tile_begin = t_begin >> 4;
+  const int tile_end = (t_end + 15) >> 4;
+  auto clamp_tile = [&](int ti) { return ti < tile_end ? ti : tile_end - 1; };
+  // stage 0 <- tile_begin; tiles tile_begin + 1, + 2 in flight
+  u32x4_t R0 = {0u, 0u, 0u, 0u}, R1 = {0u, 0u, 0u, 0u};
+  if (loader) {  // wave-uniform
+    R0 = load_chunk(tile_begin);
+    R1 = load_chunk(clamp_tile(tile_begin + 1));
+    kv_lds[0][ld_v][ld_slot] = R0;
+    R0 = load_chunk(clamp_tile(tile_begin + 2));
+  }
+  __syncthreads();
+  for (int ti = tile_begin;;) {
+    compute(0, ti);
+    if (++ti >= tile_end) break;
+    if (loader) {
+      kv_lds[1][ld_v][ld_slot] = R1;  // stage 1 was last read before the previous barrier
+      R1 = load_chunk(clamp_tile(ti + 2));
+    }
+    __syncthreads();
+    compute(1, ti);
+    if (++ti >= tile_end) break;
+    if (loader) {
+      kv_lds[0][ld_v][ld_slot] = R0;
+      R0 = load_chunk(clamp_tile(ti + 2));
+    }
+    __syncthreads();
+  }
+
+  // lane holds d = 32j + 8r + e in acc[u][e][r]
+#pragma unroll
+  for (int u = 0; u < NCG; ++u) {
+    const float l_tot = xor_sum_rows(l_run[u]);
+    const f32x4_t* a = acc[u];
+    if (!head_ok[u]) continue;
+    if (nP == 1) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      float* o = out + orow[u] * D + 32 * j;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        *(float4*)(o + 8 * r) = float4{a[0][r] * inv, a[1][r] * inv, a[2][r] * inv, a[3][r] * inv};
+        *(float4*)(o + 8 * r + 4) = float4{a[4][r] * inv, a[5][r] * inv, a[6][r] * inv, a[7][r] * inv};
+      }
+    } else {
+      const size_t row_id = orow[u] * nP + p;
+      float* o = ws.acc + row_id * D + 32 * j;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        *(float4*)(o + 8 * r) = float4{a[0][r], a[1][r], a[2][r], a[3][r]};
+        *(float4*)(o + 8 * r + 4) = float4{a[4][r], a[5][r], a[6][r], a[7][r]};
+      }
+      if (j == 0) ws.ml[row_id] = float2{m_run[u], l_tot};
+    }
+  }
+}
+
+// ===========================================================================
 // Vector-ALU kernel: any supported dtype, head_dim 64 or 128.
 //
 // Lane l handles token slot tt = l/16 of each group of four tokens and the
@@ -1262,6 +1542,26 @@ pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipSt
     cz.P = p.prefix_tokens;
     cz.CG = p.prefix_cgroups;
     cz.t0 = a->shared_prefix_len;
+  }
+  if (p.shared_tiles) {
+    // workgroups of kSharedWaves waves per (sequence, kv head, partition,
+    // wave group), one column group per wave
+    const int wgi = (cgw + kSharedWaves - 1) / kSharedWaves;
+    const size_t wgs = (size_t)a->num_seqs * a->num_kv_heads * p.num_partitions * wgi;
+    if (wgs > 0x7fffffffu) return fail(PA_ERR_UNSUPPORTED, "pa_decode: grid too large");
+    const SplitK ws = split_k(a, p);
+    const float qk = a->scale * kLog2e;
+#define PA_SHARED_LAUNCH(BS, NCG, W)                                                                            \
+  hipLaunchKernelGGL((shared_tile_mq_kernel<BS, NCG, W>), dim3((unsigned)wgs), dim3(64 * W), 0, st,             \
+                     (float*)a->out, ws, (const unsigned short*)a->q, (const char*)a->k_cache,                  \
+                     (const char*)a->v_cache, a->block_tables, a->max_blocks_per_seq, a->context_lens,          \
+                     a->num_q_heads, a->num_kv_heads, p.G, a->num_blocks, qk, p.partition_tokens,               \
+                     p.num_partitions, a->query_start_loc, cgw, wgi, a->num_queries)
+    if (a->block_size == 16) PA_SHARED_LAUNCH(16, 1, kSharedWaves);
+    else PA_SHARED_LAUNCH(32, 1, kSharedWaves);
+#undef PA_SHARED_LAUNCH
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode (shared-tile kernel) launch");
   }
   const size_t items = p.balanced ? (size_t)a->num_kv_heads * p.balanced_waves
                                   : pre_items + (size_t)a->num_seqs * a->num_kv_heads * p.num_partitions * cgw;

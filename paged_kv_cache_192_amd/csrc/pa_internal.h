@@ -61,6 +61,10 @@ constexpr int kCascadeWaves = 4;
 constexpr int kBalancedMaxSeqs = 256;
 constexpr int kBalancedMaxTiles = 64;
 constexpr int kMaxRaggedPartitions = 512;
+// waves of a workgroup sharing K/V tiles through LDS (several query rows
+// per sequence, bf16 cache, more than one wave of column groups per item),
+// one column group each: registers for 4 waves per SIMD
+constexpr int kSharedWaves = 16;
 
 // Everything the launchers need, derived on the host from pa_decode_args.
 struct DecodePlan {
@@ -73,6 +77,7 @@ struct DecodePlan {
   int cgroups;           // MFMA: groups of 16 (query row, head) columns per (sequence, kv head)
   int ncg;               // MFMA: column groups carried by one wave (1 or 2)
   int cg_waves;          // MFMA: waves per (sequence, kv head, partition) = ceil(cgroups / ncg)
+  bool shared_tiles;     // MFMA, several query rows: the waves of a workgroup share each K/V tile
   int64_t rows;          // output rows: query rows (num_seqs, or num_queries) x num_q_heads
   // shared prefix (cascade): items over the shared blocks for all
   // sequences, split into prefix_partitions partitions of prefix_tokens,
