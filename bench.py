@@ -106,9 +106,9 @@ def cpu_model() -> str:
 # (profiles/decode_mfma_llama3-70b_pmc_traffic.md).  Valid only for the
 # sources the counters were taken on: a changed kernel or plan reports null.
 PMC_TRAFFIC = {
-    "sources_sha256": "d1d29593642f31caa0766fdb1dbed72f499c486fe2fd3d3dcdbb911f9958765b",
-    "fetch_kib": 320921.59375 + 1391.0,
-    "write_kib": 2680.0 + 640.0,
+    "sources_sha256": "b9914255887f259eb6de530aa3fdb8a2ced532951403487ee57379b309a48e1b",
+    "fetch_kib": 320909.0 + 1391.0,
+    "write_kib": 2680.15625 + 640.0,
     "fetch_factor": 1.99227,
     "write_factor": 1.0,
 }
