@@ -139,7 +139,12 @@ int32_t pa_abi_version(void);
  * partitions per sequence; a ragged one into many short ones, so that no
  * wave is left with a long sequence at the end.  The hint shapes only the
  * split (and so the workspace size), never the result; 0 means unknown
- * (every sequence taken at max_context_len).  The merge needs `workspace` of at
+ * (every sequence taken at max_context_len).  With at most 8 partitions,
+ * at least 256 (sequence, kv head) pairs and one group of 16 (query row,
+ * head) columns per pair on the matrix-core kernel, a pair's partitions
+ * run as the waves of one workgroup and are combined there (no merge
+ * kernel, no workspace; the library's own split is then re-cut into 2, 4
+ * or 8 equal partitions).  Otherwise the merge needs `workspace` of at
  * least the size pa_decode_workspace_size reports for the same arguments
  * (NULL is fine when that size is 0).  The workspace is scratch of the
  * call: its contents are not needed before or after it.  Calls that may

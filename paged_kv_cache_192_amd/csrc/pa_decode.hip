@@ -451,8 +451,17 @@ static_assert(kCascadeWaves == 1 || kCascadeWaves == 2 || kCascadeWaves == 4, "1
 // wave carries NCG consecutive column groups over the same K/V tiles (one
 // score MFMA chain, softmax state and accumulator set per group, V^T
 // operands built once), so K/V are read once per NCG groups.
-template <int KV, int BS, bool TOKSC, int NCG, int MODE>
-__global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) void decode_mfma_kernel(
+//
+// Waves per workgroup WG: one, except in the cascade mode (kCascadeWaves
+// waves share each item, taking its tiles in turn) and in groups (decode or
+// several query rows with one column group per item: one workgroup per
+// (sequence, kv head), wave w taking partition w of at most WG; a wave
+// whose partition is empty still joins the combination, with no weight).
+// Either way the workgroup's waves combine (m, l, acc) through LDS and
+// wave 0 goes on with the result, so a grouped launch writes the output
+// rows itself: no partials, no merge.
+template <int KV, int BS, bool TOKSC, int NCG, int MODE, int WG>
+__global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
     float* __restrict__ out, SplitK ws,
     const unsigned short* __restrict__ q, char* __restrict__ k_cache, char* __restrict__ v_cache,
     const float* __restrict__ k_scales, const float* __restrict__ v_scales, const int32_t* __restrict__ tables,
@@ -460,7 +469,13 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
     int P, int nP, const char* __restrict__ new_k, const char* __restrict__ new_v,
     const int32_t* __restrict__ qsl, int CG, int num_rows, Cascade cz, Balanced bz) {
   constexpr bool MQ = MODE == kModeMultiQuery;
-  constexpr int WPI = MODE == kModeCascade ? kCascadeWaves : 1;  // waves per item
+  constexpr bool GROUP = WG > 1 && MODE != kModeCascade;
+  static_assert(MODE == kModeCascade ? WG == kCascadeWaves
+                : MODE == kModeBalanced ? WG == 1
+                                        : (WG == 1 || WG == 2 || WG == 4 || WG == 8) && (WG == 1 || NCG == 1),
+                "waves per workgroup");
+  constexpr int WPI = WG;                                // waves combined per workgroup
+  constexpr int TS = MODE == kModeCascade ? WG : 1;      // tile stride of one wave
   constexpr int D = 128;
   constexpr bool I8 = KV != kKvBf16;  // 1-byte codes with fp32 scales
   constexpr int E = I8 ? 1 : 2;
@@ -515,6 +530,9 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
     mfma_item(blockIdx.x, Hkv, cz.nP, cz.CG, s, g, p, cgw);
   } else if (MODE == kModeCascade) {
     mfma_item(blockIdx.x - cz.items, Hkv, nP, CG, s, g, p, cgw);
+  } else if (GROUP) {
+    mfma_item(blockIdx.x, Hkv, 1, 1, s, g, p, cgw);  // one column group per item
+    p = wv;
   } else {
     mfma_item(blockIdx.x, Hkv, nP, CG, s, g, p, cgw);
   }
@@ -525,7 +543,7 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
   const int t_begin = MODE == kModeBalanced ? piece_t0 : (MODE == kModeCascade && !pre ? cz.t0 : 0) + p * Pw;
   // partial slot of this wave's partition, of nPw per row
   const int slot = MODE == kModeBalanced ? piece_slot : MODE == kModeCascade ? (pre ? p : cz.nP + p) : p;
-  const int nPw = MODE == kModeCascade ? cz.nPw : nP;
+  const int nPw = MODE == kModeCascade ? cz.nPw : GROUP ? 1 : nP;
   // The partition's table entries, two per lane (a partition spans at most
   // 128 blocks, which the host guarantees): entry i of the partition is
   // lane i of tbl0 or lane i - 64 of tbl1.  They are read before the
@@ -536,7 +554,9 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
   const int tbl1 = (tbl_base + 64 + lane < row_blocks) ? trow[tbl_base + 64 + lane] : -1;
   // a length past the table row is a caller error; never read beyond the row
   const int n = pre ? cz.blocks * BS : MODE == kModeBalanced ? n_piece : min(context_lens[s], max_blocks * BS);
-  const int t_end = min(n, MODE == kModeBalanced ? piece_t1 : t_begin + Pw);
+  // (a grouped wave past the plan's nP partitions attends to nothing, as
+  // no wave would in the other modes)
+  const int t_end = GROUP && p >= nP ? t_begin : min(n, MODE == kModeBalanced ? piece_t1 : t_begin + Pw);
   // this lane's column in each group u: output / partial row orow[u],
   // visible tokens < lim[u] (MQ: several rows per sequence, qsl given)
   bool head_ok[NCG];
@@ -587,9 +607,11 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
     lim_lo = __builtin_amdgcn_readfirstlane(lo);
   }
 
-  if (t_begin >= t_end) {
+  if (!GROUP && t_begin >= t_end) {
     // Nothing to attend to.  With one partition the output row is zero;
-    // otherwise the partial is marked empty (no weight) for the merge.
+    // otherwise the partial is marked empty (no weight) for the merge.  (A
+    // grouped wave goes on to the combination, which every wave of the
+    // workgroup must reach, attending to no tile.)
     if (wv != 0) return;
 #pragma unroll
     for (int u = 0; u < NCG; ++u) {
@@ -630,7 +652,7 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
   // holds the position (bf16 caches only; the host rejects int8).
   const int tnew = n - 1;
   const bool owns_new = !I8 && !pre && new_k != nullptr && tnew >= cz.write_from && tnew >= t_begin &&
-                        tnew < t_end && ((tnew >> 4) - (t_begin >> 4)) % WPI == wv;  // wave-uniform
+                        tnew < t_end && (TS == 1 || ((tnew >> 4) - (t_begin >> 4)) % TS == wv);  // wave-uniform
   u32x4_t nk = {0u, 0u, 0u, 0u}, nv = {0u, 0u, 0u, 0u};
   if (owns_new) {
     const size_t src = ((size_t)s * Hkv + g) * ROW + (size_t)c * 16;
@@ -849,24 +871,25 @@ __global__ __launch_bounds__(MODE == kModeCascade ? 64 * kCascadeWaves : 64) voi
     tile_ptrs(ti, kA, vA, okA, ksA, vsA);
     mfma_load_tile<I8>(A, kA, vA, koff, voff);
     while (true) {
-      tile_ptrs(ti + WPI < tend ? ti + WPI : ti, kB, vB, okB, ksB, vsB);
+      tile_ptrs(ti + TS < tend ? ti + TS : ti, kB, vB, okB, ksB, vsB);
       mfma_load_tile<I8>(B, kB, vB, koff, voff);
       if (!FULL || okA) compute(full_tag, A, ti, okA, ksA, vsA);
-      if ((ti += WPI) >= tend) break;
-      tile_ptrs(ti + WPI < tend ? ti + WPI : ti, kA, vA, okA, ksA, vsA);
+      if ((ti += TS) >= tend) break;
+      tile_ptrs(ti + TS < tend ? ti + TS : ti, kA, vA, okA, ksA, vsA);
       mfma_load_tile<I8>(A, kA, vA, koff, voff);
       if (!FULL || okB) compute(full_tag, B, ti, okB, ksB, vsB);
-      if ((ti += WPI) >= tend) break;
+      if ((ti += TS) >= tend) break;
     }
   };
-  // wave wv: tiles tile_begin + wv, + WPI, ...; tiles below full_end are
-  // fully visible.  The split costs the second loop an unoverlapped first
-  // load, so a wave takes it only with at least 16 fully visible tiles.
+  // cascade wave wv: tiles tile_begin + wv, + TS, ...; otherwise every tile
+  // of the wave's partition.  Tiles below full_end are fully visible.  The
+  // split costs the second loop an unoverlapped first load, so a wave takes
+  // it only with at least 16 fully visible tiles.
   const int full_end = min(tile_end, max(lim_lo, 0) >> 4);
-  int ti = tile_begin + wv;
-  if (full_end - ti >= 16 * WPI) {
+  int ti = tile_begin + (TS > 1 ? wv : 0);
+  if (full_end - ti >= 16 * TS) {
     run_tiles(std::true_type{}, ti, full_end);
-    ti += (full_end - ti + WPI - 1) / WPI * WPI;
+    ti += (full_end - ti + TS - 1) / TS * TS;
   }
   run_tiles(std::false_type{}, ti, tile_end);
 
@@ -1563,28 +1586,39 @@ pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipSt
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode (shared-tile kernel) launch");
   }
-  const size_t items = p.balanced ? (size_t)a->num_kv_heads * p.balanced_waves
-                                  : pre_items + (size_t)a->num_seqs * a->num_kv_heads * p.num_partitions * cgw;
+  // workgroups: one wave each, kCascadeWaves per cascade item, or one
+  // group of p.group_waves per (sequence, kv head)
+  const size_t items = p.balanced  ? (size_t)a->num_kv_heads * p.balanced_waves
+                       : p.grouped ? (size_t)a->num_seqs * a->num_kv_heads
+                                   : pre_items + (size_t)a->num_seqs * a->num_kv_heads * p.num_partitions * cgw;
   const Balanced bz{p.balanced_min_tiles, a->max_context_len};
   if (items > 0x7fffffffu) return fail(PA_ERR_UNSUPPORTED, "pa_decode: grid too large");
   cz.items = (int)pre_items;
   const float qk = a->scale * kLog2e;
   const SplitK ws = split_k(a, p);
-#define PA_MFMA_LAUNCH1(KV, BS, TOKSC, NCG, MODE)                                                               \
-  hipLaunchKernelGGL((decode_mfma_kernel<KV, BS, TOKSC, NCG, MODE>), dim3((unsigned)items),                     \
-                     dim3(MODE == kModeCascade ? 64 * kCascadeWaves : 64), 0, st,                               \
+#define PA_MFMA_LAUNCH1(KV, BS, TOKSC, NCG, MODE, WG)                                                           \
+  hipLaunchKernelGGL((decode_mfma_kernel<KV, BS, TOKSC, NCG, MODE, WG>), dim3((unsigned)items), dim3(64 * WG),  \
+                     0, st,                                                                                    \
                      (float*)a->out, ws, (const unsigned short*)a->q, (char*)a->k_cache, (char*)a->v_cache,      \
                      a->k_scales, a->v_scales, a->block_tables, a->max_blocks_per_seq, a->context_lens,        \
                      a->num_q_heads, a->num_kv_heads, p.G, a->num_blocks, qk, p.partition_tokens,              \
                      p.num_partitions, (const char*)a->new_key, (const char*)a->new_value,                     \
                      a->query_start_loc, cgw, a->query_start_loc ? a->num_queries : a->num_seqs, cz, bz)
+#define PA_MFMA_GROUP(KV, BS, TOKSC, MODE)                                           \
+  do {                                                                               \
+    if (p.group_waves == 2) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, MODE, 2);              \
+    else if (p.group_waves == 4) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, MODE, 4);         \
+    else PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, MODE, 8);                                 \
+  } while (0)
 #define PA_MFMA_LAUNCH(KV, BS, TOKSC)                                                \
   do {                                                                               \
-    if (p.cascade) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeCascade);                  \
-    else if (p.balanced) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeBalanced);           \
-    else if (!a->query_start_loc && p.cgroups == 1) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeDecode); \
-    else if (ncg == 2) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 2, kModeMultiQuery);           \
-    else PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeMultiQuery);                         \
+    if (p.cascade) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeCascade, kCascadeWaves);  \
+    else if (p.balanced) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeBalanced, 1);        \
+    else if (p.grouped && !a->query_start_loc) PA_MFMA_GROUP(KV, BS, TOKSC, kModeDecode); \
+    else if (p.grouped) PA_MFMA_GROUP(KV, BS, TOKSC, kModeMultiQuery);                \
+    else if (!a->query_start_loc && p.cgroups == 1) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeDecode, 1); \
+    else if (ncg == 2) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 2, kModeMultiQuery, 1);        \
+    else PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeMultiQuery, 1);                      \
   } while (0)
 #define PA_MFMA_BS(KV, TOKSC)                              \
   if (a->block_size == 16) PA_MFMA_LAUNCH(KV, 16, TOKSC); \
@@ -1603,6 +1637,7 @@ pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipSt
   }
 #undef PA_MFMA_BS
 #undef PA_MFMA_LAUNCH
+#undef PA_MFMA_GROUP
 #undef PA_MFMA_LAUNCH1
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode (matrix-core kernel) launch");

@@ -61,6 +61,12 @@ constexpr int kCascadeWaves = 4;
 constexpr int kBalancedMaxSeqs = 256;
 constexpr int kBalancedMaxTiles = 64;
 constexpr int kMaxRaggedPartitions = 512;
+// Most partitions one workgroup takes in a grouped launch (one wave each,
+// combined through LDS: 2, 4 or 8 waves)
+constexpr int kMaxGroupWaves = 8;
+// ... and only with at least this many (sequence, kv head) items: one
+// workgroup per compute unit of the chip
+constexpr int64_t kGroupMinItems = 256;
 // waves of a workgroup sharing K/V tiles through LDS (several query rows
 // per sequence, bf16 cache, more than one wave of column groups per item),
 // one column group each: registers for 4 waves per SIMD
@@ -91,6 +97,12 @@ struct DecodePlan {
   // balanced_waves per head; ws_partitions partial slots per row
   bool balanced;
   int balanced_waves, balanced_min_tiles;
+  // groups (MFMA, one column group per item, 2 .. kMaxGroupWaves
+  // partitions, no cascade or balanced split): one workgroup of group_waves
+  // waves per (sequence, kv head), wave w on partition w, combined through
+  // LDS; no partials (ws_partitions = 1)
+  bool grouped;
+  int group_waves;
   size_t workspace_bytes;
 };
 

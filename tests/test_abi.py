@@ -57,16 +57,27 @@ def _ws(a):
 
 
 def test_struct_layout_and_workspace_size():
-    a = _cpu_args()
+    a = _cpu_args(kernel=pa.KERNEL_VALU)
     st, n = _ws(a)
     assert st == pa.PA_OK, pa.library().pa_last_error()
     # 3 seqs x 2 kv heads, 7 tiles: the planner splits the 100 tokens into
-    # partitions of 64 (4 tiles minimum) -> 2 partitions; workspace = the
-    # partial (m, l) rows, then the acc rows, 256-aligned
+    # partitions of 64 (4 tiles minimum) -> 2 partitions; on the vector-ALU
+    # kernel the workspace is the partial (m, l) rows, then the acc rows,
+    # 256-aligned
     nP = -(-100 // 64)
     rows = 3 * 8 * nP
     al = lambda b: (b + 255) // 256 * 256  # noqa: E731
     assert n == al(rows * 8) + al(rows * 128 * 4)
+    # the matrix-core kernel takes 2 .. 8 partitions of a (sequence, kv
+    # head) in one workgroup and combines them there: no workspace, with the
+    # automatic split or a given one (100 tokens in 16-token partitions: 7)
+    for over in ({}, {"kernel": pa.KERNEL_MFMA}, {"partition_tokens": 16}, {"partition_tokens": 32}):
+        st, n = _ws(_cpu_args(**over))
+        assert st == pa.PA_OK and n == 0, over
+    # more than 8 partitions: partials again (10 blocks x 16 = 160 tokens in
+    # 16-token partitions: 10)
+    st, n = _ws(_cpu_args(partition_tokens=16, max_context_len=160))
+    assert st == pa.PA_OK and n == al(3 * 8 * 10 * 8) + al(3 * 8 * 10 * 128 * 4)
     # one partition: no workspace
     st, n = _ws(_cpu_args(partition_tokens=128))
     assert st == pa.PA_OK and n == 0
@@ -168,7 +179,7 @@ def test_decode_rejects_null_alignment_and_workspace_before_launch():
     a = _cpu_args(q=0x1008)                            # 8-byte aligned only
     assert lib.pa_decode(ctypes.byref(a)) == pa.PA_ERR_INVALID
     assert "aligned" in lib.pa_last_error().decode()
-    a = _cpu_args(workspace=None, workspace_bytes=0)   # 2 partitions need one
+    a = _cpu_args(workspace=None, workspace_bytes=0, kernel=pa.KERNEL_VALU)   # 2 partitions need one
     assert lib.pa_decode(ctypes.byref(a)) == pa.PA_ERR_INVALID
     assert "workspace" in lib.pa_last_error().decode()
     a = _cpu_args(kernel=2, q_dtype=pa.PA_F32)
@@ -188,10 +199,14 @@ def test_multi_query_argument_checks():
     assert lib.pa_decode(ctypes.byref(a)) == pa.PA_ERR_UNSUPPORTED
     a = _cpu_args(query_start_loc=qsl, num_queries=5, max_query_len=2, new_key=0x20000, new_value=0x30000)
     assert lib.pa_decode(ctypes.byref(a)) == pa.PA_ERR_UNSUPPORTED
-    # workspace rows are query rows: 5 rows x 8 heads x 2 partitions of 64 tokens
-    st, n = _ws(_cpu_args(query_start_loc=qsl, num_queries=5, max_query_len=3, partition_tokens=64))
+    # workspace rows are query rows: 5 rows x 8 heads x 2 partitions of 64
+    # tokens, with 5 rows x 4 heads per kv head = 2 column groups per item
+    st, n = _ws(_cpu_args(query_start_loc=qsl, num_queries=5, max_query_len=5, partition_tokens=64))
     al = lambda b: (b + 255) // 256 * 256  # noqa: E731
     assert st == pa.PA_OK and n == al(5 * 8 * 2 * 8) + al(5 * 8 * 2 * 128 * 4)
+    # one column group per item (up to 4 rows of 4 heads): grouped, no workspace
+    st, n = _ws(_cpu_args(query_start_loc=qsl, num_queries=5, max_query_len=4, partition_tokens=64))
+    assert st == pa.PA_OK and n == 0
 
 
 def test_shared_prefix_argument_checks_and_plan():
