@@ -68,16 +68,22 @@ def test_struct_layout_and_workspace_size():
     rows = 3 * 8 * nP
     al = lambda b: (b + 255) // 256 * 256  # noqa: E731
     assert n == al(rows * 8) + al(rows * 128 * 4)
-    # the matrix-core kernel takes 2 .. 8 partitions of a (sequence, kv
-    # head) in one workgroup and combines them there: no workspace, with the
-    # automatic split or a given one (100 tokens in 16-token partitions: 7)
+    # with at least 256 (sequence, kv head) items the matrix-core kernel
+    # takes 2 .. 8 partitions of an item in one workgroup and combines them
+    # there: no workspace, with the automatic split or a given one (100
+    # tokens in 16-token partitions: 7); 128 sequences x 2 kv heads
     for over in ({}, {"kernel": pa.KERNEL_MFMA}, {"partition_tokens": 16}, {"partition_tokens": 32}):
-        st, n = _ws(_cpu_args(**over))
+        st, n = _ws(_cpu_args(num_seqs=128, **over))
         assert st == pa.PA_OK and n == 0, over
+    # fewer items (the 3 x 2 above, or 127 x 2): partials and the merge
+    st, n = _ws(_cpu_args())
+    assert st == pa.PA_OK and n == al(rows * 8) + al(rows * 128 * 4)
+    st, n = _ws(_cpu_args(num_seqs=127))
+    assert st == pa.PA_OK and n == al(127 * 8 * 2 * 8) + al(127 * 8 * 2 * 128 * 4)
     # more than 8 partitions: partials again (10 blocks x 16 = 160 tokens in
     # 16-token partitions: 10)
-    st, n = _ws(_cpu_args(partition_tokens=16, max_context_len=160))
-    assert st == pa.PA_OK and n == al(3 * 8 * 10 * 8) + al(3 * 8 * 10 * 128 * 4)
+    st, n = _ws(_cpu_args(num_seqs=128, partition_tokens=16, max_context_len=160))
+    assert st == pa.PA_OK and n == al(128 * 8 * 10 * 8) + al(128 * 8 * 10 * 128 * 4)
     # one partition: no workspace
     st, n = _ws(_cpu_args(partition_tokens=128))
     assert st == pa.PA_OK and n == 0
@@ -204,8 +210,9 @@ def test_multi_query_argument_checks():
     st, n = _ws(_cpu_args(query_start_loc=qsl, num_queries=5, max_query_len=5, partition_tokens=64))
     al = lambda b: (b + 255) // 256 * 256  # noqa: E731
     assert st == pa.PA_OK and n == al(5 * 8 * 2 * 8) + al(5 * 8 * 2 * 128 * 4)
-    # one column group per item (up to 4 rows of 4 heads): grouped, no workspace
-    st, n = _ws(_cpu_args(query_start_loc=qsl, num_queries=5, max_query_len=4, partition_tokens=64))
+    # one column group per item (up to 4 rows of 4 heads) and 128 x 2
+    # items: grouped, no workspace
+    st, n = _ws(_cpu_args(query_start_loc=qsl, num_seqs=128, num_queries=5, max_query_len=4, partition_tokens=64))
     assert st == pa.PA_OK and n == 0
 
 
