@@ -54,6 +54,17 @@ __device__ __forceinline__ float i8_at(unsigned w, int k) { return (float)(int)(
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Settle a loaded value before a loop: an empty asm statement that takes the
+// register as input and output emits nothing, but the compiler waits for
+// the load once, here, and inside the loop the value is no longer a load in
+// flight.  (Otherwise its wait analysis, merging the states around the loop,
+// keeps re-waiting with vmcnt(0) -- for every load, the next tiles'
+// prefetches included -- before each use in every iteration.)
+template <typename T>
+__device__ __forceinline__ void settle(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
 // Sum over the 16 lanes of a DPP row; every lane of the row gets the total.
 __device__ __forceinline__ float row_sum16(float x) {
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));  // row_ror:8
@@ -320,9 +331,12 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t w) { return __builtin_bit_
 __device__ __forceinline__ i16x4_t as_i16x4(unsigned a, unsigned b) {
   return __builtin_bit_cast(i16x4_t, u32x2_t{a, b});
 }
+// two floats to bf16 (round to nearest even), lo in the low half: one
+// v_cvt_pk_bf16_f32 (two scalar conversions would take four instructions)
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-  return (unsigned)__builtin_bit_cast(unsigned short, (__bf16)lo) |
-         ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)hi) << 16);
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // Work item of a wave: (sequence s, kv head g, partition p[, column group
@@ -1022,8 +1036,8 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
   const int t_begin = p * P;
   // the partition's table entries (at most 128 blocks), two per lane
   const int tbl_base = t_begin / BS;
-  const int tbl0 = (tbl_base + lane < max_blocks) ? trow[tbl_base + lane] : -1;
-  const int tbl1 = (tbl_base + 64 + lane < max_blocks) ? trow[tbl_base + 64 + lane] : -1;
+  const int tbl0_ld = (tbl_base + lane < max_blocks) ? trow[tbl_base + lane] : -1;
+  const int tbl1_ld = (tbl_base + 64 + lane < max_blocks) ? trow[tbl_base + 64 + lane] : -1;
   const int n = min(context_lens[s], max_blocks * BS);
   const int t_end = min(n, t_begin + P);
   bool head_ok[NCG];
@@ -1068,19 +1082,27 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
     for (int kk = 0; kk < 4; ++kk) {
       u32x4_t w = {0u, 0u, 0u, 0u};
       if (head_ok[u]) w = *(const u32x4_t*)(q + orow[u] * D + (kk * 4 + j) * 8);
+      settle(w);
       qf[u][kk] = as_bf16x8(w);
     }
+  int tbl0 = tbl0_ld, tbl1 = tbl1_ld;
+  settle(tbl0);
+  settle(tbl1);
 
   // two stages of one tile: K rows (chunk ch of row r at r * 16 + (ch ^ r),
-  // so the MFMA-layout reads of 16 rows spread over the banks) and V rows
-  // (row-major; each row is read whole by 16 lanes)
+  // so the MFMA-layout reads of 16 rows spread over the banks) and V^T as
+  // the P.V operands: entry w * 64 + l holds, for lane l = 16 j + c of any
+  // wave, the 16 bytes {a_even, a_odd} of d-pair w of chunk c over tokens
+  // 4j .. 4j+3 (read by a wave as 1 KiB in lane order: no bank conflicts)
   __shared__ __attribute__((aligned(16))) u32x4_t kv_lds[2][2][16 * CPR];
   // the first 2 * 16 * CPR threads (whole waves) load
   static_assert(W * 64 >= 2 * 16 * CPR, "a workgroup loads a tile in one pass");
   const bool loader = tid < 2 * 16 * CPR;
-  const bool ld_v = tid >= 16 * CPR;
+  const bool ld_v = tid >= 16 * CPR;  // wave-uniform
   const int ld_r = (tid & (16 * CPR - 1)) >> 4, ld_ch = tid & 15;
-  const int ld_slot = ld_r * 16 + (ld_v ? ld_ch : ld_ch ^ ld_r);
+  // a V loader's 16 bytes after the transpose: d-pair w = ld_r & 3 (its
+  // lane's row within the group of four) of chunk ld_ch, tokens 4 (ld_r >> 2) ..
+  const int ld_slot = ld_v ? (ld_r & 3) * 64 + (ld_r >> 2) * 16 + ld_ch : ld_r * 16 + (ld_ch ^ ld_r);
   const char* ld_cache = ld_v ? v_cache : k_cache;
   const unsigned ld_off = (unsigned)(ld_r * ROW + ld_ch * 16);
   const size_t head_stride = (size_t)BS * ROW;
@@ -1095,6 +1117,39 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
     const int b = block_of(ti, ok);
     const char* tile = ld_cache + ((size_t)b * Hkv + g) * head_stride + (size_t)((ti * 16) % BS) * ROW;
     return ld16(tile + ld_off);
+  };
+  // Store tile ti's chunk R into stage st.  A V loader first zeroes rows past
+  // the partition or of a block outside the pool (they may hold NaN, which
+  // a zero weight would not cancel in the MFMA), then transposes with the
+  // other three rows of its 4-row group -- lanes l, l^16, l^32, l^48 hold
+  // rows 4j .. 4j+3 of the same chunk, word w = the bf16 pair (d 2w, 2w+1)
+  // of the lane's row: after a permlane32 swap on bit 1 of the row index and
+  // a permlane16 swap on bit 0, the lane of row i holds word i of all four
+  // rows -- and packs the even and odd d of the four tokens as the A
+  // operands of the P.V products.
+  auto store_chunk = [&](int st, int ti, u32x4_t R) {
+    if (ld_v) {  // wave-uniform
+      bool ok;
+      (void)block_of(ti, ok);
+      const bool keep = ok && ti * 16 + ld_r < t_end;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) R[w] = keep ? R[w] : 0u;
+#pragma unroll
+      for (int w0 = 0; w0 < 2; ++w0) {
+        const u32x2_t a = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane32_swap(R[w0], R[2 + w0], false, false));
+        R[w0] = a[0];
+        R[2 + w0] = a[1];
+      }
+#pragma unroll
+      for (int a1 = 0; a1 < 2; ++a1) {
+        const u32x2_t b = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane16_swap(R[2 * a1], R[2 * a1 + 1], false, false));
+        R[2 * a1] = b[0];
+        R[2 * a1 + 1] = b[1];
+      }
+      R = u32x4_t{__builtin_amdgcn_perm(R[1], R[0], 0x05040100u), __builtin_amdgcn_perm(R[3], R[2], 0x05040100u),
+                  __builtin_amdgcn_perm(R[1], R[0], 0x07060302u), __builtin_amdgcn_perm(R[3], R[2], 0x07060302u)};
+    }
+    kv_lds[st][ld_v][ld_slot] = R;
   };
   int kr[4];
 #pragma unroll
@@ -1162,25 +1217,12 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
       Phi[u] = as_i16x4(hi01, hi23);
       Plo[u] = as_i16x4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
     }
-    // V^T operands from rows 4j .. 4j+3; rows past the partition or of a
-    // block outside the pool are zeroed (they may hold NaN)
-    u32x4_t vr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vr[i] = VT[(4 * j + i) * 16 + c];
-    if (!ok || ti * 16 + 15 >= t_end) {  // wave-uniform
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool keep = ok && tok0 + i < t_end;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) vr[i][w] = keep ? vr[i][w] : 0u;
-      }
-    }
+    // V^T operands as stored by the loaders (masked rows already zero)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const i16x4_t a_even = as_i16x4(__builtin_amdgcn_perm(vr[1][w], vr[0][w], 0x05040100u),
-                                      __builtin_amdgcn_perm(vr[3][w], vr[2][w], 0x05040100u));
-      const i16x4_t a_odd = as_i16x4(__builtin_amdgcn_perm(vr[1][w], vr[0][w], 0x07060302u),
-                                     __builtin_amdgcn_perm(vr[3][w], vr[2][w], 0x07060302u));
+      const u32x4_t vt = VT[w * 64 + lane];
+      const i16x4_t a_even = as_i16x4(vt[0], vt[1]);
+      const i16x4_t a_odd = as_i16x4(vt[2], vt[3]);
 #pragma unroll
       for (int u = 0; u < NCG; ++u) {
         f32x4_t* au = acc[u];
@@ -1200,7 +1242,7 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
   if (loader) {  // wave-uniform
     R0 = load_chunk(tile_begin);
     R1 = load_chunk(clamp_tile(tile_begin + 1));
-    kv_lds[0][ld_v][ld_slot] = R0;
+    store_chunk(0, tile_begin, R0);
     R0 = load_chunk(clamp_tile(tile_begin + 2));
   }
   __syncthreads();
@@ -1208,14 +1250,14 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
     compute(0, ti);
     if (++ti >= tile_end) break;
     if (loader) {
-      kv_lds[1][ld_v][ld_slot] = R1;  // stage 1 was last read before the previous barrier
+      store_chunk(1, ti, R1);  // stage 1 was last read before the previous barrier
       R1 = load_chunk(clamp_tile(ti + 2));
     }
     __syncthreads();
     compute(1, ti);
     if (++ti >= tile_end) break;
     if (loader) {
-      kv_lds[0][ld_v][ld_slot] = R0;
+      store_chunk(0, ti, R0);
       R0 = load_chunk(clamp_tile(ti + 2));
     }
     __syncthreads();
