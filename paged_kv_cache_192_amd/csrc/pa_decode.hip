@@ -1089,18 +1089,21 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
   settle(tbl0);
   settle(tbl1);
 
-  // two stages of one tile: K rows (chunk ch of row r at r * 16 + (ch ^ r),
-  // so the MFMA-layout reads of 16 rows spread over the banks) and V^T as
-  // the P.V operands: entry w * 64 + l holds, for lane l = 16 j + c of any
-  // wave, the 16 bytes {a_even, a_odd} of d-pair w of chunk c over tokens
-  // 4j .. 4j+3 (read by a wave as 1 KiB in lane order: no bank conflicts)
-  __shared__ __attribute__((aligned(16))) u32x4_t kv_lds[2][2][16 * CPR];
-  // the first 2 * 16 * CPR threads (whole waves) load
+  // Two LDS stages of two tiles (A = the stage's first, B = its second).
+  // K: per tile, chunk ch of row r at r * 16 + (ch ^ r), so the
+  // MFMA-layout reads of 16 rows spread over the banks.  V: the A operands
+  // of the P.V products for both tiles at once, kv_v[stage][parity][w * 64 + l]
+  // = for lane l = 16 j + c of any wave, the bf16 of d = 8c + 2w + parity
+  // at tokens 4j .. 4j+3 of tile A, then of tile B (read by a wave as 1 KiB
+  // in lane order: no bank conflicts).
+  __shared__ __attribute__((aligned(16))) u32x4_t kv_k[2][2][16 * CPR];
+  __shared__ __attribute__((aligned(16))) u32x4_t kv_v[2][2][16 * CPR];
+  // the first 2 * 16 * CPR threads (whole waves) load: K chunks, then V
   static_assert(W * 64 >= 2 * 16 * CPR, "a workgroup loads a tile in one pass");
   const bool loader = tid < 2 * 16 * CPR;
   const bool ld_v = tid >= 16 * CPR;  // wave-uniform
   const int ld_r = (tid & (16 * CPR - 1)) >> 4, ld_ch = tid & 15;
-  // a V loader's 16 bytes after the transpose: d-pair w = ld_r & 3 (its
+  // a V loader's entries after the transpose: d-pair w = ld_r & 3 (its
   // lane's row within the group of four) of chunk ld_ch, tokens 4 (ld_r >> 2) ..
   const int ld_slot = ld_v ? (ld_r & 3) * 64 + (ld_r >> 2) * 16 + ld_ch : ld_r * 16 + (ld_ch ^ ld_r);
   const char* ld_cache = ld_v ? v_cache : k_cache;
@@ -1118,38 +1121,46 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
     const char* tile = ld_cache + ((size_t)b * Hkv + g) * head_stride + (size_t)((ti * 16) % BS) * ROW;
     return ld16(tile + ld_off);
   };
-  // Store tile ti's chunk R into stage st.  A V loader first zeroes rows past
-  // the partition or of a block outside the pool (they may hold NaN, which
-  // a zero weight would not cancel in the MFMA), then transposes with the
-  // other three rows of its 4-row group -- lanes l, l^16, l^32, l^48 hold
-  // rows 4j .. 4j+3 of the same chunk, word w = the bf16 pair (d 2w, 2w+1)
-  // of the lane's row: after a permlane32 swap on bit 1 of the row index and
-  // a permlane16 swap on bit 0, the lane of row i holds word i of all four
-  // rows -- and packs the even and odd d of the four tokens as the A
-  // operands of the P.V products.
-  auto store_chunk = [&](int st, int ti, u32x4_t R) {
-    if (ld_v) {  // wave-uniform
-      bool ok;
-      (void)block_of(ti, ok);
-      const bool keep = ok && ti * 16 + ld_r < t_end;
+  // A V loader's chunk R of tile ti -> its {even d, odd d} operand halves.
+  // Rows past the partition or of a block outside the pool are zeroed
+  // first (they may hold NaN, which a zero weight would not cancel in the
+  // MFMA).  Then the chunk is transposed with the other three rows of its
+  // 4-row group -- lanes l, l^16, l^32, l^48 hold rows 4j .. 4j+3 of the
+  // same chunk, word w = the bf16 pair (d 2w, 2w+1) of the lane's row:
+  // after a permlane32 swap on bit 1 of the row index and a permlane16 swap
+  // on bit 0, the lane of row i holds word i of all four rows -- and the
+  // even and odd d of the four tokens are packed.
+  auto v_operands = [&](int ti, u32x4_t R) {
+    bool ok;
+    (void)block_of(min(ti, (t_end - 1) >> 4), ok);  // a tile past the partition: all rows masked
+    const bool keep = ok && ti * 16 + ld_r < t_end;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) R[w] = keep ? R[w] : 0u;
+    for (int w = 0; w < 4; ++w) R[w] = keep ? R[w] : 0u;
 #pragma unroll
-      for (int w0 = 0; w0 < 2; ++w0) {
-        const u32x2_t a = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane32_swap(R[w0], R[2 + w0], false, false));
-        R[w0] = a[0];
-        R[2 + w0] = a[1];
-      }
-#pragma unroll
-      for (int a1 = 0; a1 < 2; ++a1) {
-        const u32x2_t b = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane16_swap(R[2 * a1], R[2 * a1 + 1], false, false));
-        R[2 * a1] = b[0];
-        R[2 * a1 + 1] = b[1];
-      }
-      R = u32x4_t{__builtin_amdgcn_perm(R[1], R[0], 0x05040100u), __builtin_amdgcn_perm(R[3], R[2], 0x05040100u),
-                  __builtin_amdgcn_perm(R[1], R[0], 0x07060302u), __builtin_amdgcn_perm(R[3], R[2], 0x07060302u)};
+    for (int w0 = 0; w0 < 2; ++w0) {
+      const u32x2_t a = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane32_swap(R[w0], R[2 + w0], false, false));
+      R[w0] = a[0];
+      R[2 + w0] = a[1];
     }
-    kv_lds[st][ld_v][ld_slot] = R;
+#pragma unroll
+    for (int a1 = 0; a1 < 2; ++a1) {
+      const u32x2_t b = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane16_swap(R[2 * a1], R[2 * a1 + 1], false, false));
+      R[2 * a1] = b[0];
+      R[2 * a1 + 1] = b[1];
+    }
+    return u32x4_t{__builtin_amdgcn_perm(R[1], R[0], 0x05040100u), __builtin_amdgcn_perm(R[3], R[2], 0x05040100u),
+                   __builtin_amdgcn_perm(R[1], R[0], 0x07060302u), __builtin_amdgcn_perm(R[3], R[2], 0x07060302u)};
+  };
+  // store tiles ti (RA) and ti + 1 (RB) into stage st
+  auto store_stage = [&](int st, int ti, u32x4_t RA, u32x4_t RB) {
+    if (ld_v) {  // wave-uniform
+      const u32x4_t a = v_operands(ti, RA), b = v_operands(ti + 1, RB);
+      kv_v[st][0][ld_slot] = u32x4_t{a[0], a[1], b[0], b[1]};
+      kv_v[st][1][ld_slot] = u32x4_t{a[2], a[3], b[2], b[3]};
+    } else {
+      kv_k[st][0][ld_slot] = RA;
+      kv_k[st][1][ld_slot] = RB;
+    }
   };
   int kr[4];
 #pragma unroll
@@ -1167,33 +1178,50 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
     l_run[u] = 0.f;
   }
 
-  // one tile from LDS stage st; tiles every existing column sees whole skip
-  // the token mask
+  // Tiles ti and ti + 1 from stage st (a second tile past the partition is
+  // all masked, its V rows zero): both score chains, one rescale check,
+  // both weight sets, then the P.V products with 32-deep MFMAs whose K index
+  // 8j + e is token 4j + e of tile A for e < 4 and token 4j + e - 4 of tile
+  // B for e >= 4 -- so each lane's B operand is its own four weights of
+  // each tile, P split into bf16 hi and lo parts in two products.  Tiles
+  // every existing column sees whole skip the token mask.
   auto compute = [&](int st, int ti) {
     if (!active) return;
-    bool ok;
-    (void)block_of(ti, ok);
-    const bool full = ok && ti * 16 + 15 < lim_lo;  // wave-uniform
-    const u32x4_t* KT = kv_lds[st][0];
-    const u32x4_t* VT = kv_lds[st][1];
-    bf16x8_t ka[4];
+    bool okA, okB;
+    (void)block_of(ti, okA);
+    (void)block_of(min(ti + 1, (t_end - 1) >> 4), okB);
+    const bool full = okA && okB && ti * 16 + 31 < lim_lo;  // wave-uniform
+    bf16x8_t ka[4], kb[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) ka[kk] = as_bf16x8(KT[kr[kk]]);
+    for (int kk = 0; kk < 4; ++kk) {
+      ka[kk] = as_bf16x8(kv_k[st][0][kr[kk]]);
+      kb[kk] = as_bf16x8(kv_k[st][1][kr[kk]]);
+    }
     const int tok0 = ti * 16 + 4 * j;
-    i16x4_t Phi[NCG], Plo[NCG];
+    bf16x8_t Phi[NCG], Plo[NCG];
 #pragma unroll
     for (int u = 0; u < NCG; ++u) {
-      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+      f32x4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qf[u][kk], sc, 0, 0, 0);
-      float x[4];
+      for (int kk = 0; kk < 4; ++kk) {
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qf[u][kk], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qf[u][kk], sb, 0, 0, 0);
+      }
+      float x[8];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = sc[r] * qk_log2;
+      for (int r = 0; r < 4; ++r) {
+        x[r] = sa[r] * qk_log2;
+        x[4 + r] = sb[r] * qk_log2;
+      }
       if (!full) {  // wave-uniform
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = (ok && tok0 + r < lim[u]) ? x[r] : kNegInf;
+        for (int r = 0; r < 4; ++r) {
+          x[r] = (okA && tok0 + r < lim[u]) ? x[r] : kNegInf;
+          x[4 + r] = (okB && tok0 + 16 + r < lim[u]) ? x[4 + r] : kNegInf;
+        }
       }
-      const float xloc = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      const float xloc = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                               fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
       if (__any(xloc > m_run[u] + kRescaleThreshold)) {
         const float mloc = xor_max_rows(xloc);
         const bool need = mloc > m_run[u] + kRescaleThreshold;
@@ -1204,32 +1232,30 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
         l_run[u] *= alpha;
         m_run[u] = m_new;
       }
-      float pw[4];
+      float pw[8];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pw[r] = fast_exp2(x[r] - m_run[u]);
-      l_run[u] += (pw[0] + pw[1]) + (pw[2] + pw[3]);
-      float lo[4];
-      const unsigned hi01 = pack_bf16x2(pw[0], pw[1]), hi23 = pack_bf16x2(pw[2], pw[3]);
-      lo[0] = pw[0] - bf16_lo(hi01);
-      lo[1] = pw[1] - bf16_hi(hi01);
-      lo[2] = pw[2] - bf16_lo(hi23);
-      lo[3] = pw[3] - bf16_hi(hi23);
-      Phi[u] = as_i16x4(hi01, hi23);
-      Plo[u] = as_i16x4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
+      for (int r = 0; r < 8; ++r) pw[r] = fast_exp2(x[r] - m_run[u]);
+      l_run[u] += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
+      unsigned hi[4], lo[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        hi[k] = pack_bf16x2(pw[2 * k], pw[2 * k + 1]);
+        lo[k] = pack_bf16x2(pw[2 * k] - bf16_lo(hi[k]), pw[2 * k + 1] - bf16_hi(hi[k]));
+      }
+      Phi[u] = as_bf16x8(u32x4_t{hi[0], hi[1], hi[2], hi[3]});
+      Plo[u] = as_bf16x8(u32x4_t{lo[0], lo[1], lo[2], lo[3]});
     }
-    // V^T operands as stored by the loaders (masked rows already zero)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const u32x4_t vt = VT[w * 64 + lane];
-      const i16x4_t a_even = as_i16x4(vt[0], vt[1]);
-      const i16x4_t a_odd = as_i16x4(vt[2], vt[3]);
+      const bf16x8_t ve = as_bf16x8(kv_v[st][0][w * 64 + lane]);
+      const bf16x8_t vo = as_bf16x8(kv_v[st][1][w * 64 + lane]);
 #pragma unroll
       for (int u = 0; u < NCG; ++u) {
         f32x4_t* au = acc[u];
-        au[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_even, Phi[u], au[2 * w], 0, 0, 0);
-        au[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_even, Plo[u], au[2 * w], 0, 0, 0);
-        au[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_odd, Phi[u], au[2 * w + 1], 0, 0, 0);
-        au[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_odd, Plo[u], au[2 * w + 1], 0, 0, 0);
+        au[2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ve, Phi[u], au[2 * w], 0, 0, 0);
+        au[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vo, Phi[u], au[2 * w + 1], 0, 0, 0);
+        au[2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ve, Plo[u], au[2 * w], 0, 0, 0);
+        au[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vo, Plo[u], au[2 * w + 1], 0, 0, 0);
       }
     }
   };
@@ -1237,28 +1263,35 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
   const int tile_begin = t_begin >> 4;
   const int tile_end = (t_end + 15) >> 4;
   auto clamp_tile = [&](int ti) { return ti < tile_end ? ti : tile_end - 1; };
-  // stage 0 <- tile_begin; tiles tile_begin + 1, + 2 in flight
-  u32x4_t R0 = {0u, 0u, 0u, 0u}, R1 = {0u, 0u, 0u, 0u};
+  // Stage 0 <- tiles tile_begin, + 1; the next stage's two tiles in flight
+  // while a stage is computed.  A loader stores a stage right before it
+  // loads the next one, so the wait for its chunks (which the compiler
+  // makes a wait for every load in flight) never holds back a newer load:
+  // each load has a whole stage, two tiles of compute, to arrive.
+  u32x4_t RA = {0u, 0u, 0u, 0u}, RB = {0u, 0u, 0u, 0u};
   if (loader) {  // wave-uniform
-    R0 = load_chunk(tile_begin);
-    R1 = load_chunk(clamp_tile(tile_begin + 1));
-    store_chunk(0, tile_begin, R0);
-    R0 = load_chunk(clamp_tile(tile_begin + 2));
+    RA = load_chunk(tile_begin);
+    RB = load_chunk(clamp_tile(tile_begin + 1));
+    store_stage(0, tile_begin, RA, RB);
+    RA = load_chunk(clamp_tile(tile_begin + 2));
+    RB = load_chunk(clamp_tile(tile_begin + 3));
   }
   __syncthreads();
   for (int ti = tile_begin;;) {
     compute(0, ti);
-    if (++ti >= tile_end) break;
+    if ((ti += 2) >= tile_end) break;
     if (loader) {
-      store_chunk(1, ti, R1);  // stage 1 was last read before the previous barrier
-      R1 = load_chunk(clamp_tile(ti + 2));
+      store_stage(1, ti, RA, RB);  // stage 1 was last read before the previous barrier
+      RA = load_chunk(clamp_tile(ti + 2));
+      RB = load_chunk(clamp_tile(ti + 3));
     }
     __syncthreads();
     compute(1, ti);
-    if (++ti >= tile_end) break;
+    if ((ti += 2) >= tile_end) break;
     if (loader) {
-      store_chunk(0, ti, R0);
-      R0 = load_chunk(clamp_tile(ti + 2));
+      store_stage(0, ti, RA, RB);
+      RA = load_chunk(clamp_tile(ti + 2));
+      RB = load_chunk(clamp_tile(ti + 3));
     }
     __syncthreads();
   }
