@@ -1100,8 +1100,11 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
   __shared__ __attribute__((aligned(16))) u32x4_t kv_v[2][2][16 * CPR];
   // the first 2 * 16 * CPR threads (whole waves) load: K chunks, then V
   static_assert(W * 64 >= 2 * 16 * CPR, "a workgroup loads a tile in one pass");
-  const bool loader = tid < 2 * 16 * CPR;
-  const bool ld_v = tid >= 16 * CPR;  // wave-uniform
+  // (taken from the wave's first lane: the compiler then keeps the cache
+  // base and the tile addresses in scalar registers)
+  const int wave_tid0 = __builtin_amdgcn_readfirstlane(tid);
+  const bool loader = wave_tid0 < 2 * 16 * CPR;
+  const bool ld_v = wave_tid0 >= 16 * CPR;
   const int ld_r = (tid & (16 * CPR - 1)) >> 4, ld_ch = tid & 15;
   // a V loader's entries after the transpose: d-pair w = ld_r & 3 (its
   // lane's row within the group of four) of chunk ld_ch, tokens 4 (ld_r >> 2) ..
@@ -1119,7 +1122,7 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
     bool ok;
     const int b = block_of(ti, ok);
     const char* tile = ld_cache + ((size_t)b * Hkv + g) * head_stride + (size_t)((ti * 16) % BS) * ROW;
-    return ld16(tile + ld_off);
+    return bld16(tile_rsrc(tile, 16 * ROW), ld_off);  // uniform tile base, per-lane offset
   };
   // A V loader's chunk R of tile ti -> its {even d, odd d} operand halves.
   // Rows past the partition or of a block outside the pool are zeroed
@@ -1133,9 +1136,11 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
   auto v_operands = [&](int ti, u32x4_t R) {
     bool ok;
     (void)block_of(min(ti, (t_end - 1) >> 4), ok);  // a tile past the partition: all rows masked
-    const bool keep = ok && ti * 16 + ld_r < t_end;
+    if (!ok || ti * 16 + 16 > t_end) {  // wave-uniform
+      const bool keep = ok && ti * 16 + ld_r < t_end;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) R[w] = keep ? R[w] : 0u;
+      for (int w = 0; w < 4; ++w) R[w] = keep ? R[w] : 0u;
+    }
 #pragma unroll
     for (int w0 = 0; w0 < 2; ++w0) {
       const u32x2_t a = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane32_swap(R[w0], R[2 + w0], false, false));
