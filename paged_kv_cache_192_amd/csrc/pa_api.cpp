@@ -39,6 +39,9 @@ static bool valid_scale_mode(int m) { return m == PA_SCALE_BLOCK || m == PA_SCAL
 // partitions) measured 61-65 % of peak against 52-58 % at 5 per CU and
 // 38-49 % at 2.5.  The vector-ALU kernel keeps one tile in flight; five
 // waves per CU.
+// SIMDs of the chip (256 compute units of 4)
+constexpr int64_t kSimds = 1024;
+
 static int target_waves(KernelKind kind, pa_dtype kv) {
   if (kind == KERNEL_MFMA) return quantised(kv) ? 2560 : 640;
   return 1280;
@@ -196,7 +199,12 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
     // per partition and at most kMaxAutoPartitions partitions.
     const int64_t groups = (seqs > 0 ? seqs : 1) * per_seq * wpi;
     const int64_t tw = (tgt ? tgt : target) * wave_mult;
-    int64_t nP = (tw + groups / 2) / groups;
+    // A wave carrying two column groups computes about twice as long per
+    // tile, and two such waves on one SIMD slow each other: at most one
+    // per SIMD.  The 70B-shaped layer with 4 query rows per sequence (160
+    // items) read 70.6-71.5 % of HBM peak with 6 partitions (960 waves),
+    // 65.7-66.8 % with 8 (1,280), 64 % with 7 and 67 % with 5.
+    int64_t nP = (wave_mult == 2 && !tgt) ? kSimds / groups : (tw + groups / 2) / groups;
     if (nP < 1) nP = 1;
     if (nP > kMaxAutoPartitions) nP = kMaxAutoPartitions;
     if (nP > (tiles + 4 * wpi - 1) / (4 * wpi)) nP = (tiles + 4 * wpi - 1) / (4 * wpi);

@@ -852,17 +852,38 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       // word w holds d = 8c + 2w (low half) and 8c + 2w + 1 (high half)
-      const i16x4_t a_even = as_i16x4(__builtin_amdgcn_perm(vw[1][w], vw[0][w], 0x05040100u),
-                                      __builtin_amdgcn_perm(vw[3][w], vw[2][w], 0x05040100u));
-      const i16x4_t a_odd = as_i16x4(__builtin_amdgcn_perm(vw[1][w], vw[0][w], 0x07060302u),
-                                     __builtin_amdgcn_perm(vw[3][w], vw[2][w], 0x07060302u));
+      const unsigned e01 = __builtin_amdgcn_perm(vw[1][w], vw[0][w], 0x05040100u);
+      const unsigned e23 = __builtin_amdgcn_perm(vw[3][w], vw[2][w], 0x05040100u);
+      const unsigned o01 = __builtin_amdgcn_perm(vw[1][w], vw[0][w], 0x07060302u);
+      const unsigned o23 = __builtin_amdgcn_perm(vw[3][w], vw[2][w], 0x07060302u);
+      if constexpr (NCG == 2) {
+        // One 32-deep product per (parity, group) instead of two 16-deep
+        // ones (which take as long each): K index 8j + e is token 4j + e of
+        // the hi weights for e < 4 and of the lo weights for e >= 4, so the
+        // V^T operand is this lane's four tokens twice and the weight
+        // operand its hi then lo parts.  (The copies cost 16 moves a tile:
+        // worth it with two column groups, not with one.)
+        const bf16x8_t ae = as_bf16x8(u32x4_t{e01, e23, e01, e23});
+        const bf16x8_t ao = as_bf16x8(u32x4_t{o01, o23, o01, o23});
 #pragma unroll
-      for (int u = 0; u < NCG; ++u) {
-        f32x4_t* au = acc[u];
-        au[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_even, Phi[u], au[2 * w], 0, 0, 0);
-        au[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_even, Plo[u], au[2 * w], 0, 0, 0);
-        au[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_odd, Phi[u], au[2 * w + 1], 0, 0, 0);
-        au[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_odd, Plo[u], au[2 * w + 1], 0, 0, 0);
+        for (int u = 0; u < NCG; ++u) {
+          const bf16x8_t pb = as_bf16x8(u32x4_t{__builtin_bit_cast(u32x2_t, Phi[u])[0], __builtin_bit_cast(u32x2_t, Phi[u])[1],
+                                                __builtin_bit_cast(u32x2_t, Plo[u])[0], __builtin_bit_cast(u32x2_t, Plo[u])[1]});
+          f32x4_t* au = acc[u];
+          au[2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ae, pb, au[2 * w], 0, 0, 0);
+          au[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, pb, au[2 * w + 1], 0, 0, 0);
+        }
+      } else {
+        const i16x4_t a_even = as_i16x4(e01, e23);
+        const i16x4_t a_odd = as_i16x4(o01, o23);
+#pragma unroll
+        for (int u = 0; u < NCG; ++u) {
+          f32x4_t* au = acc[u];
+          au[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_even, Phi[u], au[2 * w], 0, 0, 0);
+          au[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_even, Plo[u], au[2 * w], 0, 0, 0);
+          au[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_odd, Phi[u], au[2 * w + 1], 0, 0, 0);
+          au[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_odd, Plo[u], au[2 * w + 1], 0, 0, 0);
+        }
       }
     }
   };
