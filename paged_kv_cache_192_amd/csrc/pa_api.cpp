@@ -263,7 +263,7 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   // ragged rule stay ahead by ~1 point.
   p->balanced = false;
   if (kind == KERNEL_MFMA && !mq && p->cgroups == 1 && !p->cascade && a->partition_tokens == 0 && a->total_context_len > 0 &&
-      a->num_seqs > 0 && a->num_seqs <= kBalancedMaxSeqs && a->max_context_len > 0 &&
+      a->num_seqs > 0 && a->num_seqs <= kBalancedWideMaxSeqs && a->max_context_len > 0 &&
       a->total_context_len * 4 < (int64_t)a->num_seqs * a->max_context_len) {
     const int64_t max_tiles = (a->max_context_len + 15) / 16;
     // tiles per head from the hint (an upper bound on the true count), and

@@ -376,7 +376,7 @@ struct Cascade {
   int write_from;        // fused write: positions below (a shared prefix) are neither stored nor taken from new_k
 };
 
-constexpr int kModeDecode = 0, kModeMultiQuery = 1, kModeCascade = 2, kModeBalanced = 3;
+constexpr int kModeDecode = 0, kModeMultiQuery = 1, kModeCascade = 2, kModeBalanced = 3, kModeBalancedWide = 4;
 
 // Balanced split of a ragged decode batch.  A kv head's work is the
 // sequence of 16-token tiles of all sequences in order; it is cut into V
@@ -384,14 +384,17 @@ constexpr int kModeDecode = 0, kModeMultiQuery = 1, kModeCascade = 2, kModeBalan
 // loop over their ranges).  A range that crosses sequence boundaries is
 // processed as pieces, one per sequence, each leaving a partial in slot
 // v - (first range of that sequence).  Every wave reads all lengths once
-// (sequence 64*ch + lane in chunk ch) and scans the tile counts; tile
-// index a -> its sequence by a ballot over the inclusive sums.
+// (sequence 64*ch + lane in chunk ch of CH) and scans the tile counts; tile
+// index a -> its sequence by a ballot over the inclusive sums.  CH = 4
+// chunks (256 sequences) in the balanced mode, 16 (1,024) in the wide one.
 constexpr int kBalancedChunks = kBalancedMaxSeqs / 64;
+constexpr int kBalancedWideChunks = kBalancedWideMaxSeqs / 64;
+template <int CH>
 struct TileMap {
-  int incl[kBalancedChunks];  // inclusive prefix sums of the tile counts
-  int len[kBalancedChunks];   // the sequences' lengths (capped at the table row)
-  int last[kBalancedChunks];  // incl of each chunk's last lane (wave-uniform)
-  int total;                  // tiles of all sequences
+  int incl[CH];  // inclusive prefix sums of the tile counts
+  int len[CH];   // the sequences' lengths (capped at the table row)
+  int last[CH];  // incl of each chunk's last lane (wave-uniform)
+  int total;     // tiles of all sequences
 };
 
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
@@ -406,17 +409,18 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 // tiles attended of a sequence of n tokens: those of its first min(n, cap)
 __device__ __forceinline__ int tile_count(int n, int cap) { return n > 0 ? (min(n, cap) + 15) >> 4 : 0; }
 
-__device__ __forceinline__ void tile_map_init(TileMap& m, const int32_t* __restrict__ context_lens, int S,
+template <int CH>
+__device__ __forceinline__ void tile_map_init(TileMap<CH>& m, const int32_t* __restrict__ context_lens, int S,
                                               int row_cap, int cap, int lane) {
-  int n[kBalancedChunks];
+  int n[CH];
 #pragma unroll
-  for (int ch = 0; ch < kBalancedChunks; ++ch) {
+  for (int ch = 0; ch < CH; ++ch) {
     const int si = 64 * ch + lane;
     n[ch] = si < S ? max(0, min(context_lens[si], row_cap)) : 0;
   }
   int run = 0;
 #pragma unroll
-  for (int ch = 0; ch < kBalancedChunks; ++ch) {
+  for (int ch = 0; ch < CH; ++ch) {
     const int x = wave_incl_scan(tile_count(n[ch], cap), lane) + run;
     m.incl[ch] = x;
     m.len[ch] = n[ch];
@@ -429,13 +433,14 @@ __device__ __forceinline__ void tile_map_init(TileMap& m, const int32_t* __restr
 // tile index a < m.total -> sequence s, its length n, tile count c and the
 // tiles before it (the chunk found by counting, its values by selects: no
 // indexing of the register arrays)
-__device__ __forceinline__ void tile_find(const TileMap& m, int a, int cap, int& s, int& n, int& c, int& excl) {
+template <int CH>
+__device__ __forceinline__ void tile_find(const TileMap<CH>& m, int a, int cap, int& s, int& n, int& c, int& excl) {
   int ch = 0;
 #pragma unroll
-  for (int k = 0; k + 1 < kBalancedChunks; ++k) ch += m.last[k] <= a ? 1 : 0;
+  for (int k = 0; k + 1 < CH; ++k) ch += m.last[k] <= a ? 1 : 0;
   int incl = m.incl[0], len = m.len[0];
 #pragma unroll
-  for (int k = 1; k < kBalancedChunks; ++k) {
+  for (int k = 1; k < CH; ++k) {
     incl = ch == k ? m.incl[k] : incl;
     len = ch == k ? m.len[k] : len;
   }
@@ -484,8 +489,10 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
     const int32_t* __restrict__ qsl, int CG, int num_rows, Cascade cz, Balanced bz) {
   constexpr bool MQ = MODE == kModeMultiQuery;
   constexpr bool GROUP = WG > 1 && MODE != kModeCascade;
+  constexpr bool BAL = MODE == kModeBalanced || MODE == kModeBalancedWide;
+  constexpr int CH = MODE == kModeBalancedWide ? kBalancedWideChunks : kBalancedChunks;
   static_assert(MODE == kModeCascade ? WG == kCascadeWaves
-                : MODE == kModeBalanced ? WG == 1
+                : BAL ? WG == 1
                                         : (WG == 1 || WG == 2 || WG == 4 || WG == 8) && (WG == 1 || NCG == 1),
                 "waves per workgroup");
   constexpr int WPI = WG;                                // waves combined per workgroup
@@ -502,9 +509,9 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
   // wave-uniform: prefix item of a cascade launch
   const bool pre = MODE == kModeCascade && (int)blockIdx.x < cz.items;
   // balanced split: this wave's ranges v = blockIdx.x / Hkv + k * Wh of pw tiles
-  TileMap tm;
+  TileMap<CH> tm;
   int pw = 1, V = 0, Wh = 1, v = 0, ra = 0, rb = 0;
-  if constexpr (MODE == kModeBalanced) {
+  if constexpr (BAL) {
     tile_map_init(tm, context_lens, num_rows, max_blocks * BS, bz.cap, lane);
     Wh = gridDim.x / Hkv;
     pw = min(max((tm.total + Wh - 1) / Wh, bz.min_tiles), kBalancedMaxTiles);
@@ -513,7 +520,7 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
     if (blockIdx.x == 0) {
       // partials of each sequence: the ranges its tiles meet
 #pragma unroll
-      for (int ch = 0; ch < kBalancedChunks; ++ch) {
+      for (int ch = 0; ch < CH; ++ch) {
         const int si = 64 * ch + lane;
         const int c = tile_count(tm.len[ch], bz.cap), in = tm.incl[ch];
         if (si < num_rows) ws.counts[si] = c > 0 ? (in - 1) / pw - (in - c) / pw + 1 : 0;
@@ -523,7 +530,7 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
   // one item per wave, except in a balanced split (a loop over pieces)
   for (;;) {
   int s, g, p, cgw, n_piece = 0, piece_t0 = 0, piece_t1 = 0, piece_slot = 0;
-  if constexpr (MODE == kModeBalanced) {
+  if constexpr (BAL) {
     if (ra >= rb) {
       v += Wh;
       if (v >= V) return;
@@ -554,9 +561,9 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
   const int32_t* trow = pre ? cz.table : tables + (size_t)s * max_blocks;
   const int row_blocks = pre ? cz.blocks : max_blocks;
   const int Pw = pre ? cz.P : P;
-  const int t_begin = MODE == kModeBalanced ? piece_t0 : (MODE == kModeCascade && !pre ? cz.t0 : 0) + p * Pw;
+  const int t_begin = BAL ? piece_t0 : (MODE == kModeCascade && !pre ? cz.t0 : 0) + p * Pw;
   // partial slot of this wave's partition, of nPw per row
-  const int slot = MODE == kModeBalanced ? piece_slot : MODE == kModeCascade ? (pre ? p : cz.nP + p) : p;
+  const int slot = BAL ? piece_slot : MODE == kModeCascade ? (pre ? p : cz.nP + p) : p;
   const int nPw = MODE == kModeCascade ? cz.nPw : GROUP ? 1 : nP;
   // The partition's table entries, two per lane (a partition spans at most
   // 128 blocks, which the host guarantees): entry i of the partition is
@@ -567,10 +574,10 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
   const int tbl0 = (tbl_base + lane < row_blocks) ? trow[tbl_base + lane] : -1;
   const int tbl1 = (tbl_base + 64 + lane < row_blocks) ? trow[tbl_base + 64 + lane] : -1;
   // a length past the table row is a caller error; never read beyond the row
-  const int n = pre ? cz.blocks * BS : MODE == kModeBalanced ? n_piece : min(context_lens[s], max_blocks * BS);
+  const int n = pre ? cz.blocks * BS : BAL ? n_piece : min(context_lens[s], max_blocks * BS);
   // (a grouped wave past the plan's nP partitions attends to nothing, as
   // no wave would in the other modes)
-  const int t_end = GROUP && p >= nP ? t_begin : min(n, MODE == kModeBalanced ? piece_t1 : t_begin + Pw);
+  const int t_end = GROUP && p >= nP ? t_begin : min(n, BAL ? piece_t1 : t_begin + Pw);
   // this lane's column in each group u: output / partial row orow[u],
   // visible tokens < lim[u] (MQ: several rows per sequence, qsl given)
   bool head_ok[NCG];
@@ -637,7 +644,7 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
         ws.ml[orow[u] * nPw + slot] = float2{kNegInf, 0.f};
       }
     }
-    if constexpr (MODE == kModeBalanced) continue;
+    if constexpr (BAL) continue;
     else return;
   }
 
@@ -1004,7 +1011,7 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
       if (j == 0) ws.ml[row_id] = float2{m_run[u], l_tot};
     }
   }
-  if constexpr (MODE != kModeBalanced) return;
+  if constexpr (!BAL) return;
   }  // piece loop
 }
 
@@ -1714,6 +1721,7 @@ pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipSt
 #define PA_MFMA_LAUNCH(KV, BS, TOKSC)                                                \
   do {                                                                               \
     if (p.cascade) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeCascade, kCascadeWaves);  \
+    else if (p.balanced && a->num_seqs > kBalancedMaxSeqs) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeBalancedWide, 1); \
     else if (p.balanced) PA_MFMA_LAUNCH1(KV, BS, TOKSC, 1, kModeBalanced, 1);        \
     else if (p.grouped && !a->query_start_loc) PA_MFMA_GROUP(KV, BS, TOKSC, kModeDecode); \
     else if (p.grouped) PA_MFMA_GROUP(KV, BS, TOKSC, kModeMultiQuery);                \

@@ -57,8 +57,10 @@ constexpr int kMaxAutoPartitions = 32;
 // waves per work item of the shared-prefix (cascade) decode
 constexpr int kCascadeWaves = 4;
 // balanced split of a ragged batch: at most this many sequences (the
-// lengths sit in four 64-lane chunks of registers) and tiles per wave range
+// lengths sit in four 64-lane chunks of registers; sixteen chunks, up to
+// kBalancedWideMaxSeqs, in the wide form) and tiles per wave range
 constexpr int kBalancedMaxSeqs = 256;
+constexpr int kBalancedWideMaxSeqs = 1024;
 constexpr int kBalancedMaxTiles = 64;
 constexpr int kMaxRaggedPartitions = 512;
 // Most partitions one workgroup takes in a grouped launch (one wave each,

@@ -147,6 +147,29 @@ def test_partition_plan_follows_the_length_hint():
     assert st == pa.PA_OK and n == ws_for(16)
 
 
+def test_balanced_split_up_to_1024_sequences():
+    """A strongly skewed batch (mean an eighth of the 32,768-token maximum)
+    takes the balanced split up to 1,024 sequences (lengths in sixteen
+    64-lane register chunks past 256): 2 kv heads, t = 4,194,304 / 16 +
+    1,024 = 263,168 tiles per head by the hint, max(320, ceil(t / 64)) = 4,112
+    waves per head of 64-tile ranges, so a 2,048-tile sequence meets at most
+    33 ranges: 33 partial slots per row and the per-sequence counts.  1,025
+    sequences fall back to the ragged rule's partitions (no counts)."""
+    al = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    big = dict(max_blocks_per_seq=2048, num_blocks=6144, max_context_len=32768)
+
+    def balanced_ws(S, slots):
+        rows = S * 8 * slots
+        return al(rows * 8) + al(rows * 128 * 4) + al(S * 4)
+
+    st, n = _ws(_cpu_args(num_seqs=1024, total_context_len=1024 * 32768 // 8, **big))
+    assert st == pa.PA_OK and n == balanced_ws(1024, 33)
+    st, n = _ws(_cpu_args(num_seqs=1025, total_context_len=1025 * 32768 // 8, **big))
+    # the ragged rule's partitions, here the 128-block cap: 16 per row, no counts
+    rows = 1025 * 8 * 16
+    assert st == pa.PA_OK and n == al(rows * 8) + al(rows * 128 * 4)
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("struct_size", 8, pa.PA_ERR_INVALID),
     ("num_q_heads", 7, pa.PA_ERR_INVALID),            # not a multiple of 2 kv heads

@@ -1,7 +1,8 @@
 """Ragged decode batches (log-normal lengths, a few empty sequences, one
 long one) under the plans the length hint selects -- the balanced split
-(each kv head's tiles cut into equal ranges over the sequences, up to 256
-sequences), short partitions, long ones: the result must not depend on the
+(each kv head's tiles cut into equal ranges over the sequences, up to 1,024
+sequences: four register chunks of lengths up to 256, sixteen past that),
+short partitions, long ones: the result must not depend on the
 hint's value, which only shapes the split.  Checked
 against the CPU oracle, max |gpu - oracle| <= 2e-3 (bf16, int8 or E4M3
 inputs), and the rows of sequences of 2,048 tokens or more within the
@@ -37,10 +38,10 @@ def _decode(case, dev, total, P=0, new=None):
     return out.cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("S", [7, 64, 200, 256, 257])
+@pytest.mark.parametrize("S", [7, 64, 200, 256, 257, 640, 1024, 1025])
 def test_ragged_grid_any_hint(S):
-    """The exact total (the balanced split; short partitions past 256
-    sequences), a quarter of it (a hint below the truth: longer ranges than
+    """The exact total (the balanced split, wide past 256 sequences; short
+    partitions past 1,024), a quarter of it (a hint below the truth: longer ranges than
     the hint suggests) and the near-uniform bound (long partitions)."""
     lens = _lognormal(S, S, 300)
     lens[0] = max(int(lens.max()), 1500)             # one long sequence: most of its partitions' peers empty
@@ -80,9 +81,9 @@ def test_ragged_grid_block32_and_fused_write():
     assert gerr <= GUARD_BF16, gerr
 
 
-@pytest.mark.parametrize("kv,mode", [(synth.I8, pa.PA_SCALE_BLOCK), (synth.FP8, pa.PA_SCALE_TOKEN)])
-def test_ragged_grid_quantised(kv, mode):
-    S = 96
+@pytest.mark.parametrize("kv,mode,S", [(synth.I8, pa.PA_SCALE_BLOCK, 96), (synth.FP8, pa.PA_SCALE_TOKEN, 96),
+                                       (synth.I8, pa.PA_SCALE_BLOCK, 700), (synth.I8, pa.PA_SCALE_TOKEN, 700)])
+def test_ragged_grid_quantised(kv, mode, S):
     lens = _lognormal(7, S, 400)
     lens[1] = 4000
     case = synth.make_case("ragged_q", 71, lens, 32, 8, 128, 16, kv_dtype=kv, free_frac=0.05)
@@ -91,7 +92,7 @@ def test_ragged_grid_quantised(kv, mode):
                                  float(case.scale), case.k_scales, case.v_scales, scale_mode=mode)
     dev = case_on_device(case)
     for hint in (int(lens.sum()), int(lens.sum()) // 3):
-        say("ragged grid quantised", kv, mode, "hint", hint)
+        say("ragged grid quantised", kv, mode, "S", S, "hint", hint)
         got = _decode(case, dev, hint)
         err, gerr = max_err(got, expect), guard_err(got, expect, lens)
         say("max |gpu - oracle| = %.3e, on long rows %.3e" % (err, gerr))
