@@ -54,8 +54,11 @@ static int target_waves(KernelKind kind, pa_dtype kv) {
 // lengths (int8 and bf16 caches): ~5,000 waves of <= 16 tiles beat both
 // fewer longer waves and more shorter ones.
 constexpr int64_t kRaggedWaves = 5120;
-// Waves of a balanced split (one launch, all kv heads).
-static int64_t balanced_waves(int32_t kv_dtype) { return kv_dtype == PA_BF16 ? 640 : 2560; }
+// Waves of a balanced split (one launch, all kv heads).  For 1-byte codes
+// 1,920 read 0.7-2 points more than 2,560 on the int8, per-token int8 and
+// E4M3 layers (64 log-normal sequences; int8 54.8-55.6 % of HBM peak against
+// 54.0-54.9 %), and more than 1,280 and 2,240; 3,072 was within noise of it.
+static int64_t balanced_waves(int32_t kv_dtype) { return kv_dtype == PA_BF16 ? 640 : 1920; }
 
 // Waves for the items over a shared prefix.  Measured on the prefix-sharing
 // layer (50 sequences, 1,984 shared tokens, 32/8 heads): 2 partitions of
