@@ -246,15 +246,17 @@ __global__ __launch_bounds__(64 * W) void decode_merge_kernel(float* __restrict_
 //    head l%16 and the 32 contiguous d = 32*(l/16) .. +31.
 // ===========================================================================
 
-template <bool I8>
+template <bool R8>
 struct MfmaTile {
   // K, coalesced and staged through LDS into the MFMA layout:
-  //    bf16 -> 4 x 16 B per lane: instruction i reads rows 4i .. 4i+3, lane
-  //    l the 16 B chunk l%16 of row 4i + l/16;
-  //    int8 -> 2 x 16 B per lane: instruction i reads rows 8i .. 8i+7, lane
-  //    l the 16 B chunk l%8 of row 8i + l/8.
-  u32x4_t k[I8 ? 2 : 4];
-  // V: rows 4*(l/16) + i, d = 8*(l%16) .. +7: bf16 -> 16 B per row, int8 -> 8 B.
+  //    256-byte rows (bf16, head_dim 128) -> 4 x 16 B per lane: instruction
+  //    i reads rows 4i .. 4i+3, lane l the 16 B chunk l%16 of row 4i + l/16;
+  //    128-byte rows (R8: 1-byte codes at head_dim 128, bf16 at 64) -> 2 x
+  //    16 B per lane: instruction i reads rows 8i .. 8i+7, lane l the 16 B
+  //    chunk l%8 of row 8i + l/8.
+  u32x4_t k[R8 ? 2 : 4];
+  // V: rows 4*(l/16) + i, the lane's sixteenth of the row (element run
+  // l%16): 16 B of a 256-byte row, 8 B of a 128-byte one (upper half zero).
   u32x4_t v[4];
 };
 
@@ -276,12 +278,12 @@ __device__ __forceinline__ u32x2_t bld8(__amdgpu_buffer_rsrc_t r, unsigned off) 
   return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2 /* nt */));
 }
 
-template <bool I8>
-__device__ __forceinline__ void mfma_load_tile(MfmaTile<I8>& T, const char* kbase, const char* vbase,
+template <bool R8>
+__device__ __forceinline__ void mfma_load_tile(MfmaTile<R8>& T, const char* kbase, const char* vbase,
                                                const unsigned (&koff)[4], const unsigned (&voff)[4]) {
-  constexpr int TILE = 16 * (I8 ? 128 : 256);  // bytes of 16 token rows
+  constexpr int TILE = 16 * (R8 ? 128 : 256);  // bytes of 16 token rows
   const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase, TILE), rv = tile_rsrc(vbase, TILE);
-  if (I8) {
+  if (R8) {
     T.k[0] = bld16(rk, koff[0]);  // rows 0..7
     T.k[1] = bld16(rk, koff[1]);  // rows 8..15
   } else {
@@ -290,7 +292,7 @@ __device__ __forceinline__ void mfma_load_tile(MfmaTile<I8>& T, const char* kbas
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (I8) {
+    if (R8) {
       const u32x2_t w = bld8(rv, voff[i]);
       T.v[i] = u32x4_t{w[0], w[1], 0u, 0u};
     } else {
@@ -479,7 +481,7 @@ static_assert(kCascadeWaves == 1 || kCascadeWaves == 2 || kCascadeWaves == 4, "1
 // Either way the workgroup's waves combine (m, l, acc) through LDS and
 // wave 0 goes on with the result, so a grouped launch writes the output
 // rows itself: no partials, no merge.
-template <int KV, int BS, bool TOKSC, int NCG, int MODE, int WG>
+template <int KV, int BS, bool TOKSC, int NCG, int MODE, int WG, int D>
 __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
     float* __restrict__ out, SplitK ws,
     const unsigned short* __restrict__ q, char* __restrict__ k_cache, char* __restrict__ v_cache,
@@ -497,9 +499,12 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
                 "waves per workgroup");
   constexpr int WPI = WG;                                // waves combined per workgroup
   constexpr int TS = MODE == kModeCascade ? WG : 1;      // tile stride of one wave
-  constexpr int D = 128;
   constexpr bool I8 = KV != kKvBf16;  // 1-byte codes with fp32 scales
   constexpr int E = I8 ? 1 : 2;
+  static_assert(D == 128 || (D == 64 && !I8), "head_dim 128, or 64 with a bf16 cache");
+  constexpr int KK = D / 32;         // score MFMAs per tile (32 d each), and V words per lane row
+  constexpr int NACC = D / 16;       // accumulator blocks: d = (D / 16) c + e, e < NACC
+  constexpr bool R8 = D * E == 128;  // 128-byte token rows
   // scales of a tile: the (block, head) scale, or the lane's four tokens'
   using Sc = typename std::conditional<TOKSC, f32x4_t, float>::type;
   const int lane = threadIdx.x & 63;
@@ -637,9 +642,9 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
 #pragma unroll
     for (int u = 0; u < NCG; ++u) {
       if (nPw == 1 && head_ok[u]) {
-        float4* o = (float4*)(out + orow[u] * D + 32 * j);
+        float4* o = (float4*)(out + orow[u] * D + (D / 4) * j);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) o[k] = float4{0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < D / 16; ++k) o[k] = float4{0.f, 0.f, 0.f, 0.f};
       } else if (nPw > 1 && head_ok[u] && j == 0) {
         ws.ml[orow[u] * nPw + slot] = float2{kNegInf, 0.f};
       }
@@ -650,11 +655,11 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
 
   // Queries as the B operand: column c of group u, the 8 values of d-chunk
   // (kk*4 + j) [bf16 cache] or (j*4 + kk) [1-byte cache].
-  bf16x8_t qf[NCG][4];
+  bf16x8_t qf[NCG][KK];
 #pragma unroll
   for (int u = 0; u < NCG; ++u)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
       const int chunk = I8 ? j * 4 + kk : kk * 4 + j;
       u32x4_t w = {0u, 0u, 0u, 0u};
       if (head_ok[u]) w = *(const u32x4_t*)(q + orow[u] * D + chunk * 8);
@@ -665,30 +670,36 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
   const int tile_end = (t_end + 15) >> 4;
 
   constexpr int ROW = D * E;                       // bytes per token row
+  constexpr int CPR = ROW / 16;                    // 16 B chunks per row
   const size_t head_stride = (size_t)BS * ROW;     // bytes per (block, kv head)
 
   // Fused cache write of the newest token (position n - 1): the wave whose
-  // partition holds it reads its K/V row (16 B chunk c per lane), stores it
-  // into the cache slot at the end and attends with it in the tile that
+  // partition holds it reads its K row (16 B chunk c per lane c < CPR) and
+  // its V row (the lane's sixteenth, as a tile row is read), stores them
+  // into the cache slot at the end and attends with them in the tile that
   // holds the position (bf16 caches only; the host rejects int8).
   const int tnew = n - 1;
   const bool owns_new = !I8 && !pre && new_k != nullptr && tnew >= cz.write_from && tnew >= t_begin &&
                         tnew < t_end && (TS == 1 || ((tnew >> 4) - (t_begin >> 4)) % TS == wv);  // wave-uniform
   u32x4_t nk = {0u, 0u, 0u, 0u}, nv = {0u, 0u, 0u, 0u};
   if (owns_new) {
-    const size_t src = ((size_t)s * Hkv + g) * ROW + (size_t)c * 16;
-    nk = *(const u32x4_t*)(new_k + src);
-    nv = *(const u32x4_t*)(new_v + src);
+    const size_t src = ((size_t)s * Hkv + g) * ROW;
+    if (c < CPR) nk = *(const u32x4_t*)(new_k + src + (size_t)c * 16);
+    if constexpr (R8) {
+      const u32x2_t w = *(const u32x2_t*)(new_v + src + (size_t)c * 8);
+      nv = u32x4_t{w[0], w[1], 0u, 0u};
+    } else {
+      nv = *(const u32x4_t*)(new_v + src + (size_t)c * 16);
+    }
   }
   // K goes through a per-wave LDS tile of 16 rows of 16 B chunks (16 per
-  // row for bf16, 8 for int8).  Chunk ch of row r sits at position
+  // row of 256 bytes, 8 of 128).  Chunk ch of row r sits at position
   // ch ^ (r mod chunks-per-row), so the row-wise writes and the MFMA-layout
   // reads (16 rows, one chunk each) spread over the banks.
-  constexpr int CPR = ROW / 16;  // 16 B chunks per row
   // With several waves per item the same LDS later holds the waves'
   // (m, l, acc) for their combination.
   constexpr int KT_BYTES = WPI * 16 * CPR * 16;
-  constexpr int ACC_BYTES = (WPI - 1) * NCG * 8 * 64 * 16;
+  constexpr int ACC_BYTES = (WPI - 1) * NCG * NACC * 64 * 16;
   constexpr int CMB_BYTES = WPI > 1 ? ACC_BYTES + WPI * NCG * 2 * 64 * 4 : 0;
   __shared__ __attribute__((aligned(16))) char smem[KT_BYTES > CMB_BYTES ? KT_BYTES : CMB_BYTES];
   u32x4_t* ktile = (u32x4_t*)smem + wv * 16 * CPR;
@@ -696,15 +707,17 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     koff[i] = lane * 16 + i * 1024;
-    voff[i] = (4 * j + i) * ROW + c * 8 * E;
+    voff[i] = (4 * j + i) * ROW + c * (ROW / 16);
   }
   int kw[4], kr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (I8) {
+    if (R8) {
       const int r = 8 * (i & 1) + (lane >> 3), ch = lane & 7;  // load i (< 2) of this lane
       kw[i] = r * 8 + (ch ^ (r & 7));
-      const int rc = 2 * j + (i & 1);                          // read: row c, chunk 2j + (i & 1)
+      // read: row c, chunk 2j + (i & 1) of 1-byte codes (the lane's 32 d,
+      // converted), chunk (i & 1) * 4 + j of bf16 at head_dim 64
+      const int rc = I8 ? 2 * j + (i & 1) : (i & 1) * 4 + j;
       kr[i] = c * 8 + (rc ^ (c & 7));
     } else {
       kw[i] = (4 * i + j) * 16 + (c ^ (4 * i + j));  // write slot of load i
@@ -737,39 +750,39 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
     }
   };
 
-  f32x4_t acc[NCG][8];
+  f32x4_t acc[NCG][NACC];
   float m_run[NCG], l_run[NCG];
 #pragma unroll
   for (int u = 0; u < NCG; ++u) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[u][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < NACC; ++e) acc[u][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     m_run[u] = kNegInf;
     l_run[u] = 0.f;
   }
 
   // FULL: every token of the tile is in the pool and visible to every
   // existing column (no mask; the scores, and so the reference, are finite).
-  auto compute = [&](auto full_tag, MfmaTile<I8>& T, int ti, bool ok, const Sc& ks, const Sc& vs) {
+  auto compute = [&](auto full_tag, MfmaTile<R8>& T, int ti, bool ok, const Sc& ks, const Sc& vs) {
     constexpr bool FULL = decltype(full_tag)::value;
     const bool new_tile = owns_new && ti == (tnew >> 4);  // wave-uniform
     const int rnew = tnew & 15;
-    if (I8) {
+    if (R8) {
       ktile[kw[0]] = T.k[0];
       ktile[kw[1]] = T.k[1];
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) ktile[kw[i]] = T.k[i];
-      if (new_tile) {
-        if (j == 0) ktile[rnew * 16 + (c ^ rnew)] = nk;
+    }
+    if (!I8 && new_tile) {
+      if (j == 0 && c < CPR) ktile[rnew * CPR + (c ^ (rnew & (CPR - 1)))] = nk;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * j + i == rnew) T.v[i] = nv;
-      }
+      for (int i = 0; i < 4; ++i)
+        if (4 * j + i == rnew) T.v[i] = nv;
     }
     // ---- scores, one MFMA chain per column group over the same K operands
-    bf16x8_t ka[4];
+    bf16x8_t ka[KK];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
       if (I8) {
         // lane holds d = 32j .. 32j+31 of row c: chunk 2j (kk 0, 1), 2j+1 (kk 2, 3)
         const u32x4_t chunk = ktile[kr[kk >> 1]];
@@ -786,7 +799,7 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
     for (int u = 0; u < NCG; ++u) {
       f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qf[u][kk], sc, 0, 0, 0);
+      for (int kk = 0; kk < KK; ++kk) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qf[u][kk], sc, 0, 0, 0);
       float x[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -806,7 +819,7 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
         const float m_new = need ? mloc : m_run[u];
         const float alpha = need ? fast_exp2(m_run[u] - m_new) : 1.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[u][e] *= alpha;
+        for (int e = 0; e < NACC; ++e) acc[u][e] *= alpha;
         l_run[u] *= alpha;
         m_run[u] = m_new;
       }
@@ -842,7 +855,7 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
         for (int w = 0; w < 4; ++w) T.v[i][w] = keep ? T.v[i][w] : 0u;
       }
     }
-    unsigned vw[4][4];
+    unsigned vw[4][KK];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (I8) {
@@ -853,12 +866,12 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
         vw[i][3] = b[1];
       } else {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) vw[i][w] = T.v[i][w];
+        for (int w = 0; w < KK; ++w) vw[i][w] = T.v[i][w];
       }
     }
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // word w holds d = 8c + 2w (low half) and 8c + 2w + 1 (high half)
+    for (int w = 0; w < KK; ++w) {
+      // word w holds d = (D / 16) c + 2w (low half) and + 2w + 1 (high half)
       const unsigned e01 = __builtin_amdgcn_perm(vw[1][w], vw[0][w], 0x05040100u);
       const unsigned e23 = __builtin_amdgcn_perm(vw[3][w], vw[2][w], 0x05040100u);
       const unsigned o01 = __builtin_amdgcn_perm(vw[1][w], vw[0][w], 0x07060302u);
@@ -903,7 +916,7 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
   // that the two bodies are never live together; a fully visible tile
   // whose block id is outside the pool is skipped (it contributes nothing,
   // as the masked body would make it).
-  MfmaTile<I8> A, B;
+  MfmaTile<R8> A, B;
   const char *kA, *vA, *kB, *vB;
   bool okA, okB;
   Sc ksA{}, vsA{}, ksB{}, vsB{};
@@ -911,14 +924,14 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
     constexpr bool FULL = decltype(full_tag)::value;
     if (ti >= tend) return;
     tile_ptrs(ti, kA, vA, okA, ksA, vsA);
-    mfma_load_tile<I8>(A, kA, vA, koff, voff);
+    mfma_load_tile<R8>(A, kA, vA, koff, voff);
     while (true) {
       tile_ptrs(ti + TS < tend ? ti + TS : ti, kB, vB, okB, ksB, vsB);
-      mfma_load_tile<I8>(B, kB, vB, koff, voff);
+      mfma_load_tile<R8>(B, kB, vB, koff, voff);
       if (!FULL || okA) compute(full_tag, A, ti, okA, ksA, vsA);
       if ((ti += TS) >= tend) break;
       tile_ptrs(ti + TS < tend ? ti + TS : ti, kA, vA, okA, ksA, vsA);
-      mfma_load_tile<I8>(A, kA, vA, koff, voff);
+      mfma_load_tile<R8>(A, kA, vA, koff, voff);
       if (!FULL || okB) compute(full_tag, B, ti, okB, ksB, vsB);
       if ((ti += TS) >= tend) break;
     }
@@ -939,9 +952,10 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
     const int e = tnew / BS - tbl_base;
     const int b = e < 64 ? __builtin_amdgcn_readlane(tbl0, e) : __builtin_amdgcn_readlane(tbl1, e - 64);
     if (b >= 0 && b < NB) {
-      const size_t dst = ((size_t)b * Hkv + g) * head_stride + (size_t)(tnew % BS) * ROW + (size_t)c * 16;
-      *(u32x4_t*)(k_cache + dst) = nk;
-      *(u32x4_t*)(v_cache + dst) = nv;
+      const size_t dst = ((size_t)b * Hkv + g) * head_stride + (size_t)(tnew % BS) * ROW;
+      if (c < CPR) *(u32x4_t*)(k_cache + dst + (size_t)c * 16) = nk;
+      if constexpr (R8) *(u32x2_t*)(v_cache + dst + (size_t)c * 8) = u32x2_t{nv[0], nv[1]};
+      else *(u32x4_t*)(v_cache + dst + (size_t)c * 16) = nv;
     }
   }
 
@@ -949,7 +963,7 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
     // Combine the item's waves lane by lane in wave order: each holds its
     // own reference m (-inf: no weight), weight sum l and acc for the same
     // (column, d) slots; wave 0 continues with the combination.
-    f32x4_t(*s_acc)[NCG][8][64] = (f32x4_t(*)[NCG][8][64])smem;
+    f32x4_t(*s_acc)[NCG][NACC][64] = (f32x4_t(*)[NCG][NACC][64])smem;
     float(*s_ml)[NCG][2][64] = (float(*)[NCG][2][64])(smem + ACC_BYTES);
     __syncthreads();  // every wave is done with its K tile
 #pragma unroll
@@ -958,7 +972,7 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
       s_ml[wv][u][1][lane] = l_run[u];
       if (wv > 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s_acc[wv - 1][u][e][lane] = acc[u][e];
+        for (int e = 0; e < NACC; ++e) s_acc[wv - 1][u][e][lane] = acc[u][e];
       }
     }
     __syncthreads();
@@ -972,44 +986,36 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
         float f = m_run[u] == kNegInf ? 0.f : fast_exp2(m_run[u] - M);
         l_run[u] *= f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[u][e] *= f;
+        for (int e = 0; e < NACC; ++e) acc[u][e] *= f;
 #pragma unroll
         for (int w = 1; w < WPI; ++w) {
           const float mw = s_ml[w][u][0][lane];
           f = mw == kNegInf ? 0.f : fast_exp2(mw - M);
           l_run[u] = fmaf(f, s_ml[w][u][1][lane], l_run[u]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[u][e] += f * s_acc[w - 1][u][e][lane];
+          for (int e = 0; e < NACC; ++e) acc[u][e] += f * s_acc[w - 1][u][e][lane];
         }
       }
       m_run[u] = M;
     }
   }
 
-  // lane holds d = 32j + 8r + e in acc[u][e][r]
+  // lane holds d = (D / 4) j + NACC r + e in acc[u][e][r]
 #pragma unroll
   for (int u = 0; u < NCG; ++u) {
     const float l_tot = xor_sum_rows(l_run[u]);
     const f32x4_t* a = acc[u];
     if (!head_ok[u]) continue;
-    if (nPw == 1) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      float* o = out + orow[u] * D + 32 * j;
+    const size_t row_id = orow[u] * nPw + slot;
+    const float inv = nPw == 1 ? (l_tot > 0.f ? 1.f / l_tot : 0.f) : 1.f;
+    float* o = nPw == 1 ? out + orow[u] * D + (D / 4) * j : ws.acc + row_id * D + (D / 4) * j;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        *(float4*)(o + 8 * r) = float4{a[0][r] * inv, a[1][r] * inv, a[2][r] * inv, a[3][r] * inv};
-        *(float4*)(o + 8 * r + 4) = float4{a[4][r] * inv, a[5][r] * inv, a[6][r] * inv, a[7][r] * inv};
-      }
-    } else {
-      const size_t row_id = orow[u] * nPw + slot;
-      float* o = ws.acc + row_id * D + 32 * j;
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        *(float4*)(o + 8 * r) = float4{a[0][r], a[1][r], a[2][r], a[3][r]};
-        *(float4*)(o + 8 * r + 4) = float4{a[4][r], a[5][r], a[6][r], a[7][r]};
-      }
-      if (j == 0) ws.ml[row_id] = float2{m_run[u], l_tot};
-    }
+      for (int h = 0; h < NACC / 4; ++h)
+        *(float4*)(o + NACC * r + 4 * h) =
+            float4{a[4 * h][r] * inv, a[4 * h + 1][r] * inv, a[4 * h + 2][r] * inv, a[4 * h + 3][r] * inv};
+    if (nPw > 1 && j == 0) ws.ml[row_id] = float2{m_run[u], l_tot};
   }
   if constexpr (!BAL) return;
   }  // piece loop
@@ -1705,7 +1711,7 @@ pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipSt
   const float qk = a->scale * kLog2e;
   const SplitK ws = split_k(a, p);
 #define PA_MFMA_LAUNCH1(KV, BS, TOKSC, NCG, MODE, WG)                                                           \
-  hipLaunchKernelGGL((decode_mfma_kernel<KV, BS, TOKSC, NCG, MODE, WG>), dim3((unsigned)items), dim3(64 * WG),  \
+  hipLaunchKernelGGL((decode_mfma_kernel<KV, BS, TOKSC, NCG, MODE, WG, D>), dim3((unsigned)items), dim3(64 * WG), \
                      0, st,                                                                                    \
                      (float*)a->out, ws, (const unsigned short*)a->q, (char*)a->k_cache, (char*)a->v_cache,      \
                      a->k_scales, a->v_scales, a->block_tables, a->max_blocks_per_seq, a->context_lens,        \
@@ -1733,16 +1739,22 @@ pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipSt
   if (a->block_size == 16) PA_MFMA_LAUNCH(KV, 16, TOKSC); \
   else PA_MFMA_LAUNCH(KV, 32, TOKSC)
   const bool tok = a->kv_scale_mode == PA_SCALE_TOKEN;
-  switch (a->kv_dtype) {
-    case PA_I8:
-      if (tok) { PA_MFMA_BS(kKvI8, true); } else { PA_MFMA_BS(kKvI8, false); }
-      break;
-    case PA_FP8_E4M3:
-      if (tok) { PA_MFMA_BS(kKvFp8, true); } else { PA_MFMA_BS(kKvFp8, false); }
-      break;
-    default:
-      PA_MFMA_BS(kKvBf16, false);
-      break;
+  if (a->head_dim == 64) {  // bf16 cache only (the plan's rule)
+    constexpr int D = 64;
+    PA_MFMA_BS(kKvBf16, false);
+  } else {
+    constexpr int D = 128;
+    switch (a->kv_dtype) {
+      case PA_I8:
+        if (tok) { PA_MFMA_BS(kKvI8, true); } else { PA_MFMA_BS(kKvI8, false); }
+        break;
+      case PA_FP8_E4M3:
+        if (tok) { PA_MFMA_BS(kKvFp8, true); } else { PA_MFMA_BS(kKvFp8, false); }
+        break;
+      default:
+        PA_MFMA_BS(kKvBf16, false);
+        break;
+    }
   }
 #undef PA_MFMA_BS
 #undef PA_MFMA_LAUNCH

@@ -22,7 +22,8 @@ VALU, MFMA = pa.KERNEL_VALU, pa.KERNEL_MFMA
 
 def _kernels(case):
     ks = [0, VALU]
-    if case.q_dtype == synth.BF16 and case.kv_dtype in (synth.BF16, synth.I8) and case.head_dim == 128:
+    if case.q_dtype == synth.BF16 and ((case.kv_dtype == synth.BF16 and case.head_dim in (64, 128)) or
+                                       (case.kv_dtype == synth.I8 and case.head_dim == 128)):
         ks.append(MFMA)
     return ks
 
@@ -146,6 +147,8 @@ SHAPES = [
     (64, 4, 128, 16, synth.BF16, synth.BF16),
     (12, 4, 128, 32, synth.BF16, synth.BF16),
     (16, 16, 64, 16, synth.BF16, synth.BF16),
+    (64, 8, 64, 16, synth.BF16, synth.BF16),
+    (32, 8, 64, 32, synth.BF16, synth.BF16),
     (32, 8, 128, 16, synth.BF16, synth.I8),
     (32, 8, 128, 32, synth.BF16, synth.I8),
     (8, 8, 64, 16, synth.F32, synth.I8),
@@ -356,6 +359,7 @@ FUSED_SHAPES = [
     (32, 8, 128, 32, synth.BF16, synth.BF16),
     (40, 40, 128, 16, synth.BF16, synth.BF16),
     (16, 16, 64, 16, synth.BF16, synth.BF16),
+    (32, 8, 64, 16, synth.BF16, synth.BF16),
     (8, 8, 64, 16, synth.F32, synth.F32),
     (8, 2, 64, 32, synth.F32, synth.F32),
 ]

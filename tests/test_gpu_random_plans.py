@@ -61,7 +61,8 @@ def _draw(seed):
     S = int(rng.integers(1, 200))
     kind, lens = _lengths(rng, S, BS)
     lens[0] = max(int(lens[0]), 1)                   # a table of at least one block
-    matrix_ok = q_dt == synth.BF16 and kv_dt in (synth.BF16, synth.I8, synth.FP8) and D == 128
+    matrix_ok = q_dt == synth.BF16 and ((kv_dt in (synth.BF16, synth.I8, synth.FP8) and D == 128) or
+                                        (kv_dt == synth.BF16 and D == 64))
     kernel = pa.KERNEL_VALU if (not matrix_ok or rng.random() < 0.15) else pa.KERNEL_AUTO
     prefix_blocks = 0
     if matrix_ok and kernel == pa.KERNEL_AUTO and rng.random() < 0.3:
