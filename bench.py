@@ -106,10 +106,10 @@ def cpu_model() -> str:
 # (profiles/decode_mfma_llama3-70b_pmc_traffic.md).  Valid only for the
 # sources the counters were taken on: a changed kernel or plan reports null.
 PMC_TRAFFIC = {
-    "sources_sha256": "fb29e2c98671f5fae7efadee85df1d598d8c16e01294e2926ad4c72271a9ec72",
-    "fetch_kib": 320905.15625 + 1391.0,
-    "write_kib": 2680.15625 + 640.0,
-    "fetch_factor": 1.99226,
+    "sources_sha256": "c791af0783fc7ba60b19c65cd4a0b68469208ed0ec0d8471de3fb34b8fe2c94e",
+    "fetch_kib": 320877.90625 + 1391.0,
+    "write_kib": 2680.0 + 640.0,
+    "fetch_factor": 1.99227,
     "write_factor": 1.0,
 }
 PMC_SOURCES = ("paged_kv_cache_192_amd/csrc/pa_decode.hip", "paged_kv_cache_192_amd/csrc/pa_api.cpp",
