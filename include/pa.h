@@ -172,8 +172,8 @@ int32_t pa_abi_version(void);
  * (a row that would see no token gets zeros).  max_query_len (host) bounds
  * L_s; rows whose index falls outside [0, num_queries) (offsets that do not
  * match num_queries, a caller error) are neither read nor written.
- * Matrix-core kernel only (bf16 queries; a bf16 cache at head_dim 64 or
- * 128, or a 1-byte cache at 128); no fused cache write.
+ * Matrix-core kernel only (bf16 queries with a bf16, int8 or E4M3 cache);
+ * no fused cache write.
  *
  * Shared prefix (optional): when every sequence's first shared_prefix_len
  * tokens are the blocks shared_prefix_table[0 .. shared_prefix_len/BS - 1]
@@ -196,9 +196,8 @@ int32_t pa_abi_version(void);
  *
  * `kernel` selects the implementation: 0 = automatic, 1 = vector-ALU
  * kernel (any supported case), 2 = matrix-core kernel (bf16 queries with a
- * bf16 cache at head_dim 64 or 128, or an int8 or E4M3 cache at head_dim
- * 128; else PA_ERR_UNSUPPORTED).  Both compute the definition above; they
- * differ in rounding only.
+ * bf16, int8 or E4M3 cache, head_dim 64 or 128; else PA_ERR_UNSUPPORTED).
+ * Both compute the definition above; they differ in rounding only.
  */
 typedef struct {
   size_t struct_size;            /* = sizeof(pa_decode_args) */

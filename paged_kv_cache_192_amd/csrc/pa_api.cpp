@@ -126,18 +126,16 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
     return fail(PA_ERR_INVALID, "pa_decode: total_context_len %lld outside [0, num_seqs * max_context_len]",
                 (long long)a->total_context_len);
 
-  // matrix-core kernel: bf16 queries; a bf16 cache at head_dim 64 or 128, or
-  // a 1-byte cache at 128
-  const bool mfma_ok = a->q_dtype == PA_BF16 && ((a->kv_dtype == PA_BF16 && (a->head_dim == 128 || a->head_dim == 64)) ||
-                                                 (i8 && a->head_dim == 128));
+  // matrix-core kernel: bf16 queries with a bf16, int8 or E4M3 cache
+  const bool mfma_ok = a->q_dtype == PA_BF16 && (a->kv_dtype == PA_BF16 || i8);
   if (mq && (!mfma_ok || a->kernel == KERNEL_VALU))
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: several query rows per sequence need the matrix-core kernel "
-                                    "(bf16 queries; bf16 cache at head_dim 64 or 128, int8/E4M3 cache at 128)");
+                                    "(bf16 queries with a bf16, int8 or E4M3 cache)");
   KernelKind kind;
   if (a->kernel == KERNEL_MFMA) {
     if (!mfma_ok)
-      return fail(PA_ERR_UNSUPPORTED, "pa_decode: matrix-core kernel needs bf16 queries and a bf16 cache "
-                                      "at head_dim 64 or 128, or an int8/E4M3 cache at head_dim 128");
+      return fail(PA_ERR_UNSUPPORTED, "pa_decode: matrix-core kernel needs bf16 queries with a bf16, int8 "
+                                      "or E4M3 cache");
     kind = KERNEL_MFMA;
   } else if (a->kernel == KERNEL_VALU) {
     kind = KERNEL_VALU;

@@ -246,17 +246,19 @@ __global__ __launch_bounds__(64 * W) void decode_merge_kernel(float* __restrict_
 //    head l%16 and the 32 contiguous d = 32*(l/16) .. +31.
 // ===========================================================================
 
-template <bool R8>
+template <int RB>
 struct MfmaTile {
-  // K, coalesced and staged through LDS into the MFMA layout:
-  //    256-byte rows (bf16, head_dim 128) -> 4 x 16 B per lane: instruction
-  //    i reads rows 4i .. 4i+3, lane l the 16 B chunk l%16 of row 4i + l/16;
-  //    128-byte rows (R8: 1-byte codes at head_dim 128, bf16 at 64) -> 2 x
-  //    16 B per lane: instruction i reads rows 8i .. 8i+7, lane l the 16 B
-  //    chunk l%8 of row 8i + l/8.
-  u32x4_t k[R8 ? 2 : 4];
+  // K, coalesced and staged through LDS into the MFMA layout, RB / 64
+  // loads of 16 B per lane:
+  //    256-byte rows (bf16, head_dim 128): instruction i reads rows
+  //    4i .. 4i+3, lane l the 16 B chunk l%16 of row 4i + l/16;
+  //    128-byte rows (1-byte codes at head_dim 128, bf16 at 64): rows
+  //    8i .. 8i+7, lane l chunk l%8 of row 8i + l/8;
+  //    64-byte rows (1-byte codes at head_dim 64): all 16 rows, lane l
+  //    chunk l%4 of row l/4.
+  u32x4_t k[RB / 64];
   // V: rows 4*(l/16) + i, the lane's sixteenth of the row (element run
-  // l%16): 16 B of a 256-byte row, 8 B of a 128-byte one (upper half zero).
+  // l%16): 16, 8 or 4 B (the rest zero).
   u32x4_t v[4];
 };
 
@@ -277,22 +279,22 @@ __device__ __forceinline__ u32x4_t bld16(__amdgpu_buffer_rsrc_t r, unsigned off)
 __device__ __forceinline__ u32x2_t bld8(__amdgpu_buffer_rsrc_t r, unsigned off) {
   return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2 /* nt */));
 }
+__device__ __forceinline__ unsigned bld4(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 2 /* nt */);
+}
 
-template <bool R8>
-__device__ __forceinline__ void mfma_load_tile(MfmaTile<R8>& T, const char* kbase, const char* vbase,
+template <int RB>
+__device__ __forceinline__ void mfma_load_tile(MfmaTile<RB>& T, const char* kbase, const char* vbase,
                                                const unsigned (&koff)[4], const unsigned (&voff)[4]) {
-  constexpr int TILE = 16 * (R8 ? 128 : 256);  // bytes of 16 token rows
+  constexpr int TILE = 16 * RB;  // bytes of 16 token rows
   const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase, TILE), rv = tile_rsrc(vbase, TILE);
-  if (R8) {
-    T.k[0] = bld16(rk, koff[0]);  // rows 0..7
-    T.k[1] = bld16(rk, koff[1]);  // rows 8..15
-  } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) T.k[i] = bld16(rk, koff[i]);
-  }
+  for (int i = 0; i < RB / 64; ++i) T.k[i] = bld16(rk, koff[i]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (R8) {
+    if constexpr (RB == 64) {
+      T.v[i] = u32x4_t{bld4(rv, voff[i]), 0u, 0u, 0u};
+    } else if constexpr (RB == 128) {
       const u32x2_t w = bld8(rv, voff[i]);
       T.v[i] = u32x4_t{w[0], w[1], 0u, 0u};
     } else {
@@ -501,10 +503,11 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
   constexpr int TS = MODE == kModeCascade ? WG : 1;      // tile stride of one wave
   constexpr bool I8 = KV != kKvBf16;  // 1-byte codes with fp32 scales
   constexpr int E = I8 ? 1 : 2;
-  static_assert(D == 128 || (D == 64 && !I8), "head_dim 128, or 64 with a bf16 cache");
+  static_assert(D == 128 || D == 64, "head_dim 64 or 128");
   constexpr int KK = D / 32;         // score MFMAs per tile (32 d each), and V words per lane row
   constexpr int NACC = D / 16;       // accumulator blocks: d = (D / 16) c + e, e < NACC
-  constexpr bool R8 = D * E == 128;  // 128-byte token rows
+  constexpr int RB = D * E;          // bytes per token row (256, 128 or 64)
+  constexpr bool R8 = RB == 128;
   // scales of a tile: the (block, head) scale, or the lane's four tokens'
   using Sc = typename std::conditional<TOKSC, f32x4_t, float>::type;
   const int lane = threadIdx.x & 63;
@@ -660,7 +663,7 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
   for (int u = 0; u < NCG; ++u)
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const int chunk = I8 ? j * 4 + kk : kk * 4 + j;
+      const int chunk = I8 ? j * KK + kk : kk * 4 + j;
       u32x4_t w = {0u, 0u, 0u, 0u};
       if (head_ok[u]) w = *(const u32x4_t*)(q + orow[u] * D + chunk * 8);
       qf[u][kk] = as_bf16x8(w);
@@ -712,7 +715,11 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
   int kw[4], kr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (R8) {
+    if (RB == 64) {
+      const int r = lane >> 2, ch = lane & 3;  // the one load of this lane
+      kw[i] = r * 4 + (ch ^ (r & 3));
+      kr[i] = c * 4 + (j ^ (c & 3));           // read: row c, chunk j (the lane's 16 d, converted)
+    } else if (R8) {
       const int r = 8 * (i & 1) + (lane >> 3), ch = lane & 7;  // load i (< 2) of this lane
       kw[i] = r * 8 + (ch ^ (r & 7));
       // read: row c, chunk 2j + (i & 1) of 1-byte codes (the lane's 32 d,
@@ -762,17 +769,12 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
 
   // FULL: every token of the tile is in the pool and visible to every
   // existing column (no mask; the scores, and so the reference, are finite).
-  auto compute = [&](auto full_tag, MfmaTile<R8>& T, int ti, bool ok, const Sc& ks, const Sc& vs) {
+  auto compute = [&](auto full_tag, MfmaTile<RB>& T, int ti, bool ok, const Sc& ks, const Sc& vs) {
     constexpr bool FULL = decltype(full_tag)::value;
     const bool new_tile = owns_new && ti == (tnew >> 4);  // wave-uniform
     const int rnew = tnew & 15;
-    if (R8) {
-      ktile[kw[0]] = T.k[0];
-      ktile[kw[1]] = T.k[1];
-    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ktile[kw[i]] = T.k[i];
-    }
+    for (int i = 0; i < RB / 64; ++i) ktile[kw[i]] = T.k[i];
     if (!I8 && new_tile) {
       if (j == 0 && c < CPR) ktile[rnew * CPR + (c ^ (rnew & (CPR - 1)))] = nk;
 #pragma unroll
@@ -784,7 +786,8 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       if (I8) {
-        // lane holds d = 32j .. 32j+31 of row c: chunk 2j (kk 0, 1), 2j+1 (kk 2, 3)
+        // lane holds d = (D / 4) j .. of row c: at head_dim 128 chunk 2j (kk 0, 1)
+        // and 2j+1 (kk 2, 3), at 64 chunk j (kk 0, 1)
         const u32x4_t chunk = ktile[kr[kk >> 1]];
         const unsigned w0 = chunk[(kk & 1) * 2], w1 = chunk[(kk & 1) * 2 + 1];
         const u32x2_t lo = codes_to_bf16x4<KV>(w0), hi = codes_to_bf16x4<KV>(w1);
@@ -859,11 +862,13 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (I8) {
-        const u32x2_t a = codes_to_bf16x4<KV>(T.v[i][0]), b = codes_to_bf16x4<KV>(T.v[i][1]);
-        vw[i][0] = a[0];
-        vw[i][1] = a[1];
-        vw[i][2] = b[0];
-        vw[i][3] = b[1];
+        // 4 codes -> 2 words of bf16 pairs, per code word of the lane's row piece
+#pragma unroll
+        for (int w2 = 0; w2 < KK / 2; ++w2) {
+          const u32x2_t a = codes_to_bf16x4<KV>(T.v[i][w2]);
+          vw[i][2 * w2] = a[0];
+          vw[i][2 * w2 + 1] = a[1];
+        }
       } else {
 #pragma unroll
         for (int w = 0; w < KK; ++w) vw[i][w] = T.v[i][w];
@@ -916,7 +921,7 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
   // that the two bodies are never live together; a fully visible tile
   // whose block id is outside the pool is skipped (it contributes nothing,
   // as the masked body would make it).
-  MfmaTile<R8> A, B;
+  MfmaTile<RB> A, B;
   const char *kA, *vA, *kB, *vB;
   bool okA, okB;
   Sc ksA{}, vsA{}, ksB{}, vsB{};
@@ -924,14 +929,14 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
     constexpr bool FULL = decltype(full_tag)::value;
     if (ti >= tend) return;
     tile_ptrs(ti, kA, vA, okA, ksA, vsA);
-    mfma_load_tile<R8>(A, kA, vA, koff, voff);
+    mfma_load_tile<RB>(A, kA, vA, koff, voff);
     while (true) {
       tile_ptrs(ti + TS < tend ? ti + TS : ti, kB, vB, okB, ksB, vsB);
-      mfma_load_tile<R8>(B, kB, vB, koff, voff);
+      mfma_load_tile<RB>(B, kB, vB, koff, voff);
       if (!FULL || okA) compute(full_tag, A, ti, okA, ksA, vsA);
       if ((ti += TS) >= tend) break;
       tile_ptrs(ti + TS < tend ? ti + TS : ti, kA, vA, okA, ksA, vsA);
-      mfma_load_tile<R8>(A, kA, vA, koff, voff);
+      mfma_load_tile<RB>(A, kA, vA, koff, voff);
       if (!FULL || okB) compute(full_tag, B, ti, okB, ksB, vsB);
       if ((ti += TS) >= tend) break;
     }
@@ -1739,23 +1744,26 @@ pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipSt
   if (a->block_size == 16) PA_MFMA_LAUNCH(KV, 16, TOKSC); \
   else PA_MFMA_LAUNCH(KV, 32, TOKSC)
   const bool tok = a->kv_scale_mode == PA_SCALE_TOKEN;
-  if (a->head_dim == 64) {  // bf16 cache only (the plan's rule)
+#define PA_MFMA_KV()                                                                 \
+  switch (a->kv_dtype) {                                                             \
+    case PA_I8:                                                                      \
+      if (tok) { PA_MFMA_BS(kKvI8, true); } else { PA_MFMA_BS(kKvI8, false); }       \
+      break;                                                                         \
+    case PA_FP8_E4M3:                                                                \
+      if (tok) { PA_MFMA_BS(kKvFp8, true); } else { PA_MFMA_BS(kKvFp8, false); }     \
+      break;                                                                         \
+    default:                                                                         \
+      PA_MFMA_BS(kKvBf16, false);                                                    \
+      break;                                                                         \
+  }
+  if (a->head_dim == 64) {
     constexpr int D = 64;
-    PA_MFMA_BS(kKvBf16, false);
+    PA_MFMA_KV();
   } else {
     constexpr int D = 128;
-    switch (a->kv_dtype) {
-      case PA_I8:
-        if (tok) { PA_MFMA_BS(kKvI8, true); } else { PA_MFMA_BS(kKvI8, false); }
-        break;
-      case PA_FP8_E4M3:
-        if (tok) { PA_MFMA_BS(kKvFp8, true); } else { PA_MFMA_BS(kKvFp8, false); }
-        break;
-      default:
-        PA_MFMA_BS(kKvBf16, false);
-        break;
-    }
+    PA_MFMA_KV();
   }
+#undef PA_MFMA_KV
 #undef PA_MFMA_BS
 #undef PA_MFMA_LAUNCH
 #undef PA_MFMA_GROUP

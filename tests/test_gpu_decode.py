@@ -22,8 +22,7 @@ VALU, MFMA = pa.KERNEL_VALU, pa.KERNEL_MFMA
 
 def _kernels(case):
     ks = [0, VALU]
-    if case.q_dtype == synth.BF16 and ((case.kv_dtype == synth.BF16 and case.head_dim in (64, 128)) or
-                                       (case.kv_dtype == synth.I8 and case.head_dim == 128)):
+    if case.q_dtype == synth.BF16 and case.kv_dtype in (synth.BF16, synth.I8):
         ks.append(MFMA)
     return ks
 
@@ -151,6 +150,8 @@ SHAPES = [
     (32, 8, 64, 32, synth.BF16, synth.BF16),
     (32, 8, 128, 16, synth.BF16, synth.I8),
     (32, 8, 128, 32, synth.BF16, synth.I8),
+    (32, 8, 64, 16, synth.BF16, synth.I8),
+    (16, 16, 64, 32, synth.BF16, synth.I8),
     (8, 8, 64, 16, synth.F32, synth.I8),
 ]
 

@@ -1,11 +1,13 @@
-"""head_dim 64 on the matrix-core kernel (bf16 queries and cache) against
-the CPU oracle, in every launch form the plan can pick: one wave per
+"""head_dim 64 on the matrix-core kernel (bf16 queries; bf16, int8 or E4M3
+cache) against the CPU oracle, in every launch form the plan can pick: one wave per
 partition with the merge, a grouped launch (at least 256 (sequence, kv
 head) items), the balanced split of a skewed batch, a shared prefix read
 once, several query rows per sequence (one and two column groups per wave),
-and the fused cache write.  A 128-byte token row is loaded like a 1-byte
-cache's (two 16-byte chunks per lane for K, an 8-byte sixteenth of each V
-row), with two score products and four accumulator blocks per tile.
+and the fused cache write.  A bf16 row (128 bytes) is loaded like a 1-byte
+cache's row at head_dim 128 (two 16-byte chunks per lane for K, an 8-byte
+sixteenth of each V row); a 1-byte row (64 bytes) in one 16-byte K chunk
+per lane and a 4-byte sixteenth of each V row; either way two score
+products and four accumulator blocks per tile.
 
 Tolerance max |gpu - oracle| <= 2e-3; the fused write bit-exact; a forced
 vector-ALU run of the same call within the same tolerance."""
@@ -16,7 +18,8 @@ import torch
 import oracle
 import paged_kv_cache_192_amd as pa
 import synth
-from gpu_helpers import TOL_BF16, case_on_device, max_err, run_decode, run_oracle, say, to_dev, to_host
+from gpu_helpers import (TOL_BF16, case_on_device, max_err, quantize_case, quantize_case_by_token, run_decode,
+                         run_oracle, say, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -133,3 +136,26 @@ def test_fused_write_head_dim64(S):
     assert np.array_equal(to_host(dev["v"]), case.v_cache)
     err = max_err(out.cpu().numpy().astype(np.float64), run_oracle(case))
     assert err <= TOL_BF16, err
+
+
+@pytest.mark.parametrize("kv,mode,BS", [(synth.I8, pa.PA_SCALE_BLOCK, 16), (synth.I8, pa.PA_SCALE_TOKEN, 32),
+                                        (synth.FP8, pa.PA_SCALE_TOKEN, 16), (synth.FP8, pa.PA_SCALE_BLOCK, 32)])
+def test_quantised_head_dim64(kv, mode, BS):
+    """1-byte caches at head_dim 64: plain, grouped (256 items) and balanced
+    (skewed lengths with the hint) launches."""
+    rng = np.random.default_rng(6)
+    lens = [0, 1, 15, 16, 17, 255, 256, 257] + [int(x) for x in rng.integers(1, 1500, size=23)] + [3000]
+    case = synth.make_case("d64-q", 360 + BS, lens, 64, 8, D, BS, kv_dtype=kv, free_frac=0.1)
+    if kv == synth.I8 and mode == pa.PA_SCALE_BLOCK:
+        quantize_case(case)
+    else:
+        quantize_case_by_token(case, mode)
+    expect = oracle.paged_decode(case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens,
+                                 float(case.scale), case.k_scales, case.v_scales, scale_mode=mode)
+    dev = case_on_device(case)
+    for kern, P, hint in ((pa.KERNEL_MFMA, 0, False), (pa.KERNEL_MFMA, 0, True), (pa.KERNEL_MFMA, 16, False),
+                          (pa.KERNEL_MFMA, 512, False), (pa.KERNEL_VALU, 0, False)):
+        say("head_dim 64 quantised", kv, mode, BS, "kernel", kern, "partition", P, "hint", hint)
+        got = run_decode(case, dev, partition_tokens=P, kernel=kern, length_hint=hint)
+        err = max_err(got, expect)
+        assert err <= TOL_BF16, (kv, mode, BS, kern, P, hint, err)

@@ -99,13 +99,16 @@ QUANT_SHAPES = [
     (40, 40, 128, 16, synth.BF16, synth.I8, pa.PA_SCALE_TOKEN),
     (8, 8, 64, 16, synth.F32, synth.FP8, pa.PA_SCALE_TOKEN),
     (8, 2, 64, 32, synth.F32, synth.I8, pa.PA_SCALE_BLOCK),
+    (32, 8, 64, 16, synth.BF16, synth.FP8, pa.PA_SCALE_TOKEN),
+    (64, 8, 64, 32, synth.BF16, synth.I8, pa.PA_SCALE_BLOCK),
+    (16, 4, 64, 16, synth.BF16, synth.I8, pa.PA_SCALE_TOKEN),
 ]
 EDGE_LENS = [0, 1, 2, 15, 16, 17, 33, 255, 256, 257, 1000, 1025]
 
 
 def _kernels(case):
     ks = [VALU]
-    if case.q_dtype == synth.BF16 and case.head_dim == 128:
+    if case.q_dtype == synth.BF16:
         ks.append(MFMA)
     return ks
 

@@ -53,7 +53,8 @@ def _draw(seed):
     Hq, Hkv, D = SHAPES[rng.integers(0, len(SHAPES))]
     BS = int(rng.choice([16, 32]))
     if D == 64:
-        q_dt, kv_dt = (synth.F32, synth.F32) if rng.random() < 0.5 else (synth.BF16, synth.BF16)
+        q_dt, kv_dt = [(synth.F32, synth.F32), (synth.BF16, synth.BF16), (synth.BF16, synth.I8),
+                       (synth.BF16, synth.FP8)][int(rng.integers(0, 4))]
     else:
         q_dt, kv_dt = synth.BF16, str(rng.choice([synth.BF16, synth.BF16, synth.I8, synth.FP8, synth.F32]))
         if kv_dt == synth.F32:
@@ -61,8 +62,7 @@ def _draw(seed):
     S = int(rng.integers(1, 200))
     kind, lens = _lengths(rng, S, BS)
     lens[0] = max(int(lens[0]), 1)                   # a table of at least one block
-    matrix_ok = q_dt == synth.BF16 and ((kv_dt in (synth.BF16, synth.I8, synth.FP8) and D == 128) or
-                                        (kv_dt == synth.BF16 and D == 64))
+    matrix_ok = q_dt == synth.BF16 and kv_dt in (synth.BF16, synth.I8, synth.FP8)
     kernel = pa.KERNEL_VALU if (not matrix_ok or rng.random() < 0.15) else pa.KERNEL_AUTO
     prefix_blocks = 0
     if matrix_ok and kernel == pa.KERNEL_AUTO and rng.random() < 0.3:
