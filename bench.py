@@ -342,6 +342,8 @@ WORKLOADS = {
     "llama13b": "13B-shaped MHA decode, one layer (32 seqs, U[200,2048] tokens, 40 heads of 128, bf16)",
     "prefix": "prefix sharing + copy-on-write, one layer (50 seqs, 2,000 shared + U[50,500], 32/8 heads, block 32)",
     "int8": "int8 KV decode, one layer (64 seqs, log-normal lengths, 32/8 heads, per-(block, head) scales)",
+    "gqa-d64": "70B-shaped batch at head_dim 64 (20 x 8,000 tokens, 64/8 heads, bf16, block 16, fused write)",
+    "int8-d64": "70B-shaped batch at head_dim 64 with an int8 cache (per-(block, head) scales)",
 }
 
 
@@ -514,7 +516,10 @@ def run_next_workload(args) -> dict:
         step is pa_quantize_and_cache of every sequence's new token (codes
         and scales computed in-kernel) then pa_decode;
       spec-decode / chunked-prefill: the 70B-shaped layer with L causal
-        query rows per sequence (the last L tokens of each context)."""
+        query rows per sequence (the last L tokens of each context);
+      gqa-d64 / int8-d64: the 70B-shaped batch (tables and lengths) at
+        head_dim 64, bf16 with the fused write or int8 codes with
+        per-(block, head) scales, seeded device values."""
     import numpy as np
     import torch
 
@@ -576,6 +581,50 @@ def run_next_workload(args) -> dict:
                     "pct_hbm_peak": round(100.0 * alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                     "algorithmic_bytes_per_layer": alg, "sum_ctx": int(np.sum(cls)),
                     "step": "pa_quantize_and_cache (new token, per-token scales) + pa_decode"})
+        return res
+    if w in ("gqa-d64", "int8-d64"):
+        st = synth.config3_structure()
+        c = synth.CFG3
+        S, Hq, Hkv, BS, D = c["num_seqs"], c["num_q_heads"], c["num_kv_heads"], c["block_size"], 64
+        NB = st["num_blocks"]
+        i8 = w == "int8-d64"
+        e = 1 if i8 else 2
+        R = max(1, -(-(1 << 30) // (2 * NB * Hkv * BS * D * e)))
+        bt = torch.from_numpy(st["block_tables"]).to(dev)
+        cl = torch.from_numpy(st["context_lens"]).to(dev)
+        shape = (NB, Hkv, BS, D)
+        if i8:
+            K = [torch.randint(-127, 128, shape, generator=gen, dtype=torch.int8, device=dev) for _ in range(R)]
+            V = [torch.randint(-127, 128, shape, generator=gen, dtype=torch.int8, device=dev) for _ in range(R)]
+            KS = [torch.rand(NB, Hkv, generator=gen, device=dev) * 0.03 + 0.01 for _ in range(R)]
+            VS = [torch.rand(NB, Hkv, generator=gen, device=dev) * 0.03 + 0.01 for _ in range(R)]
+            newk = newv = None
+        else:
+            K = [torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(R)]
+            V = [torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(R)]
+            KS = VS = [None] * R
+            newk = torch.randn(S, Hkv, D, generator=gen, device=dev).to(torch.bfloat16)
+            newv = torch.randn(S, Hkv, D, generator=gen, device=dev).to(torch.bfloat16)
+        q = torch.randn(S, Hq, D, generator=gen, device=dev).to(torch.bfloat16)
+        outs = [torch.empty(S, Hq, D, dtype=torch.float32, device=dev) for _ in range(R)]
+        ws = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
+        ctx = int(st["context_lens"][0])
+        total = int(np.sum(st["context_lens"], dtype=np.int64))
+
+        def prepare(stream):
+            return [pa.PreparedDecode(q, K[r], V[r], bt, cl, float(1.0 / math.sqrt(D)), ctx, outs[r],
+                                      k_scales=KS[r], v_scales=VS[r], workspace=ws, stream=stream,
+                                      new_key=newk, new_value=newv, partition_tokens=args.partition_tokens,
+                                      kernel=args.kernel, total_context_len=total) for r in range(R)]
+
+        ms = _timed_graph(prepare, args.steps, args.warmup, outs) / R
+        cls = st["context_lens"]
+        alg = decode_algorithmic_bytes(cls, Hq, Hkv, D, BS, e, 2, int8_scales=i8)
+        res.update({"replicas": R, "ms_per_layer": round(ms, 5), "tokens_per_s": round(S / (ms * 1e-3), 1),
+                    "kv_gbs": round(kv_bytes(cls, Hkv, D, e) / (ms * 1e-3) / 1e9, 1),
+                    "pct_hbm_peak": round(100.0 * alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                    "algorithmic_bytes_per_layer": alg,
+                    "step": "pa_decode" + (" (int8 codes, per-(block, head) scales)" if i8 else " with fused write")})
         return res
     # multi-query rows on the 70B-shaped layer
     L = 4 if w == "spec-decode" else 64
@@ -843,7 +892,7 @@ def main():
         res = run_swap(args)
     elif args.mode == "read-ceiling":
         res = read_ceiling(args)
-    elif args.workload in ("int8-token", "fp8", "spec-decode", "chunked-prefill"):
+    elif args.workload in ("int8-token", "fp8", "spec-decode", "chunked-prefill", "gqa-d64", "int8-d64"):
         res = run_next_workload(args)
     elif args.workload != "llama3-70b":
         res = run_single_layer(args)

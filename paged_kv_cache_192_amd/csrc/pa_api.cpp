@@ -37,13 +37,16 @@ static bool valid_scale_mode(int m) { return m == PA_SCALE_BLOCK || m == PA_SCAL
 // CU lost 10 %.  1-byte tiles carry half the bytes for the same arithmetic:
 // on the same layer with int8 or E4M3 codes, 10 waves per CU (512-token
 // partitions) measured 61-65 % of peak against 52-58 % at 5 per CU and
-// 38-49 % at 2.5.  The vector-ALU kernel keeps one tile in flight; five
-// waves per CU.
+// 38-49 % at 2.5.  A bf16 cache at head_dim 64 also carries half the bytes
+// per tile: on the 70B-shaped batch at head_dim 64, 1,280 waves (8
+// partitions) read 71.8-72.3 % against 62.0-62.4 % with 640 (and 67-69 %
+// with 12 or 16 partitions).  The vector-ALU kernel keeps one tile in
+// flight; five waves per CU.
 // SIMDs of the chip (256 compute units of 4)
 constexpr int64_t kSimds = 1024;
 
-static int target_waves(KernelKind kind, pa_dtype kv) {
-  if (kind == KERNEL_MFMA) return quantised(kv) ? 2560 : 640;
+static int target_waves(KernelKind kind, pa_dtype kv, int head_dim) {
+  if (kind == KERNEL_MFMA) return quantised(kv) ? 2560 : head_dim == 64 ? 1280 : 640;
   return 1280;
 }
 
@@ -175,7 +178,7 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
 
   const int64_t max_tiles = (int64_t)kMaxPartitionBlocks * a->block_size / 16;
   const int64_t total = a->total_context_len > 0 ? a->total_context_len : seq_tokens;
-  const int64_t target = target_waves(kind, a->kv_dtype);
+  const int64_t target = target_waves(kind, a->kv_dtype, a->head_dim);
 
   // Partition length for `seqs` sequences of at most max_len tokens (sum
   // total_len), each split over `per_seq` items per partition of `wpi`
