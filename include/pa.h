@@ -121,7 +121,8 @@ int32_t pa_abi_version(void);
  *                 n <= max_context_len
  *   out           [num_seqs][num_q_heads][head_dim] fp32
  * Slots at or beyond n inside a sequence's last block, and blocks no table
- * names, are never read: they may hold anything, NaN included.
+ * names, are never read: they (and their scales) may hold anything, NaN
+ * included.
  *
  * Supported: head_dim in {64, 128}; block_size in {16, 32};
  * q_dtype in {PA_F32, PA_BF16}; kv_dtype in {PA_F32, PA_BF16, PA_I8,

@@ -170,7 +170,7 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   // per wave in workgroups of kSharedWaves.  On the 70B-shaped layer with a
   // 64-row chunk per sequence (32 column groups per item) the per-wave
   // kernel is bound by those re-reads: 347-349 against 384-389 TFLOP/s.
-  p->shared_tiles = kind == KERNEL_MFMA && mq && a->kv_dtype == PA_BF16 && a->head_dim == 128 && p->cg_waves >= 2;
+  p->shared_tiles = kind == KERNEL_MFMA && mq && a->head_dim == 128 && p->cg_waves >= 2;
   if (p->shared_tiles) {
     p->ncg = 1;
     p->cg_waves = p->cgroups;

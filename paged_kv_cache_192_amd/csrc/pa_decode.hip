@@ -830,12 +830,13 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) pw[r] = (FULL || x[r] != kNegInf) ? fast_exp2(x[r] - m_run[u]) : 0.f;
       l_run[u] += (pw[0] + pw[1]) + (pw[2] + pw[3]);
+      // (a masked token's V scale may be NaN: its weight stays zero)
       if constexpr (TOKSC) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pw[r] *= vs[r];
+        for (int r = 0; r < 4; ++r) pw[r] = (FULL || x[r] != kNegInf) ? pw[r] * vs[r] : 0.f;
       } else if (I8) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pw[r] *= vs;
+        for (int r = 0; r < 4; ++r) pw[r] = (FULL || x[r] != kNegInf) ? pw[r] * vs : 0.f;
       }
       // ---- P as bf16 hi + lo, B operand of the P.V MFMA
       float lo[4];
@@ -1046,15 +1047,22 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
 // (the same speed with the softmax, half of the P.V products or the score
 // products taken out).
 // ===========================================================================
-template <int BS, int NCG, int W>
+//
+// KV: bf16 cache, or 1-byte codes (kKvI8 / kKvFp8) with fp32 scales per
+// (block, kv head) or, TOKSC, per token: the loaders convert the codes to
+// bf16 into the same LDS layout and stage each row's scales beside the
+// tile; the scores and the weights are scaled as in decode_mfma_kernel.
+template <int KV, int BS, bool TOKSC, int NCG, int W>
 __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
     float* __restrict__ out, SplitK ws, const unsigned short* __restrict__ q, const char* __restrict__ k_cache,
-    const char* __restrict__ v_cache, const int32_t* __restrict__ tables, int max_blocks,
+    const char* __restrict__ v_cache, const float* __restrict__ k_scales, const float* __restrict__ v_scales,
+    const int32_t* __restrict__ tables, int max_blocks,
     const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int NB, float qk_log2, int P, int nP,
     const int32_t* __restrict__ qsl, int CGW, int WGI, int num_rows) {
   constexpr int D = 128;
-  constexpr int ROW = D * 2;  // bytes per token row
-  constexpr int CPR = ROW / 16;
+  constexpr bool I8 = KV != kKvBf16;
+  constexpr int ROW = I8 ? D : D * 2;  // bytes per token row in the cache
+  constexpr int CPR = 16;              // 16-byte bf16 chunks per row in LDS
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1137,6 +1145,8 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
   // in lane order: no bank conflicts).
   __shared__ __attribute__((aligned(16))) u32x4_t kv_k[2][2][16 * CPR];
   __shared__ __attribute__((aligned(16))) u32x4_t kv_v[2][2][16 * CPR];
+  // 1-byte codes: each row's K and V scale, kv_s[stage][tile][K / V][row]
+  __shared__ __attribute__((aligned(16))) float kv_s[2][2][2][16];
   // the first 2 * 16 * CPR threads (whole waves) load: K chunks, then V
   static_assert(W * 64 >= 2 * 16 * CPR, "a workgroup loads a tile in one pass");
   // (taken from the wave's first lane: the compiler then keeps the cache
@@ -1149,7 +1159,11 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
   // lane's row within the group of four) of chunk ld_ch, tokens 4 (ld_r >> 2) ..
   const int ld_slot = ld_v ? (ld_r & 3) * 64 + (ld_r >> 2) * 16 + ld_ch : ld_r * 16 + (ld_ch ^ ld_r);
   const char* ld_cache = ld_v ? v_cache : k_cache;
-  const unsigned ld_off = (unsigned)(ld_r * ROW + ld_ch * 16);
+  const float* ld_scales = ld_v ? v_scales : k_scales;
+  // per-(block, head) scales: NB * Hkv floats (< 2^30 entries: the pool fits one GPU)
+  const __amdgpu_buffer_rsrc_t ld_rsc = tile_rsrc((const char*)ld_scales, I8 && !TOKSC ? NB * Hkv * 4 : 0);
+  // each loader's sixteenth of a row: 8 bf16 (16 B) or 8 codes (8 B)
+  const unsigned ld_off = (unsigned)(ld_r * ROW + ld_ch * (ROW / 16));
   const size_t head_stride = (size_t)BS * ROW;
   auto block_of = [&](int ti, bool& ok) {
     const int e = (ti * 16) / BS - tbl_base;
@@ -1157,11 +1171,37 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
     ok = b >= 0 && b < NB;
     return ok ? b : 0;
   };
-  auto load_chunk = [&](int ti) {
+  // a loader's piece of tile ti (raw codes in the low half for 1-byte
+  // caches) and, for 1-byte caches, its row's scale
+  auto load_chunk = [&](int ti, float& sc) {
     bool ok;
     const int b = block_of(ti, ok);
     const char* tile = ld_cache + ((size_t)b * Hkv + g) * head_stride + (size_t)((ti * 16) % BS) * ROW;
-    return bld16(tile_rsrc(tile, 16 * ROW), ld_off);  // uniform tile base, per-lane offset
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(tile, 16 * ROW);  // uniform tile base, per-lane offset
+    if constexpr (I8) {
+      if constexpr (TOKSC) {
+        sc = ld_scales[((size_t)b * Hkv + g) * BS + (size_t)((ti * 16) % BS) + ld_r];
+      } else {
+        // a vector-memory load, not a scalar one: a scalar load shares the
+        // LDS wait counter, so the wave's next LDS reads would wait for it
+        sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ld_rsc, (unsigned)(b * Hkv + g) * 4u, 0, 0));
+      }
+      const u32x2_t w = bld8(rs, ld_off);
+      return u32x4_t{w[0], w[1], 0u, 0u};
+    } else {
+      (void)sc;
+      return bld16(rs, ld_off);
+    }
+  };
+  // 8 codes -> the 8 bf16 of the loader's LDS chunk (exact: every int8 and
+  // E4M3 value fits bf16)
+  auto to_bf16 = [&](u32x4_t R) {
+    if constexpr (I8) {
+      const u32x2_t a = codes_to_bf16x4<KV>(R[0]), b = codes_to_bf16x4<KV>(R[1]);
+      return u32x4_t{a[0], a[1], b[0], b[1]};
+    } else {
+      return R;
+    }
   };
   // A V loader's chunk R of tile ti -> its {even d, odd d} operand halves.
   // Rows past the partition or of a block outside the pool are zeroed
@@ -1195,8 +1235,10 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
     return u32x4_t{__builtin_amdgcn_perm(R[1], R[0], 0x05040100u), __builtin_amdgcn_perm(R[3], R[2], 0x05040100u),
                    __builtin_amdgcn_perm(R[1], R[0], 0x07060302u), __builtin_amdgcn_perm(R[3], R[2], 0x07060302u)};
   };
-  // store tiles ti (RA) and ti + 1 (RB) into stage st
-  auto store_stage = [&](int st, int ti, u32x4_t RA, u32x4_t RB) {
+  // store tiles ti (RA, row scale SA) and ti + 1 (RB, SB) into stage st
+  auto store_stage = [&](int st, int ti, u32x4_t RA, u32x4_t RB, float SA, float SB) {
+    RA = to_bf16(RA);
+    RB = to_bf16(RB);
     if (ld_v) {  // wave-uniform
       const u32x4_t a = v_operands(ti, RA), b = v_operands(ti + 1, RB);
       kv_v[st][0][ld_slot] = u32x4_t{a[0], a[1], b[0], b[1]};
@@ -1204,6 +1246,19 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
     } else {
       kv_k[st][0][ld_slot] = RA;
       kv_k[st][1][ld_slot] = RB;
+    }
+    if (I8 && ld_ch == 0) {
+      if (ld_v) {
+        // a masked row's weight is zero; so is its V scale (the scale of a
+        // slot past the context may be NaN)
+        bool ok;
+        (void)block_of(min(ti, (t_end - 1) >> 4), ok);
+        SA = ok && ti * 16 + ld_r < t_end ? SA : 0.f;
+        (void)block_of(min(ti + 1, (t_end - 1) >> 4), ok);
+        SB = ok && ti * 16 + 16 + ld_r < t_end ? SB : 0.f;
+      }
+      kv_s[st][0][ld_v][ld_r] = SA;
+      kv_s[st][1][ld_v][ld_r] = SB;
     }
   };
   int kr[4];
@@ -1252,10 +1307,20 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
         sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qf[u][kk], sb, 0, 0, 0);
       }
       float x[8];
+      if constexpr (I8) {
+        // the scores of 1-byte codes times each token's K scale
+        const f32x4_t ksa = *(const f32x4_t*)&kv_s[st][0][0][4 * j], ksb = *(const f32x4_t*)&kv_s[st][1][0][4 * j];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        x[r] = sa[r] * qk_log2;
-        x[4 + r] = sb[r] * qk_log2;
+        for (int r = 0; r < 4; ++r) {
+          x[r] = sa[r] * (qk_log2 * ksa[r]);
+          x[4 + r] = sb[r] * (qk_log2 * ksb[r]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x[r] = sa[r] * qk_log2;
+          x[4 + r] = sb[r] * qk_log2;
+        }
       }
       if (!full) {  // wave-uniform
 #pragma unroll
@@ -1280,6 +1345,15 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
 #pragma unroll
       for (int r = 0; r < 8; ++r) pw[r] = fast_exp2(x[r] - m_run[u]);
       l_run[u] += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
+      if constexpr (I8) {
+        // the weights times each token's V scale
+        const f32x4_t vsa = *(const f32x4_t*)&kv_s[st][0][1][4 * j], vsb = *(const f32x4_t*)&kv_s[st][1][1][4 * j];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pw[r] *= vsa[r];
+          pw[4 + r] *= vsb[r];
+        }
+      }
       unsigned hi[4], lo[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -1313,29 +1387,30 @@ __global__ __launch_bounds__(64 * W) void shared_tile_mq_kernel(
   // makes a wait for every load in flight) never holds back a newer load:
   // each load has a whole stage, two tiles of compute, to arrive.
   u32x4_t RA = {0u, 0u, 0u, 0u}, RB = {0u, 0u, 0u, 0u};
+  float SA = 0.f, SB = 0.f;
   if (loader) {  // wave-uniform
-    RA = load_chunk(tile_begin);
-    RB = load_chunk(clamp_tile(tile_begin + 1));
-    store_stage(0, tile_begin, RA, RB);
-    RA = load_chunk(clamp_tile(tile_begin + 2));
-    RB = load_chunk(clamp_tile(tile_begin + 3));
+    RA = load_chunk(tile_begin, SA);
+    RB = load_chunk(clamp_tile(tile_begin + 1), SB);
+    store_stage(0, tile_begin, RA, RB, SA, SB);
+    RA = load_chunk(clamp_tile(tile_begin + 2), SA);
+    RB = load_chunk(clamp_tile(tile_begin + 3), SB);
   }
   __syncthreads();
   for (int ti = tile_begin;;) {
     compute(0, ti);
     if ((ti += 2) >= tile_end) break;
     if (loader) {
-      store_stage(1, ti, RA, RB);  // stage 1 was last read before the previous barrier
-      RA = load_chunk(clamp_tile(ti + 2));
-      RB = load_chunk(clamp_tile(ti + 3));
+      store_stage(1, ti, RA, RB, SA, SB);  // stage 1 was last read before the previous barrier
+      RA = load_chunk(clamp_tile(ti + 2), SA);
+      RB = load_chunk(clamp_tile(ti + 3), SB);
     }
     __syncthreads();
     compute(1, ti);
     if ((ti += 2) >= tile_end) break;
     if (loader) {
-      store_stage(0, ti, RA, RB);
-      RA = load_chunk(clamp_tile(ti + 2));
-      RB = load_chunk(clamp_tile(ti + 3));
+      store_stage(0, ti, RA, RB, SA, SB);
+      RA = load_chunk(clamp_tile(ti + 2), SA);
+      RB = load_chunk(clamp_tile(ti + 3), SB);
     }
     __syncthreads();
   }
@@ -1606,7 +1681,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(
       for (int i = 0; i < GT; ++i) {
         const float pw = valid ? fast_exp2(x[i] - m[i]) : 0.f;
         l[i] += pw;
-        const float pv = pw * vsr[r];
+        const float pv = valid ? pw * vsr[r] : 0.f;  // (a masked slot's scale may be NaN)
 #pragma unroll
         for (int k = 0; k < DC; ++k) acc[i][k] = fmaf(pv, valid ? vv[r][k] : 0.f, acc[i][k]);
       }
@@ -1693,14 +1768,29 @@ pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipSt
     if (wgs > 0x7fffffffu) return fail(PA_ERR_UNSUPPORTED, "pa_decode: grid too large");
     const SplitK ws = split_k(a, p);
     const float qk = a->scale * kLog2e;
-#define PA_SHARED_LAUNCH(BS, NCG, W)                                                                            \
-  hipLaunchKernelGGL((shared_tile_mq_kernel<BS, NCG, W>), dim3((unsigned)wgs), dim3(64 * W), 0, st,             \
+#define PA_SHARED_LAUNCH(KV, BS, TOKSC, NCG, W)                                                                 \
+  hipLaunchKernelGGL((shared_tile_mq_kernel<KV, BS, TOKSC, NCG, W>), dim3((unsigned)wgs), dim3(64 * W), 0, st,  \
                      (float*)a->out, ws, (const unsigned short*)a->q, (const char*)a->k_cache,                  \
-                     (const char*)a->v_cache, a->block_tables, a->max_blocks_per_seq, a->context_lens,          \
+                     (const char*)a->v_cache, a->k_scales, a->v_scales, a->block_tables, a->max_blocks_per_seq, \
+                     a->context_lens,                                                                           \
                      a->num_q_heads, a->num_kv_heads, p.G, a->num_blocks, qk, p.partition_tokens,               \
                      p.num_partitions, a->query_start_loc, cgw, wgi, a->num_queries)
-    if (a->block_size == 16) PA_SHARED_LAUNCH(16, 1, kSharedWaves);
-    else PA_SHARED_LAUNCH(32, 1, kSharedWaves);
+#define PA_SHARED_BS(KV, TOKSC)                                                  \
+  if (a->block_size == 16) PA_SHARED_LAUNCH(KV, 16, TOKSC, 1, kSharedWaves);    \
+  else PA_SHARED_LAUNCH(KV, 32, TOKSC, 1, kSharedWaves)
+    const bool tok = a->kv_scale_mode == PA_SCALE_TOKEN;
+    switch (a->kv_dtype) {
+      case PA_I8:
+        if (tok) { PA_SHARED_BS(kKvI8, true); } else { PA_SHARED_BS(kKvI8, false); }
+        break;
+      case PA_FP8_E4M3:
+        if (tok) { PA_SHARED_BS(kKvFp8, true); } else { PA_SHARED_BS(kKvFp8, false); }
+        break;
+      default:
+        PA_SHARED_BS(kKvBf16, false);
+        break;
+    }
+#undef PA_SHARED_BS
 #undef PA_SHARED_LAUNCH
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode (shared-tile kernel) launch");

@@ -87,10 +87,11 @@ def quantize_case(case: synth.DecodeCase) -> None:
     synth.poison_unused(case.v_cache, case.block_tables, case.context_lens, case.free_blocks, synth.I8)
 
 
-def quantize_case_by_token(case: synth.DecodeCase, scale_mode: int, static=(0.03, 0.03)) -> None:
+def quantize_case_by_token(case: synth.DecodeCase, scale_mode: int, static=(0.03, 0.03), poison=1e30) -> None:
     """int8 / E4M3 cases: every cached token's fp32 row quantised by the
     oracle's quantising write, per token (dynamic) or with static per-layer
-    scales; unused slots keep poison codes and scales."""
+    scales; unused slots keep poison codes and the scale poison (NaN is
+    allowed: slots past a sequence's length are never read)."""
     slots = synth.token_slots(case)
     NB, Hkv, BS, D = case.k_cache.shape
     kf = case.extra["k_f32"]
@@ -102,8 +103,8 @@ def quantize_case_by_token(case: synth.DecodeCase, scale_mode: int, static=(0.03
     case.k_cache = np.full(case.k_cache.shape, synth._poison_value(case.kv_dtype), dt)
     case.v_cache = case.k_cache.copy()
     sshape = oracle.scale_shape(NB, Hkv, BS, scale_mode)
-    case.k_scales = np.full(sshape, 1e30, np.float32)
-    case.v_scales = np.full(sshape, 1e30, np.float32)
+    case.k_scales = np.full(sshape, poison, np.float32)
+    case.v_scales = np.full(sshape, poison, np.float32)
     if len(slots):
         oracle.quantize_and_cache(key, val, case.k_cache, case.v_cache, case.k_scales, case.v_scales, slots,
                                   scale_mode, static[0], static[1])

@@ -22,6 +22,7 @@ MQ_SHAPES = [
     (32, 8, 16, synth.I8, pa.PA_SCALE_TOKEN),
     (64, 8, 16, synth.FP8, pa.PA_SCALE_TOKEN),
     (32, 8, 32, synth.FP8, pa.PA_SCALE_BLOCK),
+    (64, 8, 32, synth.I8, pa.PA_SCALE_BLOCK),
 ]
 # (context length, query rows): decode rows, drafted tokens, prefill chunks,
 # a whole-sequence prefill, and rows that see nothing (more rows than tokens)

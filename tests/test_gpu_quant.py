@@ -131,6 +131,42 @@ def test_quantised_decode_parity(shape):
                 assert err <= TOL_BF16, (shape, kern, P, err)
 
 
+@pytest.mark.parametrize("kvd,mode,D", [(synth.I8, pa.PA_SCALE_TOKEN, 128), (synth.FP8, pa.PA_SCALE_TOKEN, 64),
+                                        (synth.FP8, pa.PA_SCALE_BLOCK, 128)])
+def test_nan_scales_outside_the_context_are_never_used(kvd, mode, D):
+    """Scales of slots past a sequence's length (and of free blocks) set to
+    NaN: a masked token's weight must stay zero, not 0 x NaN, in the
+    single-row decode (both kernels) and with several query rows (the
+    shared-tile kernel for 64 rows of 8 heads, the per-wave one for 2)."""
+    lens = [1, 15, 17, 100, 257, 1000, 0, 33]
+    case = synth.make_case("nan-scales", 380 + D + mode, lens, 64, 8, D, 16, kv_dtype=kvd, free_frac=0.2)
+    quantize_case_by_token(case, mode, poison=np.nan)
+    expect = oracle.paged_decode(case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens,
+                                 float(case.scale), case.k_scales, case.v_scales, scale_mode=mode)
+    assert np.isfinite(expect).all()
+    dev = case_on_device(case)
+    for kern in (MFMA, VALU):
+        for P in (0, 16, 256):
+            say("NaN scales", kvd, mode, D, "kernel", kern, "partition", P)
+            err = max_err(run_decode(case, dev, partition_tokens=P, kernel=kern), expect)
+            assert err <= TOL_BF16, (kvd, mode, D, kern, P, err)
+    rng = np.random.default_rng(7)
+    for rows in (2, 64):
+        qlens = [min(rows, n) for n in lens]
+        qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+        q = synth.bf16_bits(rng.standard_normal((int(qsl[-1]), 64, D)).astype(np.float32))
+        exp_mq = oracle.paged_attention(q, case.k_cache, case.v_cache, case.block_tables, case.context_lens, qsl,
+                                        float(case.scale), case.k_scales, case.v_scales, scale_mode=mode)
+        for P in (0, 256):
+            say("NaN scales, query rows", rows, "partition", P)
+            out = pa.decode(to_dev(q), dev["k"], dev["v"], dev["bt"], dev["cl"], float(case.scale),
+                            case.max_context_len, k_scales=dev["ks"], v_scales=dev["vs"], partition_tokens=P,
+                            query_start_loc=to_dev(qsl), max_query_len=rows)
+            torch.cuda.synchronize()
+            err = max_err(out.cpu().numpy().astype(np.float64), exp_mq)
+            assert err <= TOL_BF16, (kvd, mode, D, rows, P, err)
+
+
 @pytest.mark.parametrize("kvd", [synth.I8, synth.FP8])
 def test_config5_per_token_scales(kvd):
     """The int8 workload's batch (64 sequences, log-normal lengths) with
