@@ -106,8 +106,8 @@ def cpu_model() -> str:
 # (profiles/decode_mfma_llama3-70b_pmc_traffic.md).  Valid only for the
 # sources the counters were taken on: a changed kernel or plan reports null.
 PMC_TRAFFIC = {
-    "sources_sha256": "c791af0783fc7ba60b19c65cd4a0b68469208ed0ec0d8471de3fb34b8fe2c94e",
-    "fetch_kib": 320877.90625 + 1391.0,
+    "sources_sha256": "2fc0f270bec1204e8d0eebf6dd8205125c821311bee7a4e062a1d12bd3cecf46",
+    "fetch_kib": 320886.125 + 1388.5,
     "write_kib": 2680.0 + 640.0,
     "fetch_factor": 1.99227,
     "write_factor": 1.0,
@@ -337,6 +337,7 @@ WORKLOADS = {
                    "(checking 3 drafted tokens)",
     "chunked-prefill": "70B-shaped layer (20 x 8,000 tokens, 64/8 heads, bf16) with a 64-row causal prefill chunk "
                        "per sequence",
+    "chunked-prefill-int8": "the chunked-prefill layer over an int8 cache (per-(block, head) scales, seeded codes)",
     "llama3-70b": "70B-shaped GQA decode, 80 layers (20 x 8,000 tokens, 64/8 heads, bf16, block 16)",
     "tiny": "tiny fp32 decode (4 seqs of 17/33/100/200 tokens, 8 heads of 64, block 16)",
     "llama13b": "13B-shaped MHA decode, one layer (32 seqs, U[200,2048] tokens, 40 heads of 128, bf16)",
@@ -517,6 +518,8 @@ def run_next_workload(args) -> dict:
         and scales computed in-kernel) then pa_decode;
       spec-decode / chunked-prefill: the 70B-shaped layer with L causal
         query rows per sequence (the last L tokens of each context);
+        chunked-prefill-int8 the same 64-row chunks over seeded int8 codes
+        with per-(block, head) scales;
       gqa-d64 / int8-d64: the 70B-shaped batch (tables and lengths) at
         head_dim 64, bf16 with the fused write or int8 codes with
         per-(block, head) scales, seeded device values."""
@@ -628,13 +631,24 @@ def run_next_workload(args) -> dict:
         return res
     # multi-query rows on the 70B-shaped layer
     L = 4 if w == "spec-decode" else 64
+    i8 = w == "chunked-prefill-int8"
+    e = 1 if i8 else 2
     st = synth.config3_structure()
     c = synth.CFG3
     S, Hq, Hkv, D, BS = c["num_seqs"], c["num_q_heads"], c["num_kv_heads"], c["head_dim"], c["block_size"]
     R = 2
     bt = torch.from_numpy(st["block_tables"]).to(dev)
     cl = torch.from_numpy(st["context_lens"]).to(dev)
-    layers = [synth.config3_layer_values(r, dev) for r in range(R)]
+    KS = VS = [None] * R
+    if i8:
+        NB = st["num_blocks"]
+        shape = (NB, Hkv, BS, D)
+        layers = [(None, torch.randint(-127, 128, shape, generator=gen, dtype=torch.int8, device=dev),
+                   torch.randint(-127, 128, shape, generator=gen, dtype=torch.int8, device=dev)) for _ in range(R)]
+        KS = [torch.rand(NB, Hkv, generator=gen, device=dev) * 0.03 + 0.01 for _ in range(R)]
+        VS = [torch.rand(NB, Hkv, generator=gen, device=dev) * 0.03 + 0.01 for _ in range(R)]
+    else:
+        layers = [synth.config3_layer_values(r, dev) for r in range(R)]
     qsl = torch.arange(0, S * L + 1, L, dtype=torch.int32, device=dev)
     qs = [torch.randn(S * L, Hq, D, generator=gen, device=dev).to(torch.bfloat16) for _ in range(R)]
     outs = [torch.empty(S * L, Hq, D, dtype=torch.float32, device=dev) for _ in range(R)]
@@ -643,17 +657,18 @@ def run_next_workload(args) -> dict:
 
     def prepare(stream):
         return [pa.PreparedDecode(qs[r], layers[r][1], layers[r][2], bt, cl, float(st["scale"]), ctx, outs[r],
-                                  workspace=ws, stream=stream, partition_tokens=args.partition_tokens,
-                                  query_start_loc=qsl, max_query_len=L) for r in range(R)]
+                                  k_scales=KS[r], v_scales=VS[r], workspace=ws, stream=stream,
+                                  partition_tokens=args.partition_tokens, query_start_loc=qsl, max_query_len=L)
+                for r in range(R)]
 
     ms = _timed_graph(prepare, args.steps, args.warmup, outs) / R
     cls = st["context_lens"]
-    alg = decode_algorithmic_bytes(cls, Hq, Hkv, D, BS, 2, 2, query_rows=S * L)
+    alg = decode_algorithmic_bytes(cls, Hq, Hkv, D, BS, e, 2, int8_scales=i8, query_rows=S * L)
     visible = sum(sum(int(n) - L + i + 1 for i in range(L)) for n in cls)
     flops = 4 * Hq * D * visible
     res.update({"replicas": R, "query_rows_per_seq": L, "ms_per_layer": round(ms, 5),
                 "query_tokens_per_s": round(S * L / (ms * 1e-3), 1),
-                "kv_gbs": round(kv_bytes(cls, Hkv, D, 2) / (ms * 1e-3) / 1e9, 1),
+                "kv_gbs": round(kv_bytes(cls, Hkv, D, e) / (ms * 1e-3) / 1e9, 1),
                 "pct_hbm_peak": round(100.0 * alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                 "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "algorithmic_bytes_per_layer": alg,
                 "step": "pa_decode with query_start_loc (%d causal rows per sequence)" % L})
@@ -892,7 +907,8 @@ def main():
         res = run_swap(args)
     elif args.mode == "read-ceiling":
         res = read_ceiling(args)
-    elif args.workload in ("int8-token", "fp8", "spec-decode", "chunked-prefill", "gqa-d64", "int8-d64"):
+    elif args.workload in ("int8-token", "fp8", "spec-decode", "chunked-prefill", "chunked-prefill-int8", "gqa-d64",
+                           "int8-d64"):
         res = run_next_workload(args)
     elif args.workload != "llama3-70b":
         res = run_single_layer(args)
