@@ -69,6 +69,9 @@ constexpr int kMaxGroupWaves = 8;
 // ... and only with at least this many (sequence, kv head) items: one
 // workgroup per compute unit of the chip
 constexpr int64_t kGroupMinItems = 256;
+// An automatic split into more partitions than a group holds is still
+// grouped (4 waves) when the longest sequence has at most this many tiles
+constexpr int64_t kGroupShortTiles = 128;
 // waves of a workgroup sharing K/V tiles through LDS (several query rows
 // per sequence, bf16 cache, more than one wave of column groups per item),
 // one column group each: registers for 4 waves per SIMD

@@ -84,6 +84,17 @@ def test_struct_layout_and_workspace_size():
     # 16-token partitions: 10)
     st, n = _ws(_cpu_args(num_seqs=128, partition_tokens=16, max_context_len=160))
     assert st == pa.PA_OK and n == al(128 * 8 * 10 * 8) + al(128 * 8 * 10 * 128 * 4)
+    # a short ragged batch whose automatic split asks for more than 8
+    # partitions (the longest sequence 2,048 tokens = 128 tiles, mean a
+    # half): re-cut into 4-wave groups, no workspace; one tile longer keeps
+    # the partials, and so does the vector-ALU kernel
+    short = dict(num_seqs=128, max_blocks_per_seq=129, num_blocks=128 * 129, total_context_len=128 * 1024)
+    st, n = _ws(_cpu_args(max_context_len=2048, **short))
+    assert st == pa.PA_OK and n == 0
+    st, n = _ws(_cpu_args(max_context_len=2049, **short))
+    assert st == pa.PA_OK and n > 0
+    st, n = _ws(_cpu_args(max_context_len=2048, kernel=pa.KERNEL_VALU, **short))
+    assert st == pa.PA_OK and n > 0
     # one partition: no workspace
     st, n = _ws(_cpu_args(partition_tokens=128))
     assert st == pa.PA_OK and n == 0

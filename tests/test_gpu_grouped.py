@@ -78,6 +78,32 @@ def test_grouped_decode_matches_oracle(shape):
     assert max_err(out.cpu().numpy().astype(np.float64), expect) <= TOL_BF16
 
 
+@pytest.mark.parametrize("kv", [synth.BF16, synth.I8])
+def test_short_ragged_batch_regrouped(kv):
+    """A short ragged batch with the length hint: the automatic split asks
+    for more than 8 short partitions, and the plan re-cuts it into 4-wave
+    groups (no workspace) when the longest sequence has at most 128 tiles."""
+    S, Hq, Hkv, BS = 32, 32, 8, 16
+    rng = np.random.default_rng(17)
+    lens = [0, 1, 15, 16, 17, 63, 64, 65] + [int(x) for x in rng.integers(50, 1001, size=S - 9)] + [1000]
+    case = synth.make_case("grouped-short", 950, lens, Hq, Hkv, 128, BS, kv_dtype=kv, free_frac=0.1)
+    if kv == synth.I8:
+        quantize_case(case)
+    expect = oracle.paged_decode(case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens,
+                                 float(case.scale), case.k_scales, case.v_scales)
+    d = case_on_device(case)
+    total = int(np.sum(case.context_lens, dtype=np.int64))
+    assert _grouped(case, d, 0, total_context_len=total)
+    assert not _grouped(case, d, 64, total_context_len=total)
+    for P in (0, 64):
+        say("short ragged batch", kv, "partition", P)
+        out = pa.decode(d["q"], d["k"], d["v"], d["bt"], d["cl"], float(case.scale), case.max_context_len,
+                        k_scales=d["ks"], v_scales=d["vs"], partition_tokens=P, total_context_len=total)
+        torch.cuda.synchronize()
+        err = max_err(out.cpu().numpy().astype(np.float64), expect)
+        assert err <= TOL_BF16, (kv, P, err)
+
+
 def test_fewer_items_than_compute_units_are_not_grouped():
     """160 items (20 sequences x 8 kv heads, the 70B-shaped batch) keep the
     partials and the merge: a workgroup per item would leave compute units
