@@ -308,7 +308,12 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   // 4-wave groups instead: on 32 to 64 sequences of 50 to 1,000 or 2,000
   // tokens (8 kv heads, bf16 or int8) that took 0.66 to 0.87 of the time of
   // the short partitions, their partials and the merge, and 0.87 to 1.12 of
-  // 8-wave groups.
+  // 8-wave groups.  A small batch (at most kGroupSmallTiles tiles over all
+  // its (sequence, kv head) items) takes at most 4 waves per group: on 32 to
+  // 100 sequences of 50..500 tokens (8 kv heads) 4-wave groups took 0.85 to
+  // 0.93 of the time of 8-wave ones for bf16, 0.90 to 1.02 for int8; on 128
+  // sequences of 50..1,000 tokens (33,600 tiles) and the 13B-shaped layer
+  // 8 waves stay ahead.
   p->grouped = false;
   p->group_waves = 1;
   const int64_t ctx_tiles = ((int64_t)a->max_context_len + 15) / 16;
@@ -319,7 +324,8 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
       (int64_t)a->num_seqs * a->num_kv_heads >= kGroupMinItems) {
     int w = 2;
     while (w < p->num_partitions && w < kMaxGroupWaves) w *= 2;
-    if (short_recut) w = 4;
+    const int64_t all_tiles = (total / 16 + a->num_seqs) * a->num_kv_heads;
+    if (short_recut || (a->partition_tokens == 0 && w > 4 && all_tiles <= kGroupSmallTiles)) w = 4;
     if (a->partition_tokens == 0) {
       const int64_t tiles = ctx_tiles;
       p->partition_tokens = (int)(16 * ((tiles + w - 1) / w));

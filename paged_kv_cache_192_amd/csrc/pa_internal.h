@@ -72,6 +72,9 @@ constexpr int64_t kGroupMinItems = 256;
 // An automatic split into more partitions than a group holds is still
 // grouped (4 waves) when the longest sequence has at most this many tiles
 constexpr int64_t kGroupShortTiles = 128;
+// ... and a batch of at most this many tiles in all takes at most 4 waves
+// per group
+constexpr int64_t kGroupSmallTiles = 16384;
 // waves of a workgroup sharing K/V tiles through LDS (several query rows
 // per sequence, bf16 cache, more than one wave of column groups per item),
 // one column group each: registers for 4 waves per SIMD
