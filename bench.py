@@ -106,8 +106,8 @@ def cpu_model() -> str:
 # (profiles/decode_mfma_llama3-70b_pmc_traffic.md).  Valid only for the
 # sources the counters were taken on: a changed kernel or plan reports null.
 PMC_TRAFFIC = {
-    "sources_sha256": "2fc0f270bec1204e8d0eebf6dd8205125c821311bee7a4e062a1d12bd3cecf46",
-    "fetch_kib": 320886.125 + 1388.5,
+    "sources_sha256": "29a264a9948dfcbbee370021c62d1d1ead04d5b91c5cc9118e49417f8fa4ca6a",
+    "fetch_kib": 320889.90625 + 1388.5,
     "write_kib": 2680.0 + 640.0,
     "fetch_factor": 1.99227,
     "write_factor": 1.0,
