@@ -165,11 +165,12 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   p->cg_waves = (p->cgroups + p->ncg - 1) / p->ncg;
   p->rows = (int64_t)(mq ? a->num_queries : (a->num_seqs > 0 ? a->num_seqs : 0)) * a->num_q_heads;
   // Several query rows with more than one wave of column groups per item
-  // and a bf16 cache: the item's waves share each K/V tile through LDS in
-  // workgroups (else each wave reads every tile itself), one column group
-  // per wave in workgroups of kSharedWaves.  On the 70B-shaped layer with a
-  // 64-row chunk per sequence (32 column groups per item) the per-wave
-  // kernel is bound by those re-reads: 347-349 against 384-389 TFLOP/s.
+  // (head_dim 128; bf16, int8 or E4M3 cache): the item's waves share each
+  // K/V tile through LDS in workgroups (else each wave reads every tile
+  // itself), one column group per wave in workgroups of kSharedWaves.  On
+  // the 70B-shaped layer with a 64-row chunk per sequence (32 column groups
+  // per item) the per-wave kernel is bound by those re-reads: 347-349
+  // against 384-389 TFLOP/s at first (bf16; int8 375 against 442-449).
   p->shared_tiles = kind == KERNEL_MFMA && mq && a->head_dim == 128 && p->cg_waves >= 2;
   if (p->shared_tiles) {
     p->ncg = 1;

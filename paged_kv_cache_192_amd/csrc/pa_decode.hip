@@ -1031,15 +1031,17 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
 // Several query rows per sequence with many column groups (long prefill
 // chunks): the column-group waves of one (sequence, kv head, partition)
 // share its K/V tiles.  A workgroup of W waves loads each 16-token tile
-// once -- one 16-byte chunk per thread, K in the first 256 threads and V in
-// the next 256 -- into a two-stage LDS ring, and every wave computes its
-// NCG column groups from LDS; one barrier per tile.  Used with one column
-// group per wave and 16 waves (109 VGPRs, 4 waves per SIMD): two per wave
-// in 8-wave workgroups measured 320-370 against 370-373 TFLOP/s on a 64-row
-// chunk, the per-wave kernel 344-349.
-// Each thread keeps the next two tiles' chunks in flight in registers (the
+// once -- a sixteenth of a row per thread (8 bf16, or 8 codes of a 1-byte
+// cache converted to bf16 by the loader), K in the first 256 threads and V
+// in the next 256 -- into an LDS ring of two stages of two tiles, and every
+// wave computes its NCG column groups from LDS; one barrier per stage.
+// Used with one column group per wave and 16 waves (115-119 VGPRs, 4 waves
+// per SIMD): on a 64-row chunk of the 70B-shaped layer 490-501 TFLOP/s,
+// against 449 with two column groups per wave in 8-wave workgroups and
+// 347-349 for the per-wave kernel.
+// Each loader keeps the next stage's chunks in flight in registers (the
 // loads past the partition re-read its last tile, so every iteration waits
-// for the same number of loads).  bf16 caches, head_dim 128.
+// for the same number of loads).  head_dim 128; bf16, int8 or E4M3 caches.
 //
 // Without it every column-group wave reads every tile itself (from L2 after
 // the first): a 64-row chunk with 8 query heads per kv head has 32 column

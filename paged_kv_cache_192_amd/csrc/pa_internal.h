@@ -76,8 +76,8 @@ constexpr int64_t kGroupShortTiles = 128;
 // per group
 constexpr int64_t kGroupSmallTiles = 16384;
 // waves of a workgroup sharing K/V tiles through LDS (several query rows
-// per sequence, bf16 cache, more than one wave of column groups per item),
-// one column group each: registers for 4 waves per SIMD
+// per sequence, head_dim 128, more than one wave of column groups per
+// item), one column group each: registers for 4 waves per SIMD
 constexpr int kSharedWaves = 16;
 
 // Everything the launchers need, derived on the host from pa_decode_args.
