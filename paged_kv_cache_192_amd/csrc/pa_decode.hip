@@ -367,8 +367,9 @@ __device__ __forceinline__ void mfma_item(int item, int Hkv, int nP, int CG, int
 // Both write partials: prefix partition p at slot p, the sequence's
 // partition p at slot nPp + p, of nPw slots per row.  An item of a cascade
 // launch is a workgroup of kCascadeWaves waves: wave w takes tiles
-// tile_begin + w, + 2w, ... of the partition (chains a quarter as long,
-// the neighbouring tiles in flight together) and the waves' (m, l, acc)
+// tile_begin + w, tile_begin + w + kCascadeWaves, ... of the partition
+// (chains a quarter as long, the neighbouring tiles in flight together)
+// and the waves' (m, l, acc)
 // are combined through LDS before the one partial is written.
 struct Cascade {
   const int32_t* table;  // shared prefix blocks (NULL: no prefix items)
