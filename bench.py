@@ -329,10 +329,10 @@ def run(args) -> dict:
 
 
 WORKLOADS = {
-    "int8-token": "int8 KV with per-token scales: pa_quantize_and_cache of each new token, then decode (64 seqs, "
-                  "log-normal lengths, 32/8 heads)",
-    "fp8": "E4M3 fp8 KV with per-token scales: pa_quantize_and_cache of each new token, then decode (64 seqs, "
-           "log-normal lengths, 32/8 heads)",
+    "int8-token": "int8 KV with per-token scales: each new token quantised and written, then decode, in one "
+                  "pa_decode call (--unfused: pa_quantize_and_cache first) (64 seqs, log-normal lengths, 32/8 heads)",
+    "fp8": "E4M3 fp8 KV with per-token scales: each new token quantised and written, then decode, in one pa_decode "
+           "call (--unfused: pa_quantize_and_cache first) (64 seqs, log-normal lengths, 32/8 heads)",
     "spec-decode": "70B-shaped layer (20 x 8,000 tokens, 64/8 heads, bf16) with 4 causal query rows per sequence "
                    "(checking 3 drafted tokens)",
     "chunked-prefill": "70B-shaped layer (20 x 8,000 tokens, 64/8 heads, bf16) with a 64-row causal prefill chunk "
@@ -514,8 +514,9 @@ def run_next_workload(args) -> dict:
     """Workloads of the quantised and multi-query paths, one layer per
     replica (R replicas so that >= 1 GB is touched between reuses):
       int8-token / fp8: the int8 workload's batch with per-token scales; a
-        step is pa_quantize_and_cache of every sequence's new token (codes
-        and scales computed in-kernel) then pa_decode;
+        step quantises and writes every sequence's new token and decodes,
+        in one pa_decode call with new_key/new_value (with --unfused:
+        pa_quantize_and_cache, then pa_decode);
       spec-decode / chunked-prefill: the 70B-shaped layer with L causal
         query rows per sequence (the last L tokens of each context);
         chunked-prefill-int8 the same 64-row chunks over seeded int8 codes
@@ -565,14 +566,18 @@ def run_next_workload(args) -> dict:
         ws = torch.empty(1 << 27, dtype=torch.uint8, device=dev)
         total = int(np.sum(case.context_lens, dtype=np.int64))
 
+        fused = not args.unfused
+
         def prepare(stream):
             calls = []
             for r in range(R):
-                calls.append(pa.prepare_quantize_and_cache(newk, newv, K[r], V[r], KS[r], VS[r], slots,
-                                                           stream=stream))
+                if not fused:
+                    calls.append(pa.prepare_quantize_and_cache(newk, newv, K[r], V[r], KS[r], VS[r], slots,
+                                                               stream=stream))
                 calls.append(pa.PreparedDecode(q, K[r], V[r], bt, cl, float(case.scale), case.max_context_len,
                                                outs[r], k_scales=KS[r], v_scales=VS[r], workspace=ws, stream=stream,
-                                               partition_tokens=args.partition_tokens, total_context_len=total))
+                                               partition_tokens=args.partition_tokens, total_context_len=total,
+                                               new_key=newk if fused else None, new_value=newv if fused else None))
             return calls
 
         ms = _timed_graph(prepare, args.steps, args.warmup, outs) / R
@@ -583,7 +588,8 @@ def run_next_workload(args) -> dict:
                     "kv_gbs": round(kvb / (ms * 1e-3) / 1e9, 1),
                     "pct_hbm_peak": round(100.0 * alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                     "algorithmic_bytes_per_layer": alg, "sum_ctx": int(np.sum(cls)),
-                    "step": "pa_quantize_and_cache (new token, per-token scales) + pa_decode"})
+                    "step": ("pa_decode quantising and writing each new token (per-token scales) as it attends"
+                             if fused else "pa_quantize_and_cache (new token, per-token scales) + pa_decode")})
         return res
     if w in ("gqa-d64", "int8-d64"):
         st = synth.config3_structure()
@@ -875,7 +881,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--unfused", action="store_true",
-                    help="separate slot-mapping and reshape_and_cache launches instead of the fused cache write")
+                    help="separate slot-mapping and reshape_and_cache (or pa_quantize_and_cache) launches instead "
+                         "of the fused cache write")
     ap.add_argument("--eager", dest="graph", action="store_false",
                     help="launch each call from Python instead of replaying the captured step")
     ap.add_argument("--mode", choices=["decode", "copy-calibration", "swap", "read-ceiling"], default="decode",

@@ -158,8 +158,16 @@ int32_t pa_abi_version(void);
  * (n-1) % BS, every kv head) and attends with them.  The result, cache
  * bytes included, is that of pa_slot_mapping (context_lens form) +
  * pa_reshape_and_cache + pa_decode, in one launch.  n must not exceed
- * max_context_len.  Not available for quantised caches (PA_ERR_UNSUPPORTED):
- * write them with pa_quantize_and_cache first.
+ * max_context_len.  For a quantised cache with per-token scales
+ * (PA_SCALE_TOKEN) at head_dim 128 on the matrix-core kernel, new_key and
+ * new_value are bf16 rows: the call quantises them exactly as
+ * pa_quantize_and_cache with dynamic scales would, stores the codes and
+ * the two scales (k_scales and v_scales are then written, despite their
+ * const type) and attends with them; the result, cache and scale bytes
+ * included, is that of pa_slot_mapping + pa_quantize_and_cache + pa_decode.
+ * Other quantised forms (per-block scales, head_dim 64, the vector-ALU
+ * kernel) give PA_ERR_UNSUPPORTED: write them with pa_quantize_and_cache
+ * first.
  *
  * Several query rows per sequence (chunked prefill, or checking several
  * drafted tokens in one pass: "Cache KV en production", section "Les

@@ -251,9 +251,14 @@ def make_decode_args(q, k_cache, v_cache, block_tables, context_lens, scale: flo
     a.workspace = get(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a.stream = _stream(stream) if device_pointers else None
+    quantised = _dtype_code(k_cache) in (PA_I8, PA_FP8_E4M3)
     for name, t in (("new_key", new_key), ("new_value", new_value)):
         if t is not None and tuple(t.shape) != (S, Hkv, D):
             raise ValueError("%s must be [%d][%d][%d]" % (name, S, Hkv, D))
+        want = PA_BF16 if quantised else _dtype_code(k_cache)
+        if t is not None and _dtype_code(t) != want:
+            raise ValueError("%s must hold %s rows (%s)" % (name, "bfloat16" if quantised else "the cache's type",
+                                                            "quantised by the call" if quantised else "copied"))
     a.new_key = get(new_key)
     a.new_value = get(new_value)
     a.total_context_len = int(total_context_len)

@@ -102,8 +102,9 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
   if (!std::isfinite(a->scale)) return fail(PA_ERR_INVALID, "pa_decode: scale is not finite");
   if ((a->new_key == nullptr) != (a->new_value == nullptr))
     return fail(PA_ERR_INVALID, "pa_decode: give both new_key and new_value, or neither");
-  if (a->new_key && i8)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: no fused cache write for quantised caches");
+  if (a->new_key && i8 && (a->kv_scale_mode != PA_SCALE_TOKEN || a->head_dim != 128))
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: the fused write into a quantised cache needs per-token scales "
+                                    "and head_dim 128 (else pa_quantize_and_cache first)");
   if (a->max_context_len < 0 || (int64_t)a->max_context_len > (int64_t)a->max_blocks_per_seq * a->block_size)
     return fail(PA_ERR_INVALID, "pa_decode: max_context_len %d outside [0, max_blocks_per_seq*block_size]",
                 a->max_context_len);
@@ -135,6 +136,9 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: several query rows per sequence need the matrix-core kernel "
                                     "(bf16 queries with a bf16, int8 or E4M3 cache)");
   KernelKind kind;
+  if (a->new_key && i8 && (!mfma_ok || a->kernel == KERNEL_VALU))
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: the fused write into a quantised cache needs the matrix-core "
+                                    "kernel (bf16 queries)");
   if (a->kernel == KERNEL_MFMA) {
     if (!mfma_ok)
       return fail(PA_ERR_UNSUPPORTED, "pa_decode: matrix-core kernel needs bf16 queries with a bf16, int8 "

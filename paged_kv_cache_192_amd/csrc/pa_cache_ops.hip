@@ -4,6 +4,7 @@
 // latency at decode batch sizes (the host link for swaps) and never touch
 // memory outside the slots or blocks they are given.
 #include "pa_internal.h"
+#include "pa_quant.h"
 
 namespace pa {
 
@@ -95,26 +96,6 @@ __global__ __launch_bounds__(kCopyThreads) void block_copy_kernel(
 // elements l + 64 i of the row (i < D / 64), for K and then V.
 // ---------------------------------------------------------------------------
 
-// Nearest OCP E4M3 code to v: ties to the even mantissa, magnitudes above
-// 448 saturate, NaN -> 0x7F.  Normal range: keep 3 of fp32's 23 mantissa
-// bits with round-to-nearest-even on the 20 dropped bits (a carry moves to
-// the exponent), then rebias the exponent from 127 to 7.  Below 2^-6 the
-// codes are the multiples of 2^-9 (code 8 being the smallest normal).
-__device__ __forceinline__ unsigned e4m3_encode(float v) {
-  const unsigned sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fabsf(v);
-  if (a != a) return 0x7Fu;
-  if (a > 448.f) return sign | 0x7Eu;
-  unsigned code;
-  if (a < 0.015625f) {
-    code = (unsigned)rintf(a * 512.f);
-  } else {
-    const unsigned ab = __float_as_uint(a);
-    code = ((ab + 0x7FFFFu + ((ab >> 20) & 1u)) >> 20) - (120u << 3);
-  }
-  return sign | code;
-}
-
 __device__ __forceinline__ float wave_amax(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
@@ -134,7 +115,7 @@ __global__ __launch_bounds__(64) void quantize_and_cache_kernel(
   if (slot < 0 || slot >= num_slots) return;
   const int64_t b = slot / BS;
   const int off = (int)(slot % BS);
-  const float qmax = FP8 ? 448.f : 127.f;
+  const float qmax = quant_max<FP8>();
 #pragma unroll
   for (int kv = 0; kv < 2; ++kv) {
     const SRC* src = (kv ? value : key) + ((int64_t)t * Hkv + h) * D;
@@ -155,15 +136,7 @@ __global__ __launch_bounds__(64) void quantize_and_cache_kernel(
     unsigned char* dst = (kv ? v_cache : k_cache) + ((b * Hkv + h) * BS + off) * D;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const float r = x[i] / s;
-      unsigned code;
-      if (FP8) {
-        code = e4m3_encode(r);
-      } else {
-        const float c = fminf(fmaxf(rintf(r), -127.f), 127.f);
-        code = (unsigned)(int)c & 0xFFu;
-      }
-      dst[lane + 64 * i] = (unsigned char)code;
+      dst[lane + 64 * i] = (unsigned char)quant_code<FP8>(x[i] / s);
     }
     if (lane == 0) {
       float* sc = kv ? v_scales : k_scales;

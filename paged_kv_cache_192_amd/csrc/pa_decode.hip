@@ -23,6 +23,7 @@
 #include <type_traits>
 
 #include "pa_internal.h"
+#include "pa_quant.h"
 
 namespace pa {
 
@@ -108,6 +109,29 @@ __device__ __forceinline__ float row_max16(float x) {
   return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false)));
 }
 __device__ __forceinline__ float wave_max(float x) { return xor_max_rows(row_max16(x)); }
+
+template <bool FP8>
+__device__ __forceinline__ u32x2_t quant_row8(u32x4_t w, float& scale) {
+  float x[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = __uint_as_float(w[k] << 16);
+    x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+  amax = row_max16(amax);
+  const float s = amax > 0.f ? amax / quant_max<FP8>() : 1.f;
+  unsigned lo = 0u, hi = 0u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    lo |= quant_code<FP8>(x[e] / s) << (8 * e);
+    hi |= quant_code<FP8>(x[4 + e] / s) << (8 * e);
+  }
+  scale = s;
+  return u32x2_t{lo, hi};
+}
 __device__ __forceinline__ float wave_sum(float x) { return xor_sum_rows(row_sum16(x)); }
 
 // ---------------------------------------------------------------------------
@@ -331,6 +355,14 @@ __device__ __forceinline__ u32x2_t codes_to_bf16x4(unsigned w) {
   else return i8x4_to_bf16x4(w);
 }
 
+// The fused quantising write: 8 bf16 values of a row (d = 8c .. 8c+7 in
+// lane c of a 16-lane row; the 16 lanes hold the row of 128) -> their 8
+// code bytes, and the row's per-token scale amax / quant_max, exactly as
+// pa_quantize_and_cache computes them (the same row maximum, division and
+// code function).
+template <bool FP8>
+__device__ __forceinline__ u32x2_t quant_row8(u32x4_t w, float& scale);
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t w) { return __builtin_bit_cast(bf16x8_t, w); }
 __device__ __forceinline__ i16x4_t as_i16x4(unsigned a, unsigned b) {
   return __builtin_bit_cast(i16x4_t, u32x2_t{a, b});
@@ -488,7 +520,7 @@ template <int KV, int BS, bool TOKSC, int NCG, int MODE, int WG, int D>
 __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
     float* __restrict__ out, SplitK ws,
     const unsigned short* __restrict__ q, char* __restrict__ k_cache, char* __restrict__ v_cache,
-    const float* __restrict__ k_scales, const float* __restrict__ v_scales, const int32_t* __restrict__ tables,
+    float* __restrict__ k_scales, float* __restrict__ v_scales, const int32_t* __restrict__ tables,
     int max_blocks, const int32_t* __restrict__ context_lens, int Hq, int Hkv, int G, int NB, float qk_log2,
     int P, int nP, const char* __restrict__ new_k, const char* __restrict__ new_v,
     const int32_t* __restrict__ qsl, int CG, int num_rows, Cascade cz, Balanced bz) {
@@ -681,19 +713,35 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
   // partition holds it reads its K row (16 B chunk c per lane c < CPR) and
   // its V row (the lane's sixteenth, as a tile row is read), stores them
   // into the cache slot at the end and attends with them in the tile that
-  // holds the position (bf16 caches only; the host rejects int8).
+  // holds the position.  A 1-byte cache with per-token scales at head_dim
+  // 128 (QW) takes bf16 rows and quantises them first, as
+  // pa_quantize_and_cache would: lane c codes d = 8c .. 8c+7 of each row
+  // (the same in every 16-lane row), and the new token's scales stand in
+  // for the ones in its slot.  The host rejects the other 1-byte forms.
+  constexpr bool QW = I8 && TOKSC && D == 128;
   const int tnew = n - 1;
-  const bool owns_new = !I8 && !pre && new_k != nullptr && tnew >= cz.write_from && tnew >= t_begin &&
+  const bool owns_new = (!I8 || QW) && !pre && new_k != nullptr && tnew >= cz.write_from && tnew >= t_begin &&
                         tnew < t_end && (TS == 1 || ((tnew >> 4) - (t_begin >> 4)) % TS == wv);  // wave-uniform
   u32x4_t nk = {0u, 0u, 0u, 0u}, nv = {0u, 0u, 0u, 0u};
+  float nks = 1.f, nvs = 1.f;
   if (owns_new) {
-    const size_t src = ((size_t)s * Hkv + g) * ROW;
-    if (c < CPR) nk = *(const u32x4_t*)(new_k + src + (size_t)c * 16);
-    if constexpr (R8) {
-      const u32x2_t w = *(const u32x2_t*)(new_v + src + (size_t)c * 8);
-      nv = u32x4_t{w[0], w[1], 0u, 0u};
+    if constexpr (QW) {
+      const size_t src = ((size_t)s * Hkv + g) * (D * 2);  // bf16 rows
+      const u32x2_t kc = quant_row8<KV == kKvFp8>(*(const u32x4_t*)(new_k + src + (size_t)c * 16), nks);
+      const u32x2_t vc = quant_row8<KV == kKvFp8>(*(const u32x4_t*)(new_v + src + (size_t)c * 16), nvs);
+      // a K chunk of the LDS tile is 16 codes: lane 2m holds chunk m, its
+      // own 8 codes then lane 2m + 1's
+      nk = u32x4_t{kc[0], kc[1], (unsigned)__shfl_xor((int)kc[0], 1, 64), (unsigned)__shfl_xor((int)kc[1], 1, 64)};
+      nv = u32x4_t{vc[0], vc[1], 0u, 0u};
     } else {
-      nv = *(const u32x4_t*)(new_v + src + (size_t)c * 16);
+      const size_t src = ((size_t)s * Hkv + g) * ROW;
+      if (c < CPR) nk = *(const u32x4_t*)(new_k + src + (size_t)c * 16);
+      if constexpr (R8) {
+        const u32x2_t w = *(const u32x2_t*)(new_v + src + (size_t)c * 8);
+        nv = u32x4_t{w[0], w[1], 0u, 0u};
+      } else {
+        nv = *(const u32x4_t*)(new_v + src + (size_t)c * 16);
+      }
     }
   }
   // K goes through a per-wave LDS tile of 16 rows of 16 B chunks (16 per
@@ -770,10 +818,11 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
 
   // FULL: every token of the tile is in the pool and visible to every
   // existing column (no mask; the scores, and so the reference, are finite).
-  auto compute = [&](auto full_tag, MfmaTile<RB>& T, int ti, bool ok, const Sc& ks, const Sc& vs) {
+  auto compute = [&](auto full_tag, MfmaTile<RB>& T, int ti, bool ok, const Sc& ks_in, const Sc& vs_in) {
     constexpr bool FULL = decltype(full_tag)::value;
     const bool new_tile = owns_new && ti == (tnew >> 4);  // wave-uniform
     const int rnew = tnew & 15;
+    Sc ks = ks_in, vs = vs_in;
 #pragma unroll
     for (int i = 0; i < RB / 64; ++i) ktile[kw[i]] = T.k[i];
     if (!I8 && new_tile) {
@@ -781,6 +830,19 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (4 * j + i == rnew) T.v[i] = nv;
+    }
+    if constexpr (QW) {
+      if (new_tile) {
+        if (j == 0 && (c & 1) == 0) ktile[rnew * CPR + ((c >> 1) ^ (rnew & (CPR - 1)))] = nk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (4 * j + i == rnew) {
+            T.v[i] = nv;
+            ks[i] = nks;
+            vs[i] = nvs;
+          }
+        }
+      }
     }
     // ---- scores, one MFMA chain per column group over the same K operands
     bf16x8_t ka[KK];
@@ -960,9 +1022,19 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
     const int b = e < 64 ? __builtin_amdgcn_readlane(tbl0, e) : __builtin_amdgcn_readlane(tbl1, e - 64);
     if (b >= 0 && b < NB) {
       const size_t dst = ((size_t)b * Hkv + g) * head_stride + (size_t)(tnew % BS) * ROW;
-      if (c < CPR) *(u32x4_t*)(k_cache + dst + (size_t)c * 16) = nk;
-      if constexpr (R8) *(u32x2_t*)(v_cache + dst + (size_t)c * 8) = u32x2_t{nv[0], nv[1]};
-      else *(u32x4_t*)(v_cache + dst + (size_t)c * 16) = nv;
+      if constexpr (QW) {
+        *(u32x2_t*)(k_cache + dst + (size_t)c * 8) = u32x2_t{nk[0], nk[1]};
+        *(u32x2_t*)(v_cache + dst + (size_t)c * 8) = u32x2_t{nv[0], nv[1]};
+        if (c == 0) {
+          const size_t si = ((size_t)b * Hkv + g) * BS + (size_t)(tnew % BS);
+          k_scales[si] = nks;
+          v_scales[si] = nvs;
+        }
+      } else {
+        if (c < CPR) *(u32x4_t*)(k_cache + dst + (size_t)c * 16) = nk;
+        if constexpr (R8) *(u32x2_t*)(v_cache + dst + (size_t)c * 8) = u32x2_t{nv[0], nv[1]};
+        else *(u32x4_t*)(v_cache + dst + (size_t)c * 16) = nv;
+      }
     }
   }
 
@@ -1812,7 +1884,8 @@ pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipSt
   hipLaunchKernelGGL((decode_mfma_kernel<KV, BS, TOKSC, NCG, MODE, WG, D>), dim3((unsigned)items), dim3(64 * WG), \
                      0, st,                                                                                    \
                      (float*)a->out, ws, (const unsigned short*)a->q, (char*)a->k_cache, (char*)a->v_cache,      \
-                     a->k_scales, a->v_scales, a->block_tables, a->max_blocks_per_seq, a->context_lens,        \
+                     const_cast<float*>(a->k_scales), const_cast<float*>(a->v_scales), a->block_tables,        \
+                     a->max_blocks_per_seq, a->context_lens,                                                   \
                      a->num_q_heads, a->num_kv_heads, p.G, a->num_blocks, qk, p.partition_tokens,              \
                      p.num_partitions, (const char*)a->new_key, (const char*)a->new_value,                     \
                      a->query_start_loc, cgw, a->query_start_loc ? a->num_queries : a->num_seqs, cz, bz)

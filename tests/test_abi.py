@@ -291,6 +291,15 @@ def test_fused_write_argument_checks():
     assert lib.pa_decode(ctypes.byref(a)) == pa.PA_ERR_INVALID
     a = _cpu_args(new_key=0x20000, new_value=0x30000, kv_dtype=pa.PA_I8, k_scales=64, v_scales=64)
     assert lib.pa_decode(ctypes.byref(a)) == pa.PA_ERR_UNSUPPORTED
+    # into a 1-byte cache only with per-token scales, head_dim 128 and the
+    # matrix-core kernel (the write quantises bf16 rows in the kernel)
+    quant = dict(new_key=0x20000, new_value=0x30000, k_scales=64, v_scales=64, kv_scale_mode=pa.PA_SCALE_TOKEN)
+    for kv in (pa.PA_I8, pa.PA_FP8_E4M3):
+        assert _ws(_cpu_args(kv_dtype=kv, **quant))[0] == pa.PA_OK
+        for bad in (dict(head_dim=64), dict(kernel=pa.KERNEL_VALU), dict(q_dtype=pa.PA_F32)):
+            st, _ = _ws(_cpu_args(kv_dtype=kv, **quant, **bad))
+            assert st == pa.PA_ERR_UNSUPPORTED, bad
+            assert "fused write into a quantised cache" in lib.pa_last_error().decode()
 
 
 def test_zero_sequences_is_a_no_op():

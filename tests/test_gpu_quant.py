@@ -167,6 +167,68 @@ def test_nan_scales_outside_the_context_are_never_used(kvd, mode, D):
             assert err <= TOL_BF16, (kvd, mode, D, rows, P, err)
 
 
+def _fused_cases(kvd):
+    """A skewed batch (the balanced split with the length hint) and a short
+    one of 32 sequences x 8 kv heads (grouped launches)."""
+    rng = np.random.default_rng(21)
+    skewed = [1, 2, 15, 16, 17, 31, 32, 33, 255, 256, 257] + [int(x) for x in rng.integers(1, 1500, size=28)] + [12000]
+    short = [1, 16, 17, 64, 65, 127, 128, 129] + [int(x) for x in rng.integers(1, 1200, size=23)] + [1200]
+    for name, lens in (("skewed", skewed), ("short", short)):
+        case = synth.make_case("fused-q-" + name, 390 + len(lens), lens, 32, 8, 128, 16, kv_dtype=kvd, free_frac=0.1)
+        quantize_case_by_token(case, pa.PA_SCALE_TOKEN)
+        yield name, case
+
+
+@pytest.mark.parametrize("kvd", [synth.I8, synth.FP8])
+def test_fused_quantising_write(kvd):
+    """pa_decode with new_key/new_value (bf16 rows) on a 1-byte cache with
+    per-token scales quantises and stores every sequence's newest token
+    and attends with it: codes and scales bit for bit those of the oracle's
+    quantising write (and of pa_quantize_and_cache), outputs bit for bit
+    those of pa_quantize_and_cache + pa_decode and within tolerance of the
+    oracle after its write.  Rows include all-zero ones (scale 1) and a key
+    outlier; plain, many-partition, balanced and grouped launches."""
+    for name, case in _fused_cases(kvd):
+        S, Hkv, D, BS = case.num_seqs, case.num_kv_heads, case.head_dim, case.block_size
+        rng = np.random.default_rng(31)
+        # rows of unit-order spread (the 2e-3 gate is absolute), one all
+        # zero, one key row with an outlier that sets its scale
+        kf = (rng.standard_normal((S, Hkv, D)) * rng.uniform(0.05, 4.0, (S, Hkv, 1))).astype(np.float32)
+        vf = (rng.standard_normal((S, Hkv, D)) * rng.uniform(0.05, 2.0, (S, Hkv, 1))).astype(np.float32)
+        kf[0, 0] = 0.0
+        vf[2, 1] = 0.0
+        kf[1, -1, :3] = [300.0, -300.0, 0.5]
+        nk, nv = synth.bf16_bits(kf), synth.bf16_bits(vf)
+        slots = oracle.slot_mapping(case.block_tables, case.context_lens - 1, BS)
+        exp_k, exp_v = case.k_cache.copy(), case.v_cache.copy()
+        exp_ks, exp_vs = case.k_scales.copy(), case.v_scales.copy()
+        oracle.quantize_and_cache(nk, nv, exp_k, exp_v, exp_ks, exp_vs, slots, pa.PA_SCALE_TOKEN, 0.0, 0.0)
+        expect = oracle.paged_decode(case.q, exp_k, exp_v, case.block_tables, case.context_lens, float(case.scale),
+                                     exp_ks, exp_vs, scale_mode=pa.PA_SCALE_TOKEN)
+        dnk, dnv = to_dev(nk), to_dev(nv)
+        total = int(np.sum(case.context_lens, dtype=np.int64))
+        for P, hint in ((0, False), (16, False), (0, True), (256, False)):
+            say("fused quantising write", kvd, name, "partition", P, "hint", hint)
+            kw = dict(partition_tokens=P, total_context_len=total if hint else 0)
+            a = case_on_device(case)
+            sl = pa.slot_mapping(a["bt"], BS, context_lens=a["cl"])
+            pa.quantize_and_cache(dnk, dnv, a["k"], a["v"], a["ks"], a["vs"], sl)
+            out_a = pa.decode(a["q"], a["k"], a["v"], a["bt"], a["cl"], float(case.scale), case.max_context_len,
+                              k_scales=a["ks"], v_scales=a["vs"], **kw)
+            b = case_on_device(case)
+            out_b = pa.decode(b["q"], b["k"], b["v"], b["bt"], b["cl"], float(case.scale), case.max_context_len,
+                              k_scales=b["ks"], v_scales=b["vs"], new_key=dnk, new_value=dnv, **kw)
+            torch.cuda.synchronize()
+            for key in ("k", "v", "ks", "vs"):
+                assert np.array_equal(to_host(b[key]), to_host(a[key])), (name, P, hint, key)
+            assert np.array_equal(to_host(b["k"]), exp_k) and np.array_equal(to_host(b["v"]), exp_v)
+            assert np.array_equal(to_host(b["ks"]), exp_ks) and np.array_equal(to_host(b["vs"]), exp_vs)
+            ob = out_b.cpu().numpy().astype(np.float64)
+            assert np.array_equal(out_a.cpu().numpy().astype(np.float64), ob), (name, P, hint)
+            err = max_err(ob, expect)
+            assert err <= TOL_BF16, (kvd, name, P, hint, err)
+
+
 @pytest.mark.parametrize("kvd", [synth.I8, synth.FP8])
 def test_config5_per_token_scales(kvd):
     """The int8 workload's batch (64 sequences, log-normal lengths) with
