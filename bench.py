@@ -106,8 +106,8 @@ def cpu_model() -> str:
 # (profiles/decode_mfma_llama3-70b_pmc_traffic.md).  Valid only for the
 # sources the counters were taken on: a changed kernel or plan reports null.
 PMC_TRAFFIC = {
-    "sources_sha256": "29a264a9948dfcbbee370021c62d1d1ead04d5b91c5cc9118e49417f8fa4ca6a",
-    "fetch_kib": 320889.90625 + 1388.5,
+    "sources_sha256": "36c059ca4daefa901ff7abf2f5fbc1d83ae651e455c22811893b3755b51145b5",
+    "fetch_kib": 320865.59375 + 1388.5,
     "write_kib": 2680.0 + 640.0,
     "fetch_factor": 1.99227,
     "write_factor": 1.0,
