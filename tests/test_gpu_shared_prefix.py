@@ -149,3 +149,35 @@ def test_fused_write_inside_the_prefix_is_skipped(kernel):
     assert np.array_equal(to_host(dev["v"]), case.v_cache)
     err = max_err(got, run_oracle(case))
     assert err <= TOL_BF16, err
+
+
+@pytest.mark.parametrize("kv", [synth.I8, synth.FP8])
+def test_fused_quantising_write_with_a_shared_prefix(kv):
+    """The fused write into a per-token-scaled 1-byte cache with a shared
+    prefix: sequences whose newest token lies past the prefix get its codes
+    and scales (bit for bit the oracle's quantising write) and attend with
+    them; a newest token inside the prefix is neither stored nor taken from
+    the new rows."""
+    pb, BS = 4, 32
+    L = pb * BS
+    lens = [L + 300, L - 7, L, L + 1, L + 40, L + 129, 1 + L + 31]
+    case = _shared_case("prefix_qwrite", 61, lens, 32, 8, BS, pb, kv_dtype=kv)
+    quantize_case_by_token(case, pa.PA_SCALE_TOKEN)
+    S, Hkv = case.num_seqs, case.num_kv_heads
+    rng = np.random.default_rng(10)
+    k_new = synth.bf16_bits(rng.standard_normal((S, Hkv, 128), dtype=np.float32))
+    v_new = synth.bf16_bits(rng.standard_normal((S, Hkv, 128), dtype=np.float32))
+    written = [i for i, n in enumerate(lens) if n > L]
+    slots = oracle.slot_mapping(case.block_tables[written], case.context_lens[written] - 1, BS)
+    exp = [a.copy() for a in (case.k_cache, case.v_cache, case.k_scales, case.v_scales)]
+    oracle.quantize_and_cache(k_new[written], v_new[written], *exp, slots, pa.PA_SCALE_TOKEN, 0.0, 0.0)
+    expect = oracle.paged_decode(case.q, exp[0], exp[1], case.block_tables, case.context_lens, float(case.scale),
+                                 exp[2], exp[3], scale_mode=pa.PA_SCALE_TOKEN)
+    for P in (0, 64):
+        dev = case_on_device(case)
+        say("fused quantising write with a shared prefix", kv, "partition", P)
+        got = _run(case, dev, pb, P, new=(to_dev(k_new), to_dev(v_new)))
+        for key, want in zip(("k", "v", "ks", "vs"), exp):
+            assert np.array_equal(to_host(dev[key]), want), (kv, P, key)
+        err = max_err(got, expect)
+        assert err <= TOL_BF16, (kv, P, err)
