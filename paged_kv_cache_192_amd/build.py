@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import glob
+import re
 import os
 import subprocess
 import sys
@@ -35,10 +36,26 @@ COMMON = [
 ]
 
 
+def _scratch_users(remarks: str) -> list:
+    """Kernels that spill vector registers or use scratch memory, from the
+    compiler's kernel-resource-usage remarks."""
+    bad, cur = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            continue
+        m = re.search(r"(VGPRs Spill|ScratchSize \[bytes/lane\]): (\d+)", line)
+        if m and cur and int(m.group(2)) > 0:
+            bad.append("%s: %s %s" % (cur, m.group(1), m.group(2)))
+    return bad
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [HIPCC] + COMMON + ["-c", src, "-o", obj]
-    if verbose:
+    device = src.endswith(".hip")
+    if device:
         cmd += ["-Rpass-analysis=kernel-resource-usage"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(line for line in (res.stdout + res.stderr).splitlines()
@@ -47,6 +64,11 @@ def _compile(src: str, verbose: bool) -> str:
         raise RuntimeError("compile failed: %s\n%s" % (" ".join(cmd), out))
     if verbose and out.strip():
         print(out)
+    # every kernel keeps its working set in registers: a spill or a stack
+    # array in scratch memory would cost far more than it saves
+    bad = _scratch_users(out) if device else []
+    if bad:
+        raise RuntimeError("kernels in %s use scratch memory:\n  %s" % (os.path.basename(src), "\n  ".join(bad)))
     return obj
 
 

@@ -718,7 +718,8 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
   // pa_quantize_and_cache would: lane c codes d = 8c .. 8c+7 of each row
   // (the same in every 16-lane row), and the new token's scales stand in
   // for the ones in its slot.  The host rejects the other 1-byte forms.
-  constexpr bool QW = I8 && TOKSC && D == 128;
+  // (never with several query rows: the host rejects a fused write there)
+  constexpr bool QW = I8 && TOKSC && D == 128 && !MQ;
   const int tnew = n - 1;
   const bool owns_new = (!I8 || QW) && !pre && new_k != nullptr && tnew >= cz.write_from && tnew >= t_begin &&
                         tnew < t_end && (TS == 1 || ((tnew >> 4) - (t_begin >> 4)) % TS == wv);  // wave-uniform

@@ -501,3 +501,18 @@ def test_wide_query_groups_are_planned_as_column_groups():
     assert st == pa.PA_OK
     st2, n2 = _ws(_cpu_args(total_context_len=20000, shared_prefix_table=0x40000, shared_prefix_len=160, **big))
     assert st2 == pa.PA_OK and n2 == n
+
+
+def test_build_flags_kernels_that_use_scratch():
+    """The build fails when a kernel spills vector registers or keeps an
+    array in scratch memory (read from the compiler's resource remarks)."""
+    from paged_kv_cache_192_amd import build
+    ok = ("x.hip:1:1: remark: Function Name: _Z1kv [-Rpass-analysis=kernel-resource-usage]\n"
+          "x.hip:1:1: remark:     VGPRs: 120 [-Rpass-analysis=kernel-resource-usage]\n"
+          "x.hip:1:1: remark:     VGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]\n"
+          "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]\n")
+    assert build._scratch_users(ok) == []
+    bad = ok.replace("ScratchSize [bytes/lane]: 0", "ScratchSize [bytes/lane]: 880")
+    assert build._scratch_users(bad) == ["_Z1kv: ScratchSize [bytes/lane] 880"]
+    spill = ok.replace("VGPRs Spill: 0", "VGPRs Spill: 12")
+    assert build._scratch_users(spill) == ["_Z1kv: VGPRs Spill 12"]
