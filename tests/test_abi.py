@@ -516,3 +516,23 @@ def test_build_flags_kernels_that_use_scratch():
     assert build._scratch_users(bad) == ["_Z1kv: ScratchSize [bytes/lane] 880"]
     spill = ok.replace("VGPRs Spill: 0", "VGPRs Spill: 12")
     assert build._scratch_users(spill) == ["_Z1kv: VGPRs Spill 12"]
+
+
+def test_binding_checks_new_rows_dtype():
+    """new_key/new_value hold the cache's element type for a bf16 or fp32
+    cache, and bf16 rows (quantised by the call) for an int8 or E4M3 cache."""
+    S, Hq, Hkv, D, BS, NB, MB = 3, 8, 2, 128, 16, 40, 10
+    q = torch.zeros(S, Hq, D, dtype=torch.bfloat16)
+    bt = torch.zeros(S, MB, dtype=torch.int32)
+    cl = torch.zeros(S, dtype=torch.int32)
+    rows = {dt: torch.zeros(S, Hkv, D, dtype=dt) for dt in (torch.bfloat16, torch.float32)}
+    for cache_dt, good, bad in ((torch.bfloat16, torch.bfloat16, torch.float32),
+                                (torch.int8, torch.bfloat16, torch.float32)):
+        kc = torch.zeros(NB, Hkv, BS, D, dtype=cache_dt)
+        sc = {} if cache_dt == torch.bfloat16 else dict(k_scales=torch.zeros(NB, Hkv, BS),
+                                                        v_scales=torch.zeros(NB, Hkv, BS))
+        pa.make_decode_args(q, kc, kc, bt, cl, 0.125, 100, new_key=rows[good], new_value=rows[good],
+                            device_pointers=False, **sc)
+        with pytest.raises(ValueError):
+            pa.make_decode_args(q, kc, kc, bt, cl, 0.125, 100, new_key=rows[bad], new_value=rows[bad],
+                                device_pointers=False, **sc)
