@@ -2,13 +2,14 @@
 
 Each case draws a shape, a length distribution, a cache dtype and scale
 layout, a length hint (exact, too small, too large or none), a partition
-size, the kernel, and optionally a shared prefix and the fused cache write,
+size, the kernel, and optionally a shared prefix and the fused cache write
+(into a per-token-scaled 1-byte cache too, quantising in the kernel),
 so that the partition plans (near-equal, ragged, balanced, shared prefix,
 given partitions, vector-ALU) meet in combinations the targeted tests do
 not list.  The oracle knows nothing of plans or prefixes: each result must
 be the attention over the sequence's table.  max |gpu - oracle| <= 2e-3
 (bf16 or 1-byte inputs) or 1e-5 (fp32 q and cache); the fused write
-bit-exact over the whole pool."""
+bit-exact over the whole pool, codes and scales included."""
 import math
 
 import numpy as np
@@ -22,7 +23,7 @@ from gpu_helpers import case_on_device, max_err, quantize_case_by_token, say, to
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 40
+N_CASES = 60
 MAX_TOKENS = 30000          # per case, all sequences (keeps the oracle and host copies small)
 
 # (Hq, Hkv, D)
@@ -70,7 +71,9 @@ def _draw(seed):
         lens[0] = max(int(lens[0]), prefix_blocks * BS)
     P = 0 if rng.random() < 0.7 else 16 * int(rng.integers(1, 8 * BS // 16 + 1))
     scale_mode = int(rng.choice([pa.PA_SCALE_BLOCK, pa.PA_SCALE_TOKEN]))
-    fused = kv_dt in (synth.BF16, synth.F32) and rng.random() < 0.4
+    quant_fused_ok = (kv_dt in (synth.I8, synth.FP8) and D == 128 and kernel == pa.KERNEL_AUTO
+                      and scale_mode == pa.PA_SCALE_TOKEN)
+    fused = (kv_dt in (synth.BF16, synth.F32) or quant_fused_ok) and rng.random() < (0.8 if quant_fused_ok else 0.4)
     hint_kind = str(rng.choice(["exact", "exact", "exact", "under", "over", "none"]))
     return dict(seed=seed, Hq=Hq, Hkv=Hkv, D=D, BS=BS, q_dt=q_dt, kv_dt=kv_dt, S=S, kind=kind, lens=lens,
                 kernel=kernel, prefix_blocks=prefix_blocks, P=P, scale_mode=scale_mode, fused=fused,
@@ -99,7 +102,7 @@ def test_random_plan(seed):
     if c["fused"]:
         rng = np.random.default_rng(3000 + seed)
         rows = rng.standard_normal((2, S, c["Hkv"], c["D"]), dtype=np.float32)
-        new = [synth.bf16_bits(r) if c["kv_dt"] == synth.BF16 else r for r in rows]
+        new = [r if c["kv_dt"] == synth.F32 else synth.bf16_bits(r) for r in rows]
     table = to_dev(np.ascontiguousarray(case.block_tables[0, :pb])) if pb else None
     out = pa.decode(dev["q"], dev["k"], dev["v"], dev["bt"], dev["cl"], float(case.scale), mcl, k_scales=dev["ks"],
                     v_scales=dev["vs"], partition_tokens=c["P"], kernel=c["kernel"], total_context_len=hint,
@@ -111,12 +114,20 @@ def test_random_plan(seed):
         # every sequence's newest token is written, except (with a shared
         # prefix on the matrix-core kernel) those inside the prefix
         written = np.nonzero((lens >= 1) & (lens > pb * BS if pb else True))[0]
+        quant = c["kv_dt"] in (synth.I8, synth.FP8)
         if len(written):
             slots = oracle.slot_mapping(case.block_tables[written], lens[written] - 1, BS)
-            oracle.reshape_and_cache(new[0][written], new[1][written], case.k_cache, case.v_cache, slots)
+            if quant:
+                oracle.quantize_and_cache(new[0][written], new[1][written], case.k_cache, case.v_cache,
+                                          case.k_scales, case.v_scales, slots, pa.PA_SCALE_TOKEN, 0.0, 0.0)
+            else:
+                oracle.reshape_and_cache(new[0][written], new[1][written], case.k_cache, case.v_cache, slots)
         # byte for byte: unused fp32 slots hold NaN poison
         assert np.array_equal(to_host(dev["k"]).view(np.uint8), case.k_cache.view(np.uint8))
         assert np.array_equal(to_host(dev["v"]).view(np.uint8), case.v_cache.view(np.uint8))
+        if quant:
+            assert np.array_equal(to_host(dev["ks"]).view(np.uint8), case.k_scales.view(np.uint8))
+            assert np.array_equal(to_host(dev["vs"]).view(np.uint8), case.v_scales.view(np.uint8))
     expect = oracle.paged_decode(case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens,
                                  float(case.scale), case.k_scales, case.v_scales, scale_mode=mode)
     err = max_err(got, expect)
