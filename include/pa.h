@@ -119,7 +119,7 @@ int32_t pa_abi_version(void);
  *                 every row must be allocated in full
  *   context_lens  [num_seqs] int32, 0 <= n <= max_blocks_per_seq * BS and
  *                 n <= max_context_len
- *   out           [num_seqs][num_q_heads][head_dim] fp32
+ *   out           [num_seqs][num_q_heads][head_dim] fp32, or bf16
  * Slots at or beyond n inside a sequence's last block, and blocks no table
  * names, are never read: they (and their scales) may hold anything, NaN
  * included.
@@ -127,7 +127,10 @@ int32_t pa_abi_version(void);
  * Supported: head_dim in {64, 128}; block_size in {16, 32};
  * q_dtype in {PA_F32, PA_BF16}; kv_dtype in {PA_F32, PA_BF16, PA_I8,
  * PA_FP8_E4M3};
- * out_dtype PA_F32; num_q_heads a multiple of num_kv_heads (any number of
+ * out_dtype PA_F32 or PA_BF16 (the fp32 result rounded to nearest even
+ * by one more pass over it, which takes num_seqs * num_q_heads * head_dim
+ * fp32 of workspace; fp32 is the direct form); num_q_heads a multiple of
+ * num_kv_heads (any number of
  * query heads per kv head: the matrix-core kernel takes them 16 at a time,
  * two groups of 16 per wave).  All of q, caches and out 16-byte aligned.
  *

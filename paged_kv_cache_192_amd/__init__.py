@@ -288,7 +288,8 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, max_co
            stream=None, new_key=None, new_value=None, total_context_len: int = 0, query_start_loc=None,
            max_query_len: int = 0, shared_prefix_table=None, shared_prefix_len: int = 0):
     """Paged decode attention (``pa_decode``).  Returns ``out`` (float32
-    ``[S][Hq][D]``), allocated on q's device when not given.  A workspace
+    ``[S][Hq][D]``, allocated on q's device when not given, or the
+    bfloat16 tensor passed: the fp32 result rounded).  A workspace
     is allocated when the plan needs one and none is passed (its contents
     are scratch of the call)."""
     torch = _torch()

@@ -92,7 +92,8 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* p) {
     return fail(PA_ERR_INVALID, "pa_decode: block_size %d not in {16, 32}", a->block_size);
   if (!valid_dtype(a->q_dtype) || !valid_dtype(a->kv_dtype) || !valid_dtype(a->out_dtype))
     return fail(PA_ERR_INVALID, "pa_decode: unknown dtype code");
-  if (a->out_dtype != PA_F32) return fail(PA_ERR_UNSUPPORTED, "pa_decode: out_dtype must be PA_F32");
+  if (a->out_dtype != PA_F32 && a->out_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: out_dtype must be PA_F32 or PA_BF16");
   if (quantised(a->q_dtype)) return fail(PA_ERR_UNSUPPORTED, "pa_decode: quantised queries");
   const bool i8 = quantised(a->kv_dtype);  // 1-byte codes with scales
   if (i8 != (a->k_scales != nullptr) || i8 != (a->v_scales != nullptr))
@@ -412,9 +413,18 @@ pa_status pa_decode(const pa_decode_args* a) {
   }
   hipStream_t st = (hipStream_t)a->stream;
   if (debug_enabled() && (s = debug_check_decode(a, st)) != PA_OK) return s;
-  s = p.kind == KERNEL_MFMA ? launch_decode_mfma(a, p, st) : launch_decode_valu(a, p, st);
-  if (s != PA_OK || p.ws_partitions == 1) return s;
-  return launch_decode_merge(a, p, st);
+  // a bf16 output: the kernels write the fp32 rows into the workspace, and
+  // one more pass rounds them into out
+  pa_decode_args f = *a;
+  if (a->out_dtype == PA_BF16) {
+    f.out = (char*)a->workspace + workspace_layout(a, p).out_offset;
+    f.out_dtype = PA_F32;
+  }
+  s = p.kind == KERNEL_MFMA ? launch_decode_mfma(&f, p, st) : launch_decode_valu(&f, p, st);
+  if (s == PA_OK && p.ws_partitions > 1) s = launch_decode_merge(&f, p, st);
+  if (s == PA_OK && a->out_dtype == PA_BF16)
+    s = launch_f32_to_bf16((const float*)f.out, a->out, (size_t)p.rows * a->head_dim, st);
+  return s;
 }
 
 pa_status pa_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,

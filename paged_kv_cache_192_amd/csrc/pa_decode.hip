@@ -2006,6 +2006,24 @@ static void merge_dispatch(const pa_decode_args* a, const DecodePlan& p, hipStre
 #undef PA_MERGE_LAUNCH
 }
 
+// fp32 -> bf16 (round to nearest even), four values per thread
+__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float4* __restrict__ in, u32x2_t* __restrict__ out,
+                                                          size_t n4) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const float4 v = in[i];
+  out[i] = u32x2_t{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+}
+
+pa_status launch_f32_to_bf16(const float* in, void* out, size_t n, hipStream_t st) {
+  const size_t n4 = n / 4;
+  if (n4 == 0) return PA_OK;
+  hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, (const float4*)in,
+                     (u32x2_t*)out, n4);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PA_OK : hip_fail(e, "pa_decode (bf16 output) launch");
+}
+
 pa_status launch_decode_merge(const pa_decode_args* a, const DecodePlan& p, hipStream_t st) {
   const size_t rows = (size_t)p.rows;
   if (rows == 0) return PA_OK;

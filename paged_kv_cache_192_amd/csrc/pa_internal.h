@@ -123,26 +123,34 @@ pa_status plan_decode(const pa_decode_args* a, DecodePlan* plan);
 // Every entry a merge reads is written by the same call, so the workspace
 // needs no initialisation.
 struct WorkspaceLayout {
-  size_t ml_offset, acc_offset, counts_offset, bytes;
+  size_t ml_offset, acc_offset, counts_offset, out_offset, bytes;
 };
 
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 inline WorkspaceLayout workspace_layout(const pa_decode_args* a, const DecodePlan& p) {
-  WorkspaceLayout L{0, 0, 0, 0};
-  if (p.ws_partitions <= 1) return L;
-  const size_t rows = (size_t)p.rows * p.ws_partitions;
-  L.ml_offset = 0;
-  L.acc_offset = align256(rows * 2 * sizeof(float));
-  L.counts_offset = L.acc_offset + align256(rows * a->head_dim * sizeof(float));
-  // balanced split: partials per sequence, int32 [num_seqs]
-  L.bytes = L.counts_offset + (p.balanced ? align256((size_t)a->num_seqs * sizeof(int32_t)) : 0);
+  WorkspaceLayout L{0, 0, 0, 0, 0};
+  if (p.ws_partitions > 1) {
+    const size_t rows = (size_t)p.rows * p.ws_partitions;
+    L.ml_offset = 0;
+    L.acc_offset = align256(rows * 2 * sizeof(float));
+    L.counts_offset = L.acc_offset + align256(rows * a->head_dim * sizeof(float));
+    // balanced split: partials per sequence, int32 [num_seqs]
+    L.bytes = L.counts_offset + (p.balanced ? align256((size_t)a->num_seqs * sizeof(int32_t)) : 0);
+  }
+  // a bf16 output: the fp32 result rows, rounded into out by a last pass
+  if (a->out_dtype == PA_BF16) {
+    L.out_offset = L.bytes;
+    L.bytes += align256((size_t)p.rows * a->head_dim * sizeof(float));
+  }
   return L;
 }
 
 pa_status launch_decode_mfma(const pa_decode_args* a, const DecodePlan& p, hipStream_t st);
 pa_status launch_decode_valu(const pa_decode_args* a, const DecodePlan& p, hipStream_t st);
 pa_status launch_decode_merge(const pa_decode_args* a, const DecodePlan& p, hipStream_t st);
+// n fp32 values -> bf16, round to nearest even (n a multiple of 4)
+pa_status launch_f32_to_bf16(const float* in, void* out, size_t n, hipStream_t st);
 
 pa_status launch_slot_mapping(const int32_t* block_tables, int32_t max_blocks, int32_t num_seqs, const int32_t* seq_idx,
                               const int32_t* positions, const int32_t* context_lens, int32_t T,

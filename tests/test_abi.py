@@ -98,6 +98,12 @@ def test_struct_layout_and_workspace_size():
     # one partition: no workspace
     st, n = _ws(_cpu_args(partition_tokens=128))
     assert st == pa.PA_OK and n == 0
+    # a bf16 output adds the fp32 result rows (3 x 8 rows of 128) after the
+    # partials, or alone
+    st, n = _ws(_cpu_args(partition_tokens=128, out_dtype=pa.PA_BF16))
+    assert st == pa.PA_OK and n == al(3 * 8 * 128 * 4)
+    st, n = _ws(_cpu_args(out_dtype=pa.PA_BF16))
+    assert st == pa.PA_OK and n == al(rows * 8) + al(rows * 128 * 4) + al(3 * 8 * 128 * 4)
     # distinctive values reach the right fields
     st, _ = _ws(_cpu_args(head_dim=96))
     assert st == pa.PA_ERR_INVALID and "head_dim 96" in pa.library().pa_last_error().decode()
@@ -187,7 +193,7 @@ def test_balanced_split_up_to_1024_sequences():
     ("num_q_heads", 0, pa.PA_ERR_INVALID),
     ("head_dim", 256, pa.PA_ERR_INVALID),
     ("block_size", 8, pa.PA_ERR_INVALID),
-    ("out_dtype", pa.PA_BF16, pa.PA_ERR_UNSUPPORTED),
+    ("out_dtype", pa.PA_I8, pa.PA_ERR_UNSUPPORTED),
     ("q_dtype", pa.PA_I8, pa.PA_ERR_UNSUPPORTED),
     ("kv_dtype", 7, pa.PA_ERR_INVALID),
     ("kv_dtype", pa.PA_I8, pa.PA_ERR_INVALID),        # int8 without scales
