@@ -106,10 +106,10 @@ def cpu_model() -> str:
 # (profiles/decode_mfma_llama3-70b_pmc_traffic.md).  Valid only for the
 # sources the counters were taken on: a changed kernel or plan reports null.
 PMC_TRAFFIC = {
-    "sources_sha256": "3d4d997c751148c02a273daec303470227b0ca801684b4f6237d76741a971861",
-    "fetch_kib": 320877.40625 + 1391.0,
-    "write_kib": 2680.046875 + 640.0,
-    "fetch_factor": 1.99226,
+    "sources_sha256": "c5459350c97ea4207d25e87d93a4a459b75acfc845b4740a5e8b28106e7fde5d",
+    "fetch_kib": 320872.65625 + 1391.0,
+    "write_kib": 2680.0625 + 640.0,
+    "fetch_factor": 1.99227,
     "write_factor": 1.0,
 }
 PMC_SOURCES = ("paged_kv_cache_192_amd/csrc/pa_decode.hip", "paged_kv_cache_192_amd/csrc/pa_api.cpp",
