@@ -232,15 +232,16 @@ def run(args) -> dict:
         else:
             eager_step()
 
-    # replays must reproduce the eager result bit for bit
+    # replays must reproduce the eager result bit for bit (checked before the
+    # warmup, so that the warmup runs straight into the timed region)
     eager_step()
     torch.cuda.synchronize()
     ref = torch.stack(outs).clone()
-    for _ in range(args.warmup):
-        step()
+    step()
     torch.cuda.synchronize()
     if not torch.equal(torch.stack(outs), ref):
         raise RuntimeError("graph replay differs from the eager step")
+    warm_run = warm_up(step, args.warmup, args.warmup_ms)
 
     # timed region: exactly `steps` steps between two synchronisations; an
     # event pair around each step gives the per-step distribution (events
@@ -294,6 +295,7 @@ def run(args) -> dict:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_run,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -435,11 +437,11 @@ def run_single_layer(args) -> dict:
         for f in gcalls:
             f()
     torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        graph.replay()
+    graph.replay()
     torch.cuda.synchronize()
     if not torch.equal(torch.stack(outs), ref):
         raise RuntimeError("graph replay differs from the eager step")
+    warm_run = warm_up(graph.replay, args.warmup, args.warmup_ms)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
@@ -451,7 +453,7 @@ def run_single_layer(args) -> dict:
     kvb = kv_bytes(cls, Hkv, D, e)
     alg = decode_algorithmic_bytes(cls, Hq, Hkv, D, BS, e, eq, int8_scales=(w == "int8"))
     res = {"workload": w, "description": WORKLOADS[w], "replicas": R, "partition_tokens": args.partition_tokens,
-           "kernel": args.kernel, "steps": args.steps, "warmup": args.warmup,
+           "kernel": args.kernel, "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": warm_run,
            "ms_per_layer": round(ms_layer, 5), "tokens_per_s": round(S / (ms_layer * 1e-3), 1),
            "kv_gbs": round(kvb / (ms_layer * 1e-3) / 1e9, 1),
            "pct_hbm_peak": round(100.0 * alg / (ms_layer * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
@@ -478,9 +480,32 @@ def run_single_layer(args) -> dict:
     return res
 
 
-def _timed_graph(prepare, steps: int, warmup: int, outs):
+def warm_up(step, warmup: int, min_ms: float) -> int:
+    """Untimed steps before a timed region: at least `warmup` of them and at
+    least `min_ms` of wall time, synchronising every few steps so that the
+    host does not run ahead of the device.  Returns the steps run.
+
+    The floor is there because the device's clocks settle under load: after
+    an idle gap of a few milliseconds the first ~30 ms of matrix-core work
+    run up to a quarter slower (replay times rise, then fall back), and a
+    handful of short steps ends inside that transient."""
+    import torch
+
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or (time.perf_counter() - t0) * 1e3 < min_ms:
+        step()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
+def _timed_graph(prepare, steps: int, warmup: int, outs, warmup_ms: float = 0.0):
     """Capture prepare()'s calls once as a graph, check one replay against
-    the eager result bit for bit, and return the mean replay time in ms."""
+    the eager result bit for bit, warm up, and return the mean replay time
+    in ms and the warmup replays run."""
     import torch
 
     main = torch.cuda.current_stream()
@@ -496,18 +521,18 @@ def _timed_graph(prepare, steps: int, warmup: int, outs):
         for f in gcalls:
             f()
     torch.cuda.synchronize()
-    for _ in range(warmup):
-        graph.replay()
+    graph.replay()
     torch.cuda.synchronize()
     if not all(torch.equal(a, b) for a, b in zip(outs, ref)):
         raise RuntimeError("graph replay differs from the eager step")
+    warm_run = warm_up(graph.replay, warmup, warmup_ms)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
         graph.replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    return e0.elapsed_time(e1) / steps, warm_run
 
 
 def run_next_workload(args) -> dict:
@@ -580,11 +605,13 @@ def run_next_workload(args) -> dict:
                                                new_key=newk if fused else None, new_value=newv if fused else None))
             return calls
 
-        ms = _timed_graph(prepare, args.steps, args.warmup, outs) / R
+        ms, warm_run = _timed_graph(prepare, args.steps, args.warmup, outs, args.warmup_ms)
+        ms /= R
         cls = case.context_lens
         alg = decode_algorithmic_bytes(cls, Hq, Hkv, D, BS, 1, 2, token_scales=True)
         kvb = kv_bytes(cls, Hkv, D, 1)
-        res.update({"replicas": R, "ms_per_layer": round(ms, 5), "tokens_per_s": round(S / (ms * 1e-3), 1),
+        res.update({"replicas": R, "warmup_steps_run": warm_run, "ms_per_layer": round(ms, 5),
+                    "tokens_per_s": round(S / (ms * 1e-3), 1),
                     "kv_gbs": round(kvb / (ms * 1e-3) / 1e9, 1),
                     "pct_hbm_peak": round(100.0 * alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                     "algorithmic_bytes_per_layer": alg, "sum_ctx": int(np.sum(cls)),
@@ -626,10 +653,12 @@ def run_next_workload(args) -> dict:
                                       new_key=newk, new_value=newv, partition_tokens=args.partition_tokens,
                                       kernel=args.kernel, total_context_len=total) for r in range(R)]
 
-        ms = _timed_graph(prepare, args.steps, args.warmup, outs) / R
+        ms, warm_run = _timed_graph(prepare, args.steps, args.warmup, outs, args.warmup_ms)
+        ms /= R
         cls = st["context_lens"]
         alg = decode_algorithmic_bytes(cls, Hq, Hkv, D, BS, e, 2, int8_scales=i8)
-        res.update({"replicas": R, "ms_per_layer": round(ms, 5), "tokens_per_s": round(S / (ms * 1e-3), 1),
+        res.update({"replicas": R, "warmup_steps_run": warm_run, "ms_per_layer": round(ms, 5),
+                    "tokens_per_s": round(S / (ms * 1e-3), 1),
                     "kv_gbs": round(kv_bytes(cls, Hkv, D, e) / (ms * 1e-3) / 1e9, 1),
                     "pct_hbm_peak": round(100.0 * alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                     "algorithmic_bytes_per_layer": alg,
@@ -667,12 +696,13 @@ def run_next_workload(args) -> dict:
                                   partition_tokens=args.partition_tokens, query_start_loc=qsl, max_query_len=L)
                 for r in range(R)]
 
-    ms = _timed_graph(prepare, args.steps, args.warmup, outs) / R
+    ms, warm_run = _timed_graph(prepare, args.steps, args.warmup, outs, args.warmup_ms)
+    ms /= R
     cls = st["context_lens"]
     alg = decode_algorithmic_bytes(cls, Hq, Hkv, D, BS, e, 2, int8_scales=i8, query_rows=S * L)
     visible = sum(sum(int(n) - L + i + 1 for i in range(L)) for n in cls)
     flops = 4 * Hq * D * visible
-    res.update({"replicas": R, "query_rows_per_seq": L, "ms_per_layer": round(ms, 5),
+    res.update({"replicas": R, "warmup_steps_run": warm_run, "query_rows_per_seq": L, "ms_per_layer": round(ms, 5),
                 "query_tokens_per_s": round(S * L / (ms * 1e-3), 1),
                 "kv_gbs": round(kv_bytes(cls, Hkv, D, e) / (ms * 1e-3) / 1e9, 1),
                 "pct_hbm_peak": round(100.0 * alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
@@ -877,6 +907,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-ms", type=float, default=200.0,
+                    help="keep warming up until this much wall time has passed (the clocks settle under load)")
     ap.add_argument("--layers", type=int, default=80, help="layers of the 70B-shaped model (80 is the workload)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
