@@ -10,10 +10,15 @@ and the one-GPU guard.  No GPU is used.
 * Contiguous reservation wastes what the pages' fragmentation examples
   give (tests/golden/waste_examples.json); paged storage wastes only the
   tail of the last block.
-* `bench.py --gpus 2` stops with a message before touching a GPU."""
+* `bench.py --gpus 2` stops with a message before touching a GPU.
+* The warm-up before a timed region runs at least the asked steps and at
+  least the asked wall time, synchronising as it goes and once at the end
+  (synchronisation stubbed out: no GPU)."""
 import os
 import subprocess
 import sys
+
+import time
 
 import bench
 
@@ -65,3 +70,29 @@ def test_more_than_one_gpu_is_refused_before_any_gpu_work():
     assert r.returncode == 2
     assert "exactly one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_warm_up_runs_the_asked_steps_and_the_time_floor(monkeypatch):
+    import torch
+
+    log = []
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda *a, **k: log.append("sync"))
+
+    def step():
+        log.append("step")
+
+    # no time floor: exactly the asked steps, then a synchronisation
+    assert bench.warm_up(step, 6, 0.0) == 6
+    assert log.count("step") == 6 and log[-1] == "sync"
+    assert log.index("sync") == 4                      # one synchronisation every four steps
+    log.clear()
+    assert bench.warm_up(step, 0, 0.0) == 0 and log == ["sync"]
+
+    # a time floor: steps continue until it has passed, the last one synchronised
+    log.clear()
+    slow = lambda: (log.append("step"), time.sleep(0.002))  # noqa: E731
+    t0 = time.perf_counter()
+    n = bench.warm_up(slow, 2, 30.0)
+    assert (time.perf_counter() - t0) * 1e3 >= 30.0
+    assert n == log.count("step") and n > 2
+    assert log[-1] == "sync"
