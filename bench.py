@@ -101,15 +101,15 @@ def cpu_model() -> str:
 
 # HBM bytes of one pa_decode call on the 70B-shaped layer (decode + merge
 # kernels, fused cache write), from rocprofv3 --pmc FETCH_SIZE and
-# WRITE_SIZE runs: FETCH_SIZE scaled by 1.99227 and WRITE_SIZE by 1.0, the
+# WRITE_SIZE runs: FETCH_SIZE scaled by 1.99226 and WRITE_SIZE by 1.0, the
 # ratios of a plain copy's known bytes to what the same counters read for it
 # (profiles/decode_mfma_llama3-70b_pmc_traffic.md).  Valid only for the
 # sources the counters were taken on: a changed kernel or plan reports null.
 PMC_TRAFFIC = {
-    "sources_sha256": "c5459350c97ea4207d25e87d93a4a459b75acfc845b4740a5e8b28106e7fde5d",
-    "fetch_kib": 320824.34375 + 1391.0,
-    "write_kib": 2680.0 + 640.0,
-    "fetch_factor": 1.99227,
+    "sources_sha256": "3771626bdf6aa622e106d3a8103b10ed1f21a78f57d35395baf912066c20be1f",
+    "fetch_kib": 320854.71875 + 1386.5,
+    "write_kib": 2680.0625 + 640.0,
+    "fetch_factor": 1.99226,
     "write_factor": 1.0,
 }
 PMC_SOURCES = ("paged_kv_cache_192_amd/csrc/pa_decode.hip", "paged_kv_cache_192_amd/csrc/pa_api.cpp",

@@ -297,32 +297,37 @@ constexpr int kBufferFormat = 0x00020000;  // raw buffer, 32-bit data format
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, bytes, kBufferFormat);
 }
+// AUX: the loads' cache policy bits, 2 = non-temporal (streamed K/V, read
+// once), 0 = normal (tiles that other waves read again soon)
+template <int AUX = 2>
 __device__ __forceinline__ u32x4_t bld16(__amdgpu_buffer_rsrc_t r, unsigned off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2 /* nt */));
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
 }
+template <int AUX = 2>
 __device__ __forceinline__ u32x2_t bld8(__amdgpu_buffer_rsrc_t r, unsigned off) {
-  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2 /* nt */));
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX));
 }
+template <int AUX = 2>
 __device__ __forceinline__ unsigned bld4(__amdgpu_buffer_rsrc_t r, unsigned off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 2 /* nt */);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX);
 }
 
-template <int RB>
+template <int RB, int AUX = 2>
 __device__ __forceinline__ void mfma_load_tile(MfmaTile<RB>& T, const char* kbase, const char* vbase,
                                                const unsigned (&koff)[4], const unsigned (&voff)[4]) {
   constexpr int TILE = 16 * RB;  // bytes of 16 token rows
   const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase, TILE), rv = tile_rsrc(vbase, TILE);
 #pragma unroll
-  for (int i = 0; i < RB / 64; ++i) T.k[i] = bld16(rk, koff[i]);
+  for (int i = 0; i < RB / 64; ++i) T.k[i] = bld16<AUX>(rk, koff[i]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if constexpr (RB == 64) {
-      T.v[i] = u32x4_t{bld4(rv, voff[i]), 0u, 0u, 0u};
+      T.v[i] = u32x4_t{bld4<AUX>(rv, voff[i]), 0u, 0u, 0u};
     } else if constexpr (RB == 128) {
-      const u32x2_t w = bld8(rv, voff[i]);
+      const u32x2_t w = bld8<AUX>(rv, voff[i]);
       T.v[i] = u32x4_t{w[0], w[1], 0u, 0u};
     } else {
-      T.v[i] = bld16(rv, voff[i]);
+      T.v[i] = bld16<AUX>(rv, voff[i]);
     }
   }
 }
@@ -990,18 +995,19 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
   const char *kA, *vA, *kB, *vB;
   bool okA, okB;
   Sc ksA{}, vsA{}, ksB{}, vsB{};
-  auto run_tiles = [&](auto full_tag, int ti, int tend) {
+  auto run_tiles = [&](auto full_tag, auto aux_tag, int ti, int tend) {
     constexpr bool FULL = decltype(full_tag)::value;
+    constexpr int AUX = decltype(aux_tag)::value;
     if (ti >= tend) return;
     tile_ptrs(ti, kA, vA, okA, ksA, vsA);
-    mfma_load_tile<RB>(A, kA, vA, koff, voff);
+    mfma_load_tile<RB, AUX>(A, kA, vA, koff, voff);
     while (true) {
       tile_ptrs(ti + TS < tend ? ti + TS : ti, kB, vB, okB, ksB, vsB);
-      mfma_load_tile<RB>(B, kB, vB, koff, voff);
+      mfma_load_tile<RB, AUX>(B, kB, vB, koff, voff);
       if (!FULL || okA) compute(full_tag, A, ti, okA, ksA, vsA);
       if ((ti += TS) >= tend) break;
       tile_ptrs(ti + TS < tend ? ti + TS : ti, kA, vA, okA, ksA, vsA);
-      mfma_load_tile<RB>(A, kA, vA, koff, voff);
+      mfma_load_tile<RB, AUX>(A, kA, vA, koff, voff);
       if (!FULL || okB) compute(full_tag, B, ti, okB, ksB, vsB);
       if ((ti += TS) >= tend) break;
     }
@@ -1012,11 +1018,19 @@ __global__ __launch_bounds__(64 * WG) void decode_mfma_kernel(
   // it only with at least 16 fully visible tiles.
   const int full_end = min(tile_end, max(lim_lo, 0) >> 4);
   int ti = tile_begin + (TS > 1 ? wv : 0);
+  // A prefix item's tiles are read again by the other column groups of its
+  // kv head: normal loads keep them in L2; every other tile is streamed.
+  auto run = [&](auto full_tag, int a, int b) {
+    if (MODE == kModeCascade && pre)  // wave-uniform
+      run_tiles(full_tag, std::integral_constant<int, 0>{}, a, b);
+    else
+      run_tiles(full_tag, std::integral_constant<int, 2>{}, a, b);
+  };
   if (full_end - ti >= 16 * TS) {
-    run_tiles(std::true_type{}, ti, full_end);
+    run(std::true_type{}, ti, full_end);
     ti += (full_end - ti + TS - 1) / TS * TS;
   }
-  run_tiles(std::false_type{}, ti, tile_end);
+  run(std::false_type{}, ti, tile_end);
 
   if (owns_new && j == 0) {
     const int e = tnew / BS - tbl_base;
