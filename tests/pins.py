@@ -696,6 +696,36 @@ def pin_multi_query_rows_are_prefix_decodes():
             assert np.array_equal(out[r], one[0]), (s, i)
 
 
+def pin_multi_query_matches_library_attention():
+    """Several causal query rows against a library routine: torch's
+    scaled_dot_product_attention in float64 on the CPU over each sequence's
+    contiguous K/V (each kv head repeated for its query heads), with an
+    explicit mask in which query row i of L sees the first n - L + i + 1
+    tokens (the rows are the sequence's last L tokens); within 1e-12."""
+    import torch  # noqa: PLC0415
+
+    rng = np.random.default_rng(49)
+    lens = [40, 100, 7, 64, 1]
+    qlens = [8, 33, 7, 1, 1]          # every row sees at least one token
+    Hq, Hkv, D, BS, NB = 8, 2, 64, 16, 20
+    K = [rng.standard_normal((n, Hkv, D)).astype(np.float32) for n in lens]
+    V = [rng.standard_normal((n, Hkv, D)).astype(np.float32) for n in lens]
+    kc, bt = paginate(K, BS, NB, rng=rng)
+    vc, _ = paginate(V, BS, NB, tables=bt)
+    qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = rng.standard_normal((int(qsl[-1]), Hq, D)).astype(np.float32)
+    scale = 0.125
+    out = oracle.paged_attention(q, kc, vc, bt, np.array(lens, np.int32), qsl, scale)
+    for s, (n, L) in enumerate(zip(lens, qlens)):
+        qs = torch.from_numpy(q[qsl[s]:qsl[s + 1]].astype(np.float64)).permute(1, 0, 2)
+        ks = torch.from_numpy(K[s].astype(np.float64)).permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
+        vs = torch.from_numpy(V[s].astype(np.float64)).permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
+        mask = torch.arange(n)[None, :] <= (n - L + torch.arange(L))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qs, ks, vs, attn_mask=mask, scale=scale)
+        err = np.max(np.abs(out[qsl[s]:qsl[s + 1]] - ref.permute(1, 0, 2).numpy()))
+        assert err < 1e-12, (s, err)
+
+
 QUANT_PINS = [pin_fp8_format_values, pin_fp8_encode, pin_per_token_scales_closed_form,
               pin_quantised_decode_matches_contiguous, pin_quantising_write_hand_values,
               pin_quantising_write_round_trip, pin_swap_blocks_exact]
@@ -704,6 +734,7 @@ CACHE_PINS = [pin_slot_mapping_figure, pin_slot_mapping_edges,
               pin_reshape_writes_exactly_one_slot_per_token, pin_copy_blocks_exact,
               pin_quantiser_hand_values, pin_quantiser_invariants]
 
-MULTI_QUERY_PINS = [pin_multi_query_closed_forms, pin_multi_query_rows_are_prefix_decodes]
+MULTI_QUERY_PINS = [pin_multi_query_closed_forms, pin_multi_query_rows_are_prefix_decodes,
+                    pin_multi_query_matches_library_attention]
 
 ALL_PINS = DECODE_PINS + CACHE_PINS + QUANT_PINS + MULTI_QUERY_PINS
